@@ -1,0 +1,306 @@
+#!/usr/bin/env python3
+"""W4A16 g128 decode benchmark on one MI355X.
+
+Workload (one "step"): a 70B-shaped decode step at batch 1 -- 80 layers, each
+with the seven GQA matrices q/o 8192x8192, k/v 1024x8192, gate/up 28672x8192
+and down 8192x28672, quantized to asymmetric int4 with group 128 and resident
+in HBM in the kernel layout (about 36 GB); every matrix is multiplied once by
+its bf16 activation row with w4_gemv, all 560 launches back to back and
+replayed from one captured graph.  Weights are N(0, 0.02) and activations
+N(0, 1), drawn on the GPU from fixed seeds (synthetic, no checkpoint).
+
+The printed JSON line reports the achieved HBM bandwidth of the step computed
+from algorithmic bytes (codes + fp16 scales + byte zeros + activations +
+outputs), the roofline fraction against the 8 TB/s HBM peak, and the CPU
+oracle's rate on a bounded sample of the same work.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_DENSE_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+METRIC = "W4A16 g128 GEMV achieved HBM GB/s (% of peak), 70B layer shapes, batch 1"
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--layers", type=int, default=80)
+    ap.add_argument("--no-graph", action="store_true", help="launch the 560 GEMVs eagerly")
+    ap.add_argument("--skip-extras", action="store_true",
+                    help="only the headline step (no batch sweep, per-shape, GEMM, quantizer)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def build_stack(layers: int, dev: str):
+    import torch
+
+    import dequant_gemv_w4_amd as w4
+    import synth
+
+    prepared = {}
+    t0 = time.time()
+    for layer in range(layers):
+        for name in synth.MATRIX_ORDER:
+            n, k = synth.LLAMA70B_SHAPES[name]
+            W = synth.normal_weights(n, k, synth.seed_for(4, name, layer), dev)
+            p, s, z = w4.w4_quantize(W)
+            prepared[(layer, name)] = w4.w4_prepare(p, s, z)
+            del W, p, s, z
+        if layer % 10 == 9 or layer == layers - 1:
+            torch.cuda.synchronize()
+            log(f"quantized and prepared {layer + 1}/{layers} layers ({time.time() - t0:.1f} s)")
+    return prepared
+
+
+def make_step(prepared, layers: int, m: int, dev: str):
+    import torch
+
+    import synth
+    from dequant_gemv_w4_amd.decode import DecodeStep, GemvCall
+
+    # activation rows feeding each matrix (the step's inputs; fixed across layers)
+    xs = {
+        "attn": synth.normal_activations(m, 8192, 40001, dev),
+        "o": synth.normal_activations(m, 8192, 40002, dev),
+        "mlp": synth.normal_activations(m, 8192, 40003, dev),
+        "down": synth.normal_activations(m, 28672, 40004, dev),
+    }
+    feed = {"q": "attn", "k": "attn", "v": "attn", "o": "o", "gate": "mlp", "up": "mlp",
+            "down": "down"}
+    calls = []
+    for layer in range(layers):
+        for name in synth.MATRIX_ORDER:
+            n, k = synth.LLAMA70B_SHAPES[name]
+            y = torch.empty(m, n, dtype=torch.float32, device=dev)
+            calls.append(GemvCall(prepared[(layer, name)], n, k, xs[feed[name]], y))
+    return DecodeStep(calls)
+
+
+def time_step(step, steps: int, warmup: int) -> float:
+    """Milliseconds per step from HIP events on the launch stream."""
+    import torch
+    for _ in range(warmup):
+        step.run()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        step.run()
+    end.record()
+    end.synchronize()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def per_shape(prepared, layers: int, dev: str, reps: int = 3):
+    """Isolated GB/s per matrix shape: the same shape across all layers, back to back."""
+    import synth
+    from dequant_gemv_w4_amd.decode import DecodeStep, GemvCall
+    import torch
+
+    out = {}
+    for name in synth.MATRIX_ORDER:
+        n, k = synth.LLAMA70B_SHAPES[name]
+        x = synth.normal_activations(1, k, 40100, dev)
+        calls = [GemvCall(prepared[(layer, name)], n, k, x,
+                          torch.empty(1, n, dtype=torch.float32, device=dev))
+                 for layer in range(layers)]
+        st = DecodeStep(calls)
+        st.capture()
+        ms = time_step(st, reps, 1)
+        out[name] = {"N": n, "K": k, "us_per_call": round(ms * 1000 / layers, 2),
+                     "GB/s": round(st.algorithmic_bytes() / (ms * 1e-3) / 1e9, 1)}
+    return out
+
+
+def prefill_gemm(prepared, dev: str, reps: int = 3):
+    import torch
+
+    import dequant_gemv_w4_amd as w4
+    import synth
+
+    m, n, k = 4096, 28672, 8192
+    X = synth.normal_activations(m, k, 40200, dev)
+    Y = torch.empty(m, n, dtype=torch.float32, device=dev)
+    prep = prepared[(0, "gate")]
+    w4.w4_gemm(prep, n, k, X, Y=Y)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        w4.w4_gemm(prep, n, k, X, Y=Y)
+    end.record()
+    end.synchronize()
+    ms = start.elapsed_time(end) / reps
+    tflops = 2.0 * m * n * k / (ms * 1e-3) / 1e12
+    return {"M": m, "N": n, "K": k, "ms": round(ms, 3), "TFLOP/s": round(tflops, 1),
+            "mfma_util_vs_2.5PF_dense_bf16": round(tflops / BF16_DENSE_TFLOPS, 4)}
+
+
+def quantizer_rate(dev: str, reps: int = 3):
+    import torch
+
+    import dequant_gemv_w4_amd as w4
+    import synth
+
+    n, k = 28672, 8192
+    W = synth.normal_weights(n, k, 40300, dev)
+    p, s, z = w4.w4_quantize(W)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        w4.w4_quantize(W, packed=p, scales=s, zeros=z)
+    end.record()
+    end.synchronize()
+    ms = start.elapsed_time(end) / reps
+    nbytes = n * k * 4 + n * k // 2 + (n * k // 128) * 3
+    return {"N": n, "K": k, "ms": round(ms, 3), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+
+
+def cpu_baseline():
+    """The oracle's dequantize-then-dot (fp64) on one 8192x8192 matrix at M=1, on host cores."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    n, k = 8192, 8192
+    W = synth.normal_weights(n, k, synth.seed_for(4, "o", 0), "cpu").numpy()
+    x = synth.normal_activations(1, k, 40002, "cpu").float().numpy()
+    p, s, z = oracle.quantize_ref(W)
+    reps = 3
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        oracle.gemv_ref(p, s, z, x)
+    dt = (time.perf_counter() - t0) / reps
+    nbytes = n * k // 2 + (n * k // 128) * 3 + k * 2 + n * 4
+    threads = 1
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([1] + [int(i.get("num_threads", 1)) for i in threadpool_info()])
+    except Exception:
+        pass
+    del np
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"70B o_proj {n}x{k}, M=1: oracle fp64 dequantize-then-dot (gemv_ref), "
+                      f"{reps} repetitions, {dt:.2f} s each; quantization untimed",
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main() -> int:
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the method needs no "
+                                   "inter-GPU communication and multi-GPU runs are not supported",
+                          "n_gpus": args.gpus}))
+        return 2
+
+    import torch
+
+    import dequant_gemv_w4_amd as w4
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    w4.lib()
+    log(f"device {torch.cuda.get_device_name(0)}; building {args.layers} layers")
+    prepared = build_stack(args.layers, dev)
+
+    step = make_step(prepared, args.layers, 1, dev)
+    if not args.no_graph:
+        step.capture()
+        log("captured the step into a graph")
+    ms = time_step(step, args.steps, args.warmup)
+    nbytes = step.algorithmic_bytes()
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    launches = len(step.calls)
+    log(f"step {ms:.3f} ms, {gbs:.1f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of peak)")
+
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "llama70b-shaped decode step: 80 layers x {q,k,v,o,gate,up,down} w4_gemv, M=1",
+            "layers": args.layers,
+            "gemv_launches_per_step": launches,
+            "batch": 1,
+            "resident_prepared_bytes": int(sum(t.numel() for t in prepared.values())),
+            "algorithmic_bytes_per_step": int(nbytes),
+            "graph_replay": not args.no_graph,
+            "parallelism": "single GPU",
+        },
+        "tokens_per_s_equiv": round(1000.0 / ms, 2),
+        "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel": "w4_gemv (gemv_kernel<1,false,1,1024>)",
+            "per_launch": f"{nbytes / launches / 1e6:.2f} MB algorithmic in "
+                          f"{ms * 1000 / launches:.2f} us average (step time / launches)",
+        },
+    }
+
+    if not args.skip_extras:
+        batches = {}
+        for m in (4, 8, 16):
+            st = make_step(prepared, args.layers, m, dev)
+            st.capture()
+            msm = time_step(st, max(2, args.steps // 4), 1)
+            batches[str(m)] = {"ms_per_step": round(msm, 3),
+                               "GB/s": round(st.algorithmic_bytes() / (msm * 1e-3) / 1e9, 1),
+                               "tokens_per_s": round(1000.0 * m / msm, 1)}
+            del st
+            log(f"M={m}: {msm:.3f} ms/step")
+        result["batch_sweep"] = batches
+        result["per_shape_m1"] = per_shape(prepared, args.layers, dev)
+        log("per-shape done")
+        result["prefill_gemm"] = prefill_gemm(prepared, dev)
+        log(f"prefill GEMM: {result['prefill_gemm']}")
+        result["quantizer"] = quantizer_rate(dev)
+
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle sample")
+        result["cpu_baseline"] = cpu_baseline()
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,258 @@
+"""Python binding of libw4a16 (asymmetric group-128 int4 weights, fused W4A16 products on gfx950).
+
+Argument marshalling only: every step of quantization, layout and the products
+runs in the HIP kernels of ``libw4a16.so``.  PyTorch supplies device memory and
+the current stream.  There is no fallback: if the library is missing or the
+device is not gfx950 the calls raise.
+
+The names mirror the C entry points declared in ``include/w4a16.h``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+__all__ = [
+    "W4Error", "lib", "declared_symbols",
+    "w4_quantize", "w4_prepared_bytes", "w4_prepare", "w4_unprepare",
+    "w4_gemv", "w4_gemm_workspace_bytes", "w4_gemm",
+    "w4_status_string", "w4_last_hip_error", "w4_format_version",
+    "W4_OK", "W4_F32", "W4_BF16", "GROUP",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libw4a16.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "w4a16.h")
+
+GROUP = 128
+W4_OK = 0
+W4_F32 = 0
+W4_BF16 = 1
+STATUS_NONFINITE = 1
+STATUS_SCALE_OVERFLOW = 2
+STATUS_SCALE_ZERO = 4
+
+_lib = None
+
+
+class W4Error(RuntimeError):
+    """A libw4a16 call returned a non-OK status."""
+
+    def __init__(self, status: int, where: str):
+        msg = _status_text(status)
+        if status == 8:  # W4_ERR_HIP
+            msg += ": " + w4_last_hip_error()
+        super().__init__(f"{where}: {msg} (status {status})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libw4a16.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m dequant_gemv_w4_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, u32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32, ctypes.c_size_t
+    i32 = ctypes.c_int
+    L.w4_quantize.argtypes = [vp, i32, i64, i64, vp, vp, vp, vp, vp]
+    L.w4_quantize.restype = i32
+    L.w4_prepared_bytes.argtypes = [i64, i64]
+    L.w4_prepared_bytes.restype = sz
+    L.w4_prepare.argtypes = [vp, vp, vp, i64, i64, vp, sz, vp]
+    L.w4_prepare.restype = i32
+    L.w4_unprepare.argtypes = [vp, i64, i64, vp, vp, vp, vp]
+    L.w4_unprepare.restype = i32
+    L.w4_gemv.argtypes = [vp, i64, i64, vp, i32, i64, vp, i32, vp]
+    L.w4_gemv.restype = i32
+    L.w4_gemm_workspace_bytes.argtypes = [i64, i64, i64]
+    L.w4_gemm_workspace_bytes.restype = sz
+    L.w4_gemm.argtypes = [vp, i64, i64, vp, i64, vp, i32, vp, sz, vp]
+    L.w4_gemm.restype = i32
+    L.w4_status_string.argtypes = [i32]
+    L.w4_status_string.restype = ctypes.c_char_p
+    L.w4_last_hip_error.argtypes = []
+    L.w4_last_hip_error.restype = ctypes.c_char_p
+    L.w4_format_version.argtypes = []
+    L.w4_format_version.restype = i32
+    del u32
+    _lib = L
+    return L
+
+
+def declared_symbols() -> list[str]:
+    """Function names declared in include/w4a16.h."""
+    with open(HEADER_PATH) as fh:
+        text = fh.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(w4_[a-z0-9_]+)\s*\(", text)))
+
+
+def _status_text(status: int) -> str:
+    return lib().w4_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != W4_OK:
+        raise W4Error(status, where)
+
+
+def _stream(t) -> ctypes.c_void_p:
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _require(t, dtype, shape, name):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name} has dtype {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# --------------------------------------------------------------------------
+# Entry points
+# --------------------------------------------------------------------------
+
+def w4_status_string(status: int) -> str:
+    return _status_text(status)
+
+
+def w4_last_hip_error() -> str:
+    return lib().w4_last_hip_error().decode()
+
+
+def w4_format_version() -> int:
+    return int(lib().w4_format_version())
+
+
+def w4_prepared_bytes(N: int, K: int) -> int:
+    return int(lib().w4_prepared_bytes(int(N), int(K)))
+
+
+def w4_gemm_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib().w4_gemm_workspace_bytes(int(M), int(N), int(K)))
+
+
+def w4_quantize(W, packed=None, scales=None, zeros=None, status=None):
+    """Quantize W [N, K] (float32 or bfloat16, on the GPU).
+
+    Returns (packed uint8 [N, K/2], scales float16 [N, K/128], zeros uint8 [N, K/128]).
+    ``status`` may be an int32 tensor of one element; W4 status bits are OR-ed into it.
+    """
+    import torch
+    _require(W, (torch.float32, torch.bfloat16), None, "W")
+    if W.dim() != 2:
+        raise ValueError("W must be 2-D")
+    N, K = W.shape
+    kg = K // GROUP
+    dev = W.device
+    if packed is None:
+        packed = torch.empty(N, K // 2, dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty(N, kg, dtype=torch.float16, device=dev)
+    if zeros is None:
+        zeros = torch.empty(N, kg, dtype=torch.uint8, device=dev)
+    _require(packed, torch.uint8, (N, K // 2), "packed")
+    _require(scales, torch.float16, (N, kg), "scales")
+    _require(zeros, torch.uint8, (N, kg), "zeros")
+    st_ptr = ctypes.c_void_p(None)
+    if status is not None:
+        _require(status, (torch.int32,), None, "status")
+        st_ptr = _ptr(status)
+    wt = W4_BF16 if W.dtype == torch.bfloat16 else W4_F32
+    _check(lib().w4_quantize(_ptr(W), wt, N, K, _ptr(packed), _ptr(scales), _ptr(zeros),
+                             st_ptr, _stream(W)), "w4_quantize")
+    return packed, scales, zeros
+
+
+def w4_prepare(packed, scales, zeros, prepared=None):
+    """Kernel layout of the canonical arrays; returns a uint8 tensor of w4_prepared_bytes(N, K)."""
+    import torch
+    _require(packed, torch.uint8, None, "packed")
+    N, Kh = packed.shape
+    K = 2 * Kh
+    _require(scales, torch.float16, (N, K // GROUP), "scales")
+    _require(zeros, torch.uint8, (N, K // GROUP), "zeros")
+    nbytes = w4_prepared_bytes(N, K)
+    if prepared is None:
+        prepared = torch.empty(nbytes, dtype=torch.uint8, device=packed.device)
+    _require(prepared, torch.uint8, None, "prepared")
+    _check(lib().w4_prepare(_ptr(packed), _ptr(scales), _ptr(zeros), N, K, _ptr(prepared),
+                            prepared.numel(), _stream(packed)), "w4_prepare")
+    return prepared
+
+
+def w4_unprepare(prepared, N: int, K: int):
+    """Inverse of w4_prepare: returns (packed, scales, zeros)."""
+    import torch
+    _require(prepared, torch.uint8, None, "prepared")
+    if prepared.numel() < w4_prepared_bytes(N, K):
+        raise ValueError("prepared buffer too small")
+    dev = prepared.device
+    packed = torch.empty(N, K // 2, dtype=torch.uint8, device=dev)
+    scales = torch.empty(N, K // GROUP, dtype=torch.float16, device=dev)
+    zeros = torch.empty(N, K // GROUP, dtype=torch.uint8, device=dev)
+    _check(lib().w4_unprepare(_ptr(prepared), N, K, _ptr(packed), _ptr(scales), _ptr(zeros),
+                              _stream(prepared)), "w4_unprepare")
+    return packed, scales, zeros
+
+
+def w4_gemv(prepared, N: int, K: int, x, y=None, out_dtype=None):
+    """y [M, N] = x [M, K] @ w_hat^T for 1 <= M <= 16 (x bfloat16 or float32)."""
+    import torch
+    _require(prepared, torch.uint8, None, "prepared")
+    _require(x, (torch.bfloat16, torch.float32), None, "x")
+    if x.dim() == 1:
+        x = x.unsqueeze(0)
+    M = x.shape[0]
+    if x.shape[1] != K:
+        raise ValueError("x must be [M, K]")
+    if out_dtype is None:
+        out_dtype = y.dtype if y is not None else torch.float32
+    if y is None:
+        y = torch.empty(M, N, dtype=out_dtype, device=x.device)
+    _require(y, (torch.float32, torch.bfloat16), (M, N), "y")
+    xt = W4_F32 if x.dtype == torch.float32 else W4_BF16
+    yt = W4_F32 if y.dtype == torch.float32 else W4_BF16
+    _check(lib().w4_gemv(_ptr(prepared), N, K, _ptr(x), xt, M, _ptr(y), yt, _stream(x)),
+           "w4_gemv")
+    return y
+
+
+def w4_gemm(prepared, N: int, K: int, X, Y=None, out_dtype=None, workspace=None):
+    """Y [M, N] = X [M, K] (bfloat16) @ w_hat^T on MFMA."""
+    import torch
+    _require(prepared, torch.uint8, None, "prepared")
+    _require(X, torch.bfloat16, None, "X")
+    M = X.shape[0]
+    if X.shape[1] != K:
+        raise ValueError("X must be [M, K]")
+    if out_dtype is None:
+        out_dtype = Y.dtype if Y is not None else torch.float32
+    if Y is None:
+        Y = torch.empty(M, N, dtype=out_dtype, device=X.device)
+    _require(Y, (torch.float32, torch.bfloat16), (M, N), "Y")
+    need = w4_gemm_workspace_bytes(M, N, K)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
+    ws_ptr = _ptr(workspace) if workspace is not None else ctypes.c_void_p(None)
+    ws_len = workspace.numel() if workspace is not None else 0
+    yt = W4_F32 if Y.dtype == torch.float32 else W4_BF16
+    _check(lib().w4_gemm(_ptr(prepared), N, K, _ptr(X), M, _ptr(Y), yt, ws_ptr, ws_len,
+                         _stream(X)), "w4_gemm")
+    return Y

@@ -1,0 +1,163 @@
+// C-ABI entry points of libw4a16: argument validation, device check, launch.
+// The kernels live in w4_quantize.hip, w4_gemv.hip and w4_gemm.hip.
+#include <atomic>
+#include <cstring>
+#include <string>
+
+#include "../../include/w4a16.h"
+#include "w4_internal.h"
+
+namespace {
+
+thread_local std::string g_last_hip_error;
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+w4_status hip_fail(hipError_t e) {
+    g_last_hip_error = hipGetErrorString(e);
+    return W4_ERR_HIP;
+}
+
+w4_status check_arch() {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    if (dev < 0 || dev >= kMaxDevices) return W4_ERR_ARCH;
+    int st = g_arch_state[dev].load(std::memory_order_acquire);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess) return hip_fail(e);
+        st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+        g_arch_state[dev].store(st, std::memory_order_release);
+    }
+    return st == 1 ? W4_OK : W4_ERR_ARCH;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+w4_status check_nk(int64_t n, int64_t k) {
+    if (n < 1 || k < W4_GROUP || k % W4_GROUP != 0) return W4_ERR_SHAPE;
+    if (n > (int64_t)0x7FFFFFFF || k > (int64_t)0x7FFFFFFF) return W4_ERR_SHAPE;
+    return W4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* w4_status_string(w4_status s) {
+    switch (s) {
+        case W4_OK: return "ok";
+        case W4_ERR_NULL: return "null pointer";
+        case W4_ERR_SHAPE: return "unsupported shape";
+        case W4_ERR_ALIGN: return "misaligned pointer";
+        case W4_ERR_DTYPE: return "unsupported dtype";
+        case W4_ERR_UNSUPPORTED: return "unsupported format";
+        case W4_ERR_ARCH: return "device is not gfx950";
+        case W4_ERR_WORKSPACE: return "workspace missing or too small";
+        case W4_ERR_HIP: return "HIP runtime error";
+        case W4_ERR_BUFFER: return "destination buffer too small";
+    }
+    return "unknown status";
+}
+
+const char* w4_last_hip_error(void) { return g_last_hip_error.c_str(); }
+
+int w4_format_version(void) { return W4_FORMAT_VERSION; }
+
+w4_status w4_quantize(const void* W, w4_dtype wt, int64_t N, int64_t K, uint8_t* packed,
+                      uint16_t* scales_f16, uint8_t* zeros, uint32_t* d_status,
+                      hipStream_t stream) {
+    if (!W || !packed || !scales_f16 || !zeros) return W4_ERR_NULL;
+    if (wt != W4_F32 && wt != W4_BF16) return W4_ERR_DTYPE;
+    w4_status st = check_nk(N, K);
+    if (st != W4_OK) return st;
+    if (!aligned(W, 16) || !aligned(packed, 16) || !aligned(scales_f16, 2) ||
+        (d_status && !aligned(d_status, 4)))
+        return W4_ERR_ALIGN;
+    st = check_arch();
+    if (st != W4_OK) return st;
+    hipError_t e = w4::launch_quantize(W, wt == W4_BF16, N * (K / W4_GROUP), packed, scales_f16,
+                                       zeros, d_status, stream);
+    return e == hipSuccess ? W4_OK : hip_fail(e);
+}
+
+size_t w4_prepared_bytes(int64_t N, int64_t K) {
+    if (check_nk(N, K) != W4_OK) return 0;
+    return (size_t)w4::prepared_total(N, K);
+}
+
+w4_status w4_prepare(const uint8_t* packed, const uint16_t* scales_f16, const uint8_t* zeros,
+                     int64_t N, int64_t K, void* prepared, size_t prepared_bytes,
+                     hipStream_t stream) {
+    if (!packed || !scales_f16 || !zeros || !prepared) return W4_ERR_NULL;
+    w4_status st = check_nk(N, K);
+    if (st != W4_OK) return st;
+    if (!aligned(packed, 16) || !aligned(scales_f16, 2) || !aligned(prepared, 256))
+        return W4_ERR_ALIGN;
+    if (prepared_bytes < w4_prepared_bytes(N, K)) return W4_ERR_BUFFER;
+    st = check_arch();
+    if (st != W4_OK) return st;
+    hipError_t e = w4::launch_prepare(packed, scales_f16, zeros, N, K,
+                                      static_cast<uint8_t*>(prepared), stream);
+    return e == hipSuccess ? W4_OK : hip_fail(e);
+}
+
+w4_status w4_unprepare(const void* prepared, int64_t N, int64_t K, uint8_t* packed,
+                       uint16_t* scales_f16, uint8_t* zeros, hipStream_t stream) {
+    if (!packed || !scales_f16 || !zeros || !prepared) return W4_ERR_NULL;
+    w4_status st = check_nk(N, K);
+    if (st != W4_OK) return st;
+    if (!aligned(packed, 16) || !aligned(scales_f16, 2) || !aligned(prepared, 256))
+        return W4_ERR_ALIGN;
+    st = check_arch();
+    if (st != W4_OK) return st;
+    hipError_t e = w4::launch_unprepare(static_cast<const uint8_t*>(prepared), N, K, packed,
+                                        scales_f16, zeros, stream);
+    return e == hipSuccess ? W4_OK : hip_fail(e);
+}
+
+w4_status w4_gemv(const void* prepared, int64_t N, int64_t K, const void* x, w4_dtype xt,
+                  int64_t M, void* y, w4_dtype yt, hipStream_t stream) {
+    if (!prepared || !x || !y) return W4_ERR_NULL;
+    if ((xt != W4_F32 && xt != W4_BF16) || (yt != W4_F32 && yt != W4_BF16)) return W4_ERR_DTYPE;
+    w4_status st = check_nk(N, K);
+    if (st != W4_OK) return st;
+    if (K > W4_GEMV_MAX_K || M < 1 || M > W4_GEMV_MAX_M) return W4_ERR_SHAPE;
+    if (!aligned(prepared, 256) || !aligned(x, 16) || !aligned(y, yt == W4_F32 ? 4 : 2))
+        return W4_ERR_ALIGN;
+    st = check_arch();
+    if (st != W4_OK) return st;
+    hipError_t e = w4::launch_gemv(static_cast<const uint8_t*>(prepared), N, K, x, xt == W4_F32,
+                                   M, y, yt == W4_BF16, stream);
+    return e == hipSuccess ? W4_OK : hip_fail(e);
+}
+
+size_t w4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    (void)M;
+    (void)N;
+    (void)K;
+    return 0;
+}
+
+w4_status w4_gemm(const void* prepared, int64_t N, int64_t K, const void* X, int64_t M, void* Y,
+                  w4_dtype yt, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    (void)workspace;
+    if (!prepared || !X || !Y) return W4_ERR_NULL;
+    if (yt != W4_F32 && yt != W4_BF16) return W4_ERR_DTYPE;
+    w4_status st = check_nk(N, K);
+    if (st != W4_OK) return st;
+    if (M < 1 || (M + 127) / 128 > 65535) return W4_ERR_SHAPE;
+    if (workspace_bytes < w4_gemm_workspace_bytes(M, N, K)) return W4_ERR_WORKSPACE;
+    if (!aligned(prepared, 256) || !aligned(X, 16) || !aligned(Y, yt == W4_F32 ? 4 : 2))
+        return W4_ERR_ALIGN;
+    st = check_arch();
+    if (st != W4_OK) return st;
+    hipError_t e = w4::launch_gemm(static_cast<const uint8_t*>(prepared), N, K, X, M, Y,
+                                   yt == W4_BF16, stream);
+    return e == hipSuccess ? W4_OK : hip_fail(e);
+}
+
+}  // extern "C"

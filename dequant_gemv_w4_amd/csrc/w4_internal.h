@@ -1,0 +1,71 @@
+// Internal definitions shared by the libw4a16 kernels and host code.
+//
+// Prepared ("kernel") layout, format version 1.  The canonical arrays are
+// rearranged so that one 16-byte load feeds 32 codes to a lane and the unpack
+// needs no data movement between lanes (page "LLM Quantization Architecture in
+// Depth" › "Kernels and memory layout: the format is a contract": packed
+// weights are pre-shuffled and scales sit beside them; architecture page,
+// stage "Memory Layout": scale interleaving).
+//
+//   region A, offset 0:   N rows x (K/2) bytes.  Each aligned 32-bit word holds
+//                         the 8 codes c0..c7 of 8 consecutive inputs, stored as
+//                         bits [4j, 4j+4)      = c(2j)    (j = 0..3)
+//                         bits [16+4j, 20+4j)  = c(2j+1)
+//                         so (word >> 4j) & 0x000F000F places the codes of the
+//                         input pair (2j, 2j+1) in the low bits of two 16-bit
+//                         halves, the same order as a bf16 pair of x in memory.
+//   region B, offset A_bytes rounded up to 256:
+//                         N x (K/128) 32-bit words: bits 0..15 the binary16
+//                         scale, bits 16..23 the zero, bits 24..31 zero.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4 {
+
+constexpr int kGroup = 128;
+
+inline __host__ __device__ int64_t packed_bytes(int64_t n, int64_t k) { return n * (k / 2); }
+inline __host__ __device__ int64_t sz_offset(int64_t n, int64_t k) {
+    return (packed_bytes(n, k) + 255) / 256 * 256;
+}
+inline __host__ __device__ int64_t prepared_total(int64_t n, int64_t k) {
+    return sz_offset(n, k) + n * (k / kGroup) * 4;
+}
+
+// canonical word (code i at bits 4i) -> prepared word
+__device__ __forceinline__ uint32_t to_kernel_word(uint32_t w) {
+    uint32_t e = w & 0x0F0F0F0Fu;          // c0 c2 c4 c6 at bits 0, 8, 16, 24
+    uint32_t o = (w >> 4) & 0x0F0F0F0Fu;   // c1 c3 c5 c7
+    e = (e | (e >> 4)) & 0x00FF00FFu;
+    e = (e | (e >> 8)) & 0x0000FFFFu;      // c0 c2 c4 c6 at bits 0, 4, 8, 12
+    o = (o | (o >> 4)) & 0x00FF00FFu;
+    o = (o | (o >> 8)) & 0x0000FFFFu;
+    return e | (o << 16);
+}
+
+// prepared word -> canonical word
+__device__ __forceinline__ uint32_t to_canonical_word(uint32_t p) {
+    uint32_t e = p & 0xFFFFu;
+    uint32_t o = p >> 16;
+    e = (e | (e << 8)) & 0x00FF00FFu;
+    e = (e | (e << 4)) & 0x0F0F0F0Fu;
+    o = (o | (o << 8)) & 0x00FF00FFu;
+    o = (o | (o << 4)) & 0x0F0F0F0Fu;
+    return e | (o << 4);
+}
+
+// Launch wrappers (defined in the .hip files); return hipSuccess or the launch error.
+hipError_t launch_quantize(const void* W, bool bf16, int64_t n_groups, uint8_t* packed,
+                           uint16_t* scales, uint8_t* zeros, uint32_t* status, hipStream_t s);
+hipError_t launch_prepare(const uint8_t* packed, const uint16_t* scales, const uint8_t* zeros,
+                          int64_t n, int64_t k, uint8_t* prepared, hipStream_t s);
+hipError_t launch_unprepare(const uint8_t* prepared, int64_t n, int64_t k, uint8_t* packed,
+                            uint16_t* scales, uint8_t* zeros, hipStream_t s);
+hipError_t launch_gemv(const uint8_t* prepared, int64_t n, int64_t k, const void* x, bool x_f32,
+                       int64_t m, void* y, bool y_bf16, hipStream_t s);
+hipError_t launch_gemm(const uint8_t* prepared, int64_t n, int64_t k, const void* X, int64_t m,
+                       void* Y, bool y_bf16, hipStream_t s);
+
+}  // namespace w4

@@ -1,0 +1,154 @@
+/*
+ * libw4a16 -- asymmetric group-wise 4-bit weights (group 128) and fused
+ * dequantizing matrix-vector / matrix-matrix products for AMD gfx950.
+ *
+ * Plain C ABI: every buffer is a raw device pointer owned by the caller, every
+ * size is an integer, every call is asynchronous on the given HIP stream.
+ * The library never allocates, frees or synchronizes device memory.
+ *
+ * Format (page "Weight quantization", sections "How it works" and "Code";
+ * the affine map is also given on "LLM Quantization Architecture in Depth"
+ * › "Number formats, scales and granularity"):
+ *   - W is [N, K] row-major (N outputs, K inputs); groups are 128 consecutive
+ *     inputs of one row, so K must be a multiple of 128.
+ *   - per group: lo = min(min(w), 0), hi = max(max(w), 0);
+ *     scale = (hi - lo) / 15 in binary32, or 1 when hi == lo;
+ *     zero  = clamp(round(-lo / scale), 0, 15);
+ *     code  = clamp(round(w / scale) + zero, 0, 15);
+ *     round = nearest, halves away from zero; every step one IEEE binary32
+ *     operation (true division, no fused multiply-add, subnormals kept).
+ *   - canonical storage: packed [N, K/2] bytes, code of the even input index in
+ *     the low nibble; scales [N, K/128] binary16 bit patterns (the binary32
+ *     scale rounded to nearest even); zeros [N, K/128] bytes.
+ *   - w_hat = (code - zero) * scale16 and the products use, per group,
+ *     scale16 * (sum code*x - zero * sum x): one multiply per group.
+ *
+ * Readings of points the pages leave open are fixed above: halves away from
+ * zero, codes from the binary32 scale, fp16 stored scale, byte zero.
+ *
+ * Errors: the return value reports argument validation and launch failures
+ * synchronously; W4_ERR_HIP carries the runtime's message in
+ * w4_last_hip_error().  Data conditions found on the device are OR-ed into the
+ * optional status word (see w4_quantize).  Nothing falls back to another code
+ * path: an unsupported request is refused.
+ *
+ * Threading: no mutable global state except a per-device architecture check
+ * done once; calls from several host threads are safe.  Calls that share an
+ * output buffer must be ordered by the caller.
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define W4_GROUP 128
+#define W4_FORMAT_VERSION 1
+#define W4_GEMV_MAX_M 16
+#define W4_GEMV_MAX_K 32768
+
+typedef enum {
+    W4_OK = 0,
+    W4_ERR_NULL = 1,         /* a required pointer is NULL */
+    W4_ERR_SHAPE = 2,        /* N < 1, K < 128, K % 128 != 0, M out of range, size limit */
+    W4_ERR_ALIGN = 3,        /* a pointer breaks its stated alignment */
+    W4_ERR_DTYPE = 4,        /* dtype value not accepted by this call */
+    W4_ERR_UNSUPPORTED = 5,  /* request outside the fixed format */
+    W4_ERR_ARCH = 6,         /* current device is not gfx950 */
+    W4_ERR_WORKSPACE = 7,    /* workspace missing or too small */
+    W4_ERR_HIP = 8,          /* HIP runtime error; see w4_last_hip_error() */
+    W4_ERR_BUFFER = 9        /* destination buffer smaller than required */
+} w4_status;
+
+typedef enum { W4_F32 = 0, W4_BF16 = 1 } w4_dtype;
+
+/* Device status word bits written by w4_quantize (OR-ed, never cleared). */
+#define W4_STATUS_NONFINITE      1u  /* a weight was NaN or +-inf (outputs undefined) */
+#define W4_STATUS_SCALE_OVERFLOW 2u  /* a binary32 scale rounded to binary16 infinity */
+#define W4_STATUS_SCALE_ZERO     4u  /* a non-empty group's scale rounded to binary16 zero */
+
+/*
+ * w4_quantize -- round-to-nearest quantization of W (page "Weight quantization",
+ * "How it works": scale, zero and code formulas; "Code": range widened to 0,
+ * f32 arithmetic, nibble packing with the even index low).
+ *   W          [N, K] row-major, binary32 (wt = W4_F32) or bfloat16 (W4_BF16); 16-B aligned.
+ *   packed     out [N, K/2] bytes; 16-B aligned.
+ *   scales_f16 out [N, K/128] binary16 bit patterns; 2-B aligned.
+ *   zeros      out [N, K/128] bytes.
+ *   d_status   optional device word (may be NULL); W4_STATUS_* bits are OR-ed in.
+ * Requires N >= 1, K >= 128, K % 128 == 0.  Deterministic; bit-exact with the
+ * formulas above for finite input.
+ */
+w4_status w4_quantize(const void* W, w4_dtype wt, int64_t N, int64_t K,
+                      uint8_t* packed, uint16_t* scales_f16, uint8_t* zeros,
+                      uint32_t* d_status, hipStream_t stream);
+
+/*
+ * Kernel layout ("pre-shuffled" weights with interleaved scale and zero: page
+ * "LLM Quantization Architecture in Depth" › "Kernels and memory layout: the
+ * format is a contract"; the stage list's "Memory Layout" on the
+ * architecture page).  The prepared buffer is opaque; its size is
+ * w4_prepared_bytes(N, K).  w4_prepare is a bijection of the canonical arrays
+ * and w4_unprepare is its exact inverse.
+ *   packed/scales_f16/zeros  canonical arrays as produced by w4_quantize
+ *                            (packed 16-B aligned, scales 2-B aligned).
+ *   prepared                 [w4_prepared_bytes(N, K)] bytes, 256-B aligned.
+ */
+size_t w4_prepared_bytes(int64_t N, int64_t K);
+w4_status w4_prepare(const uint8_t* packed, const uint16_t* scales_f16, const uint8_t* zeros,
+                     int64_t N, int64_t K, void* prepared, size_t prepared_bytes,
+                     hipStream_t stream);
+w4_status w4_unprepare(const void* prepared, int64_t N, int64_t K,
+                       uint8_t* packed, uint16_t* scales_f16, uint8_t* zeros,
+                       hipStream_t stream);
+
+/*
+ * w4_gemv -- decode-sized product y[m, n] = sum_k w_hat[n, k] * x[m, k] for
+ * 1 <= M <= 16, never forming w_hat in memory (page "Weight quantization",
+ * "How it works": the per-group factored dot; architecture page stage "Fused
+ * Kernels": dequantization inside the product).
+ *   prepared  from w4_prepare (256-B aligned).
+ *   x         [M, K] row-major, bfloat16 (xt = W4_BF16) or binary32 (W4_F32); 16-B aligned.
+ *   y         [M, N] row-major, binary32 (yt = W4_F32) or bfloat16 (W4_BF16); must
+ *             not overlap the inputs; 4-B aligned.
+ * Requires K <= W4_GEMV_MAX_K.  Accumulates in binary32; deterministic (no atomics).
+ */
+w4_status w4_gemv(const void* prepared, int64_t N, int64_t K,
+                  const void* x, w4_dtype xt, int64_t M,
+                  void* y, w4_dtype yt, hipStream_t stream);
+
+/*
+ * w4_gemm -- prefill-sized product Y[M, N] = X[M, K] * w_hat^T for any M >= 1
+ * (page "LLM Quantization Architecture in Depth" › "Why fewer bits make
+ * decoding faster": prefill is compute bound and weight-only formats must turn
+ * weights back into 16-bit values before the matrix units).  Weight tiles are
+ * dequantized to bfloat16 in LDS and multiplied on bf16 MFMA with binary32
+ * accumulation.
+ *   prepared  from w4_prepare.
+ *   X         [M, K] bfloat16 row-major; 16-B aligned.
+ *   Y         [M, N] row-major, binary32 or bfloat16; 4-B aligned.
+ *   workspace optional; w4_gemm_workspace_bytes() reports how many bytes the
+ *             call needs (0 means none, and workspace may be NULL).
+ */
+size_t w4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+w4_status w4_gemm(const void* prepared, int64_t N, int64_t K,
+                  const void* X, int64_t M, void* Y, w4_dtype yt,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Text of a status code (static storage). */
+const char* w4_status_string(w4_status s);
+/* Message of the last W4_ERR_HIP on the calling thread ("" if none). */
+const char* w4_last_hip_error(void);
+/* W4_FORMAT_VERSION of the library (prepared-layout version). */
+int w4_format_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_H */

@@ -1,0 +1,75 @@
+"""Host-side checks of the C-ABI library (no GPU needed).
+
+The library must load, export every function that include/w4a16.h declares,
+and reject bad arguments before touching the device.  No call here passes
+validation, so no kernel is ever launched.
+"""
+
+import ctypes
+
+import pytest
+
+import dequant_gemv_w4_amd as w4
+
+
+def test_library_loads_and_exports_declared_symbols():
+    L = w4.lib()
+    declared = w4.declared_symbols()
+    assert "w4_gemv" in declared and "w4_quantize" in declared and "w4_gemm" in declared
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_format_version_and_status_strings():
+    assert w4.w4_format_version() == 1
+    assert w4.w4_status_string(0) == "ok"
+    assert "gfx950" in w4.w4_status_string(6)
+    assert w4.w4_status_string(99) == "unknown status"
+
+
+def test_prepared_bytes_closed_form():
+    # packed bytes rounded up to 256, then one 32-bit scale/zero word per group
+    assert w4.w4_prepared_bytes(8192, 8192) == 8192 * 4096 + 8192 * 64 * 4
+    assert w4.w4_prepared_bytes(3, 384) == 768 + 3 * 3 * 4
+    assert w4.w4_prepared_bytes(1, 100) == 0     # K not a multiple of 128
+    assert w4.w4_prepared_bytes(0, 128) == 0
+    assert w4.w4_gemm_workspace_bytes(4096, 28672, 8192) == 0
+
+
+def _fake(addr=0x100000):
+    return ctypes.c_void_p(addr)
+
+
+NULL = ctypes.c_void_p(None)
+
+
+def test_validation_errors_before_device_work():
+    L = w4.lib()
+    s = NULL
+    # null pointers
+    assert L.w4_quantize(NULL, 0, 4, 128, _fake(), _fake(), _fake(), NULL, s) == 1
+    assert L.w4_gemv(NULL, 4, 128, _fake(), 1, 1, _fake(), 0, s) == 1
+    assert L.w4_gemm(_fake(), 4, 128, NULL, 1, _fake(), 0, NULL, 0, s) == 1
+    assert L.w4_prepare(_fake(), NULL, _fake(), 4, 128, _fake(), 1 << 20, s) == 1
+    # dtype
+    assert L.w4_quantize(_fake(), 7, 4, 128, _fake(), _fake(), _fake(), NULL, s) == 4
+    assert L.w4_gemv(_fake(), 4, 128, _fake(), 5, 1, _fake(), 0, s) == 4
+    # shapes
+    assert L.w4_quantize(_fake(), 0, 4, 100, _fake(), _fake(), _fake(), NULL, s) == 2
+    assert L.w4_quantize(_fake(), 0, 0, 128, _fake(), _fake(), _fake(), NULL, s) == 2
+    assert L.w4_gemv(_fake(), 4, 128, _fake(), 1, 0, _fake(), 0, s) == 2
+    assert L.w4_gemv(_fake(), 4, 128, _fake(), 1, 17, _fake(), 0, s) == 2
+    assert L.w4_gemv(_fake(), 4, 65536, _fake(), 1, 1, _fake(), 0, s) == 2
+    assert L.w4_gemm(_fake(), 4, 192, _fake(), 4, _fake(), 0, NULL, 0, s) == 2
+    # alignment
+    assert L.w4_quantize(_fake(0x100004), 0, 4, 128, _fake(), _fake(), _fake(), NULL, s) == 3
+    assert L.w4_gemv(_fake(0x100010), 4, 128, _fake(), 1, 1, _fake(), 0, s) == 3
+    assert L.w4_gemv(_fake(), 4, 128, _fake(0x100008), 1, 1, _fake(), 0, s) == 3
+    # destination too small
+    assert L.w4_prepare(_fake(), _fake(), _fake(), 4, 128, _fake(), 10, s) == 9
+
+
+def test_python_layer_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    with pytest.raises(ValueError):
+        w4.w4_quantize(torch.zeros(4, 128))

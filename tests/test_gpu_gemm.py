@@ -1,0 +1,70 @@
+"""GPU parity of w4_gemm (bf16 MFMA with weights dequantized in LDS) against the oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import dequant_gemv_w4_amd as w4
+import oracle
+import synth
+from _util import assert_within, to_np32
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _prep(W):
+    p, s, z = w4.w4_quantize(W)
+    return w4.w4_prepare(p, s, z)
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 1, 128), (200, 300, 384), (128, 128, 8192), (257, 129, 1024)])
+def test_small_full(m, n, k):
+    rng = np.random.default_rng(m * 7 + n)
+    w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
+    X = torch.from_numpy(rng.standard_normal((m, k)).astype(np.float32)).to(torch.bfloat16)
+    prep = _prep(torch.from_numpy(w).to(DEV))
+    Y = w4.w4_gemm(prep, n, k, X.to(DEV))
+    torch.cuda.synchronize()
+    p, s, z = oracle.quantize_ref(w)
+    x32 = to_np32(X)
+    r = assert_within(to_np32(Y), oracle.gemv_ref(p, s, z, x32), oracle.tolerance_ref(p, s, z, x32),
+                      f"GEMM M={m} N={n} K={k}")
+    print(f"worst err/bound {r:.3e}")
+
+
+def test_prefill_shape_sampled_outputs():
+    W, X = synth.prefill_operands(device=DEV)
+    n, k = W.shape
+    m = X.shape[0]
+    prep = _prep(W)
+    Y = w4.w4_gemm(prep, n, k, X)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(31)
+    mrows = np.unique(np.concatenate([[0, m - 1], rng.choice(m, 62, replace=False)]))
+    ncols = np.unique(np.concatenate([[0, n - 1], rng.choice(n, 510, replace=False)]))
+    p, s, z = oracle.quantize_ref(to_np32(W[torch.from_numpy(ncols).to(DEV)]))
+    x32 = to_np32(X[torch.from_numpy(mrows).to(DEV)])
+    yr = oracle.gemv_ref(p, s, z, x32)
+    bound = oracle.tolerance_ref(p, s, z, x32)
+    yg = to_np32(Y)[np.ix_(mrows, ncols)]
+    r = assert_within(yg, yr, bound, "prefill 4096x8192x28672 sampled")
+    print(f"worst err/bound {r:.3e}")
+    # a full 256-row block against 512 columns
+    cols = np.arange(512)
+    p, s, z = oracle.quantize_ref(to_np32(W[:512]))
+    x32 = to_np32(X[:256])
+    r = assert_within(to_np32(Y[:256, :512]), oracle.gemv_ref(p, s, z, x32),
+                      oracle.tolerance_ref(p, s, z, x32), "prefill 256x512 block")
+    del cols
+
+
+def test_gemm_deterministic():
+    rng = np.random.default_rng(2)
+    w = torch.from_numpy((0.02 * rng.standard_normal((512, 2048))).astype(np.float32)).to(DEV)
+    X = torch.from_numpy(rng.standard_normal((300, 2048)).astype(np.float32)).to(torch.bfloat16).to(DEV)
+    prep = _prep(w)
+    y1 = w4.w4_gemm(prep, 512, 2048, X).clone()
+    y2 = w4.w4_gemm(prep, 512, 2048, X)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)

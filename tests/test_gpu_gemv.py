@@ -1,0 +1,150 @@
+"""GPU parity of w4_gemv against the oracle (dequantize, then dot, in fp64).
+
+Bar: |y_gpu - y_ref| <= 1e-3 * sum_k |w_hat[n, k] * x[m, k]| for every checked
+output; one-hot inputs and all-zero rows must match exactly.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import dequant_gemv_w4_amd as w4
+import oracle
+import synth
+from _util import assert_within, oracle_quant_rows, to_np32
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _quant_prepare(W):
+    p, s, z = w4.w4_quantize(W)
+    prep = w4.w4_prepare(p, s, z)
+    return prep, (p, s, z)
+
+
+def _ref_from_oracle(W32, x32, rows=None):
+    """Oracle quantization of W (rows) and fp64 products with x."""
+    rows = np.arange(W32.shape[0]) if rows is None else rows
+    p, s, z = oracle_quant_rows(W32, rows)
+    return oracle.gemv_ref(p, s, z, x32), oracle.tolerance_ref(p, s, z, x32), (p, s, z)
+
+
+def _run(prep, n, k, x, out_dtype=torch.float32):
+    y = w4.w4_gemv(prep, n, k, x, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return y
+
+
+def test_single_layer_f32_activations():
+    w, x = synth.page_single_layer(4096, 4096)
+    prep, _ = _quant_prepare(torch.from_numpy(w).to(DEV))
+    y = _run(prep, 4096, 4096, torch.from_numpy(x).to(DEV))
+    yr, bound, _ = _ref_from_oracle(w, x)
+    r = assert_within(to_np32(y), yr, bound, "4096x4096 f32 x")
+    print(f"worst err/bound {r:.3e}")
+
+
+@pytest.mark.parametrize("xdtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("m", [1, 3, 16])
+def test_one_hot_columns_exact(xdtype, m):
+    rng = np.random.default_rng(1)
+    n, k = 300, 4096
+    W = torch.from_numpy((0.02 * rng.standard_normal((n, k))).astype(np.float32)).to(DEV)
+    prep, (p, s, z) = _quant_prepare(W)
+    cols = rng.choice(k, m, replace=False)
+    x = torch.zeros(m, k, dtype=xdtype, device=DEV)
+    for i, c in enumerate(cols):
+        x[i, c] = 1.0
+    y = to_np32(_run(prep, n, k, x))
+    wh = oracle.dequant_ref(p.cpu().numpy(), s.cpu().numpy(), z.cpu().numpy())
+    for i, c in enumerate(cols):
+        assert np.array_equal(y[i].astype(np.float64), wh[:, c]), f"column {c}"
+
+
+@pytest.mark.parametrize("matrix", synth.MATRIX_ORDER)
+def test_llama7b_layer_with_outlier_channels(matrix):
+    W, x = synth.llama7b_layer_matrix(matrix, device=DEV)
+    n, k = W.shape
+    prep, _ = _quant_prepare(W)
+    y = _run(prep, n, k, x)
+    yr, bound, _ = _ref_from_oracle(to_np32(W), to_np32(x))
+    r = assert_within(to_np32(y), yr, bound, f"7B {matrix}")
+    print(f"{matrix}: worst err/bound {r:.3e}")
+
+
+@pytest.mark.parametrize("matrix", synth.MATRIX_ORDER)
+def test_llama70b_layer_batches_sampled_rows(matrix):
+    W, x16 = synth.llama70b_layer_matrix(matrix, device=DEV, m=16)
+    n, k = W.shape
+    prep, _ = _quant_prepare(W)
+    rng = np.random.default_rng(23)
+    rows = np.unique(np.concatenate([[0, 1, n - 1], rng.choice(n, 256, replace=False)]))
+    W32 = to_np32(W[torch.from_numpy(rows).to(DEV)])
+    x32 = to_np32(x16)
+    p, s, z = oracle.quantize_ref(W32)
+    for m in (1, 4, 8, 16):
+        y = to_np32(_run(prep, n, k, x16[:m].contiguous()))
+        yr = oracle.gemv_ref(p, s, z, x32[:m])
+        bound = oracle.tolerance_ref(p, s, z, x32[:m])
+        r = assert_within(y[:, rows], yr, bound, f"70B {matrix} M={m}")
+        print(f"{matrix} M={m}: worst err/bound {r:.3e}")
+
+
+@pytest.mark.parametrize("n,k,m", [(1, 128, 1), (5, 256, 16), (1000, 384, 2), (77, 11008, 1),
+                                   (64, 32768, 1), (64, 32768, 5), (4099, 2048, 8)])
+def test_shapes_and_ragged_edges(n, k, m):
+    rng = np.random.default_rng(n + k + m)
+    w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
+    x = torch.from_numpy(rng.standard_normal((m, k)).astype(np.float32)).to(torch.bfloat16)
+    prep, _ = _quant_prepare(torch.from_numpy(w).to(DEV))
+    y = _run(prep, n, k, x.to(DEV))
+    yr, bound, _ = _ref_from_oracle(w, to_np32(x))
+    assert_within(to_np32(y), yr, bound, f"N={n} K={k} M={m}")
+
+
+@pytest.mark.parametrize("m", [1, 7, 16])
+def test_f32_activations_several_rows(m):
+    rng = np.random.default_rng(m)
+    n, k = 513, 20480
+    w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    prep, _ = _quant_prepare(torch.from_numpy(w).to(DEV))
+    y = _run(prep, n, k, torch.from_numpy(x).to(DEV))
+    yr, bound, _ = _ref_from_oracle(w, x)
+    assert_within(to_np32(y), yr, bound, f"f32 x M={m}")
+
+
+def test_bf16_output():
+    rng = np.random.default_rng(4)
+    n, k, m = 256, 4096, 4
+    w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
+    x = torch.from_numpy(rng.standard_normal((m, k)).astype(np.float32)).to(torch.bfloat16)
+    prep, _ = _quant_prepare(torch.from_numpy(w).to(DEV))
+    y = _run(prep, n, k, x.to(DEV), out_dtype=torch.bfloat16)
+    assert y.dtype == torch.bfloat16
+    yr, bound, _ = _ref_from_oracle(w, to_np32(x))
+    # the bf16 store adds at most half an ulp of bf16 (2^-9 relative)
+    assert_within(to_np32(y), yr, bound, "bf16 y", extra=np.abs(yr) * 2.0 ** -8)
+
+
+def test_all_zero_rows_give_exact_zero():
+    rng = np.random.default_rng(8)
+    n, k = 64, 8192
+    w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
+    w[::3] = 0.0
+    w[1, :1024] = 0.0
+    x = torch.from_numpy(rng.standard_normal((2, k)).astype(np.float32)).to(torch.bfloat16)
+    prep, _ = _quant_prepare(torch.from_numpy(w).to(DEV))
+    y = to_np32(_run(prep, n, k, x.to(DEV)))
+    assert np.all(y[:, ::3] == 0.0)
+    yr, bound, _ = _ref_from_oracle(w, to_np32(x))
+    assert_within(y, yr, bound, "rows with zero groups")
+
+
+def test_deterministic_repeat():
+    W, x = synth.llama70b_layer_matrix("q", device=DEV, m=4)
+    prep, _ = _quant_prepare(W)
+    y1 = _run(prep, 8192, 8192, x).clone()
+    y2 = _run(prep, 8192, 8192, x)
+    assert torch.equal(y1, y2)

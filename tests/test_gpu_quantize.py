@@ -1,0 +1,125 @@
+"""GPU parity of w4_quantize and the layout permutation (bit-exact against the oracle)."""
+
+import numpy as np
+import pytest
+import torch
+
+import dequant_gemv_w4_amd as w4
+import oracle
+import synth
+from _util import assert_quant_equal, oracle_quant_rows, quant_arrays_np, to_np32
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _gpu_quant(W):
+    status = torch.zeros(1, dtype=torch.int32, device=W.device)
+    p, s, z = w4.w4_quantize(W, status=status)
+    torch.cuda.synchronize()
+    return quant_arrays_np(p, s, z), int(status.item())
+
+
+def test_single_layer_4096_bit_exact():
+    w, _ = synth.page_single_layer(4096, 4096)
+    gpu, st = _gpu_quant(torch.from_numpy(w).to(DEV))
+    assert st == 0
+    assert_quant_equal(gpu, oracle.quantize_ref(w), "4096x4096 page draws")
+
+
+def _edge_rows():
+    rng = np.random.default_rng(5)
+    rows = []
+    # hand-derived tie groups repeated over a 128-group
+    for vals in ([-6.5, 8.5, 2.5, -2.5, 0.5, -0.5, 0.0, 1.5], [-1.5, -0.75, -0.05, 0.0],
+                 [3.0] * 4, [-3.0] * 4, [0.0] * 4):
+        rows.append(np.array(vals * (128 // len(vals)), dtype=np.float32))
+    # random groups whose quotients land on exact halves: multiples of s/2 with s = 1
+    t = rng.integers(-15, 16, 128).astype(np.float32) / 2
+    t[0], t[1] = -7.5, 7.5
+    rows.append(t)
+    # subnormal ranges, including scales that underflow to 0 in f32 and in fp16
+    sub = np.float32(2.0 ** -149)
+    rows.append(np.array([-3 * sub, sub, 0.0, 2 * sub] * 32, dtype=np.float32))
+    rows.append(np.array([sub, 2 * sub, 0.0, sub] * 32, dtype=np.float32))
+    rows.append((rng.standard_normal(128) * 1e-39).astype(np.float32))
+    rows.append((rng.standard_normal(128) * 1e-9).astype(np.float32))
+    # one-signed and skewed groups, outliers
+    rows.append(np.abs(rng.standard_normal(128)).astype(np.float32))
+    rows.append(-np.abs(rng.standard_normal(128)).astype(np.float32))
+    o = (0.02 * rng.standard_normal(128)).astype(np.float32)
+    o[17] = 3.0
+    rows.append(o)
+    # two groups per row: pad every row to 256 with a random group
+    out = []
+    for r in rows:
+        out.append(np.concatenate([r, (0.02 * rng.standard_normal(128)).astype(np.float32)]))
+    return np.stack(out)
+
+
+def test_edge_groups_bit_exact():
+    w = _edge_rows()
+    gpu, st = _gpu_quant(torch.from_numpy(w).to(DEV))
+    assert_quant_equal(gpu, oracle.quantize_ref(w), "edge groups")
+    assert st & w4.STATUS_SCALE_ZERO          # fp16 scale underflow reported
+    assert not st & w4.STATUS_NONFINITE
+
+
+def test_bf16_weights_bit_exact():
+    rng = np.random.default_rng(9)
+    w = torch.from_numpy((0.02 * rng.standard_normal((37, 384))).astype(np.float32)).to(torch.bfloat16)
+    gpu, st = _gpu_quant(w.to(DEV))
+    assert st == 0
+    assert_quant_equal(gpu, oracle.quantize_ref(to_np32(w)), "bf16 W, ragged 37x384")
+
+
+def test_status_bits():
+    w = torch.zeros(2, 256, device=DEV)
+    w[0, 3] = float("nan")
+    _, st = _gpu_quant(w)
+    assert st & w4.STATUS_NONFINITE
+    w = torch.zeros(1, 128, device=DEV)
+    w[0, 0], w[0, 1] = -1e6, 1e6                    # scale 133333 > fp16 max
+    _, st = _gpu_quant(w)
+    assert st & w4.STATUS_SCALE_OVERFLOW
+
+
+@pytest.mark.parametrize("matrix", synth.MATRIX_ORDER)
+def test_llama7b_matrices_bit_exact(matrix):
+    W, _ = synth.llama7b_layer_matrix(matrix, device=DEV)
+    gpu, st = _gpu_quant(W)
+    assert st == 0
+    assert_quant_equal(gpu, oracle.quantize_ref(to_np32(W)), f"7B {matrix}")
+
+
+@pytest.mark.parametrize("matrix", synth.MATRIX_ORDER)
+def test_llama70b_matrices_sampled_rows_bit_exact(matrix):
+    W, _ = synth.llama70b_layer_matrix(matrix, device=DEV)
+    gpu, st = _gpu_quant(W)
+    assert st == 0
+    n = W.shape[0]
+    rng = np.random.default_rng(17)
+    rows = np.unique(np.concatenate([[0, n - 1], rng.choice(n, 384, replace=False)]))
+    Wr = to_np32(W[torch.from_numpy(rows).to(DEV)])
+    ref = oracle.quantize_ref(Wr)
+    gp, gs, gz = gpu
+    assert_quant_equal((gp[rows], gs[rows], gz[rows]), ref, f"70B {matrix} sampled rows")
+
+
+def test_prepare_unprepare_round_trip_random_bytes():
+    g = torch.Generator(device=DEV)
+    g.manual_seed(3)
+    for n, k in [(1, 128), (37, 384), (1024, 8192), (8192, 11008 // 128 * 128)]:
+        packed = torch.randint(0, 256, (n, k // 2), dtype=torch.uint8, device=DEV, generator=g)
+        scales = torch.randint(-32768, 32767, (n, k // 128), dtype=torch.int16, device=DEV,
+                               generator=g).view(torch.float16)
+        zeros = torch.randint(0, 256, (n, k // 128), dtype=torch.uint8, device=DEV, generator=g)
+        prep = w4.w4_prepare(packed, scales, zeros)
+        assert prep.numel() == w4.w4_prepared_bytes(n, k)
+        p2, s2, z2 = w4.w4_unprepare(prep, n, k)
+        torch.cuda.synchronize()
+        assert torch.equal(p2, packed)
+        assert torch.equal(s2.view(torch.int16), scales.view(torch.int16))
+        assert torch.equal(z2, zeros)
+        # the prepared words are a permutation of the canonical nibbles
+        assert not torch.equal(prep[: packed.numel()], packed.flatten()) or n * k < 256
