@@ -5,9 +5,12 @@ Workload (one "step"): a 70B-shaped decode step at batch 1 -- 80 layers, each
 with the seven GQA matrices q/o 8192x8192, k/v 1024x8192, gate/up 28672x8192
 and down 8192x28672, quantized to asymmetric int4 with group 128 and resident
 in HBM in the kernel layout (about 36 GB); every matrix is multiplied once by
-its bf16 activation row with w4_gemv, all 560 launches back to back and
-replayed from one captured graph.  Weights are N(0, 0.02) and activations
-N(0, 1), drawn on the GPU from fixed seeds (synthetic, no checkpoint).
+its bf16 activation row with w4_gemv, back to back, replayed from one captured
+graph.  The headline step stores the same-input matrices concatenated along N
+(q|k|v as 10240x8192, gate|up as 57344x8192), so a layer is four launches
+(qkv, o, gate_up, down); the step with seven separate launches per layer is
+reported beside it.  Weights are N(0, 0.02) and activations N(0, 1), drawn on
+the GPU from fixed seeds (synthetic, no checkpoint).
 
 The printed JSON line reports the achieved HBM bandwidth of the step computed
 from algorithmic bytes (codes + fp16 scales + byte zeros + activations +
@@ -49,7 +52,12 @@ def parse_args():
     return ap.parse_args()
 
 
-def build_stack(layers: int, dev: str):
+def build_stack(layers: int, dev: str, fused: bool = False):
+    """Quantize and prepare every matrix of the stack on the GPU (weights drawn there).
+
+    With fused=True the same-input matrices are drawn as one concatenated matrix
+    (q|k|v: 10240 x 8192, gate|up: 57344 x 8192), so each group is one launch.
+    """
     import torch
 
     import dequant_gemv_w4_amd as w4
@@ -57,10 +65,13 @@ def build_stack(layers: int, dev: str):
 
     prepared = {}
     t0 = time.time()
+    order = synth.FUSED_ORDER if fused else synth.MATRIX_ORDER
+    shapes = synth.LLAMA70B_FUSED_SHAPES if fused else synth.LLAMA70B_SHAPES
     for layer in range(layers):
-        for name in synth.MATRIX_ORDER:
-            n, k = synth.LLAMA70B_SHAPES[name]
-            W = synth.normal_weights(n, k, synth.seed_for(4, name, layer), dev)
+        for name in order:
+            n, k = shapes[name]
+            seed = synth.seed_for(4, synth.FUSED_PARTS[name][0] if fused else name, layer)
+            W = synth.normal_weights(n, k, seed + (10000 if fused else 0), dev)
             p, s, z = w4.w4_quantize(W)
             prepared[(layer, name)] = w4.w4_prepare(p, s, z)
             del W, p, s, z
@@ -70,7 +81,7 @@ def build_stack(layers: int, dev: str):
     return prepared
 
 
-def make_step(prepared, layers: int, m: int, dev: str):
+def make_step(prepared, layers: int, m: int, dev: str, fused: bool = False):
     import torch
 
     import synth
@@ -84,11 +95,13 @@ def make_step(prepared, layers: int, m: int, dev: str):
         "down": synth.normal_activations(m, 28672, 40004, dev),
     }
     feed = {"q": "attn", "k": "attn", "v": "attn", "o": "o", "gate": "mlp", "up": "mlp",
-            "down": "down"}
+            "down": "down", "qkv": "attn", "gate_up": "mlp"}
+    order = synth.FUSED_ORDER if fused else synth.MATRIX_ORDER
+    shapes = synth.LLAMA70B_FUSED_SHAPES if fused else synth.LLAMA70B_SHAPES
     calls = []
     for layer in range(layers):
-        for name in synth.MATRIX_ORDER:
-            n, k = synth.LLAMA70B_SHAPES[name]
+        for name in order:
+            n, k = shapes[name]
             y = torch.empty(m, n, dtype=torch.float32, device=dev)
             calls.append(GemvCall(prepared[(layer, name)], n, k, xs[feed[name]], y))
     return DecodeStep(calls)
@@ -111,15 +124,17 @@ def time_step(step, steps: int, warmup: int) -> float:
     return start.elapsed_time(end) / steps
 
 
-def per_shape(prepared, layers: int, dev: str, reps: int = 3):
+def per_shape(prepared, layers: int, dev: str, reps: int = 3, fused: bool = False):
     """Isolated GB/s per matrix shape: the same shape across all layers, back to back."""
     import synth
     from dequant_gemv_w4_amd.decode import DecodeStep, GemvCall
     import torch
 
     out = {}
-    for name in synth.MATRIX_ORDER:
-        n, k = synth.LLAMA70B_SHAPES[name]
+    order = synth.FUSED_ORDER if fused else synth.MATRIX_ORDER
+    shapes = synth.LLAMA70B_FUSED_SHAPES if fused else synth.LLAMA70B_SHAPES
+    for name in order:
+        n, k = shapes[name]
         x = synth.normal_activations(1, k, 40100, dev)
         calls = [GemvCall(prepared[(layer, name)], n, k, x,
                           torch.empty(1, n, dtype=torch.float32, device=dev))
@@ -225,10 +240,10 @@ def main() -> int:
     dev = "cuda:0"
     torch.cuda.set_device(0)
     w4.lib()
-    log(f"device {torch.cuda.get_device_name(0)}; building {args.layers} layers")
-    prepared = build_stack(args.layers, dev)
+    log(f"device {torch.cuda.get_device_name(0)}; building {args.layers} fused layers")
+    prepared = build_stack(args.layers, dev, fused=True)
 
-    step = make_step(prepared, args.layers, 1, dev)
+    step = make_step(prepared, args.layers, 1, dev, fused=True)
     if not args.no_graph:
         step.capture()
         log("captured the step into a graph")
@@ -252,7 +267,9 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "llama70b-shaped decode step: 80 layers x {q,k,v,o,gate,up,down} w4_gemv, M=1",
+            "workload": "llama70b-shaped decode step, batch 1: 80 layers x w4_gemv over "
+                        "qkv 10240x8192 (q|k|v concatenated), o 8192x8192, gate_up 57344x8192 "
+                        "(gate|up concatenated), down 8192x28672",
             "layers": args.layers,
             "gemv_launches_per_step": launches,
             "batch": 1,
@@ -270,7 +287,7 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(gbs / HBM_PEAK_GBS, 4),
             "traffic": None,
-            "kernel": "w4_gemv (gemv_kernel<1,false,1,1024>)",
+            "kernel": "w4_gemv (gemv_kernel, M=1 bf16 variants)",
             "per_launch": f"{nbytes / launches / 1e6:.2f} MB algorithmic in "
                           f"{ms * 1000 / launches:.2f} us average (step time / launches)",
         },
@@ -279,7 +296,7 @@ def main() -> int:
     if not args.skip_extras:
         batches = {}
         for m in (4, 8, 16):
-            st = make_step(prepared, args.layers, m, dev)
+            st = make_step(prepared, args.layers, m, dev, fused=True)
             st.capture()
             msm = time_step(st, max(2, args.steps // 4), 1)
             batches[str(m)] = {"ms_per_step": round(msm, 3),
@@ -287,11 +304,26 @@ def main() -> int:
                                "tokens_per_s": round(1000.0 * m / msm, 1)}
             del st
             log(f"M={m}: {msm:.3f} ms/step")
-        result["batch_sweep"] = batches
-        result["per_shape_m1"] = per_shape(prepared, args.layers, dev)
+        result["batch_sweep_fused"] = batches
+        result["per_shape_fused_m1"] = per_shape(prepared, args.layers, dev, fused=True)
+        del step, prepared
+        torch.cuda.empty_cache()
+        log("building the unfused stack")
+        unfused = build_stack(args.layers, dev, fused=False)
+        st = make_step(unfused, args.layers, 1, dev, fused=False)
+        st.capture()
+        msu = time_step(st, max(2, args.steps // 2), 2)
+        result["unfused_step_m1"] = {
+            "launches_per_step": len(st.calls), "ms_per_step": round(msu, 4),
+            "GB/s": round(st.algorithmic_bytes() / (msu * 1e-3) / 1e9, 1),
+            "pct_of_hbm_peak": round(100 * st.algorithmic_bytes() / (msu * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
+        del st
+        result["per_shape_m1"] = per_shape(unfused, args.layers, dev)
         log("per-shape done")
-        result["prefill_gemm"] = prefill_gemm(prepared, dev)
+        result["prefill_gemm"] = prefill_gemm(unfused, dev)
         log(f"prefill GEMM: {result['prefill_gemm']}")
+        del unfused
+        torch.cuda.empty_cache()
         result["quantizer"] = quantizer_rate(dev)
 
     if not args.no_cpu_baseline:

@@ -86,10 +86,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ w
                                                                 kg * (BK / 2) + h * 32);
                 a = p[0];
                 b = p[1];
-                szv = sz[(int64_t)row * Kg + kg];
+                szv = sz[sz_index(row, kg, Kg)];
             }
             const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)(szv & 0xFFFFu));
-            const float z = (float)((szv >> 16) & 0xFFu);
+            const float z = (float)((szv >> 16) & 0xFFu) - 128.0f;
             const uint32_t words[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
             uint32_t out[32];
 #pragma unroll

@@ -14,20 +14,27 @@
 //     pairs for the whole workgroup, so each row costs one 16-byte load per
 //     lane and a wave load covers 1 KiB of contiguous weights;
 //   * a workgroup holds ceil(K/2048) waves and walks rows_per_wg rows, four at
-//     a time, prefetching the next four rows while it computes the current;
-//   * unpack: (word >> 4j) & 0x000F000F | 0x43004300 turns the two codes of an
-//     input pair into the bf16 values 128+q, and v_dot2_f32_bf16 multiplies the
-//     pair by the matching x pair and accumulates in f32: D = sum (128+q)*x.
-//     The slice sum S = sum x is computed once per workgroup by the same
-//     instruction sequence with the pair (1, 1), so the slice's share of the
-//     group term is scale16 * (D - (128 + zero) * S) = scale16 * (sum q*x -
-//     zero * sum x).  Because scaling by 128 commutes with rounding, a slice
-//     whose codes are all 0 gives D = 128*S exactly and contributes exactly 0;
-//     a one-hot x gives exactly (q - zero) * scale16;
-//   * reduction: across lanes with a transposed butterfly over the four rows,
-//     then across waves through LDS; no atomics, so results are deterministic.
+//     a time; NBUF steps of loads are in flight (static buffer indices, no
+//     register copies), and the first ones are issued before x is loaded;
+//   * the scale/zero words of the four rows of a step are one 16-byte load;
+//   * unpack: v_and_or_b32((word >> 4j), 0x000F000F, 0x43004300) turns the two
+//     codes of an input pair into the bf16 values 128+q, and v_dot2_f32_bf16
+//     multiplies the pair by the matching x pair and accumulates in f32:
+//     D = sum (128+q)*x.  The slice sum S = sum x is computed once per
+//     workgroup by the same instruction sequence with the pair (1, 1), so the
+//     slice's share of the group term is scale16 * (D - (128 + zero) * S) =
+//     scale16 * (sum q*x - zero * sum x).  Because scaling by 128 commutes
+//     with rounding, a slice whose codes are all 0 gives D = 128*S exactly and
+//     contributes exactly 0, and a one-hot x gives exactly (q - zero)*scale16;
+//   * reduction of the four rows across the wave: v_permlane32_swap and
+//     v_permlane16_swap transpose-and-add (each lane ends with one row), DPP
+//     row rotations finish the 16-lane sums; waves are combined through LDS.
+//     No atomics, so results are deterministic.
 // Binary32 activations are split into two bf16 parts (hi = bf16(x),
 // lo = bf16(x - hi)) that are accumulated separately and added at the end.
+#include <atomic>
+#include <cstdlib>
+
 #include "w4_internal.h"
 
 namespace w4 {
@@ -36,11 +43,10 @@ namespace {
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
+constexpr int kRowsPerStep = 4;
+
 // one 16-byte weight slice, marked non-temporal: every byte is read exactly once
 __device__ __forceinline__ u32x4_t load_stream(const u32x4_t* p) { return __builtin_nontemporal_load(p); }
-
-constexpr int kRowsPerStep = 4;
-constexpr int kMaxThreads = 1024;
 
 __device__ __forceinline__ float dot2(uint32_t w, uint32_t x, float acc) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w),
@@ -61,13 +67,51 @@ __device__ __forceinline__ float pair_sum(const uint32_t (&p)[16]) {
     return d;
 }
 
-template <int MT, bool XF32, int SPT, int MAXT>
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                                 0xF, 0xF, false));
+}
+
+// exchange the upper 32 lanes of a with the lower 32 lanes of b
+__device__ __forceinline__ void swap32(float& a, float& b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, a),
+                                                    __builtin_bit_cast(uint32_t, b), false, false);
+    a = __builtin_bit_cast(float, (uint32_t)r[0]);
+    b = __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
+// exchange the odd 16-lane rows of a with the even 16-lane rows of b
+__device__ __forceinline__ void swap16(float& a, float& b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, a),
+                                                    __builtin_bit_cast(uint32_t, b), false, false);
+    a = __builtin_bit_cast(float, (uint32_t)r[0]);
+    b = __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
+// four per-lane row values -> lane l holds the wave-wide sum of row (l >> 4) & 3
+__device__ __forceinline__ float reduce4(float a0, float a1, float a2, float a3) {
+    swap32(a0, a2);
+    swap32(a1, a3);
+    float k0 = a0 + a2;  // lanes 0-31: row 0, lanes 32-63: row 2
+    float k1 = a1 + a3;  // lanes 0-31: row 1, lanes 32-63: row 3
+    swap16(k0, k1);
+    float k = k0 + k1;   // 16-lane row r of the wave holds output row r
+    k += dpp<0x128>(k);  // row_ror:8
+    k += dpp<0x124>(k);  // row_ror:4
+    k += dpp<0x122>(k);  // row_ror:2
+    k += dpp<0x121>(k);  // row_ror:1
+    return k;
+}
+
+template <int MT, bool XF32, int SPT, int MAXT, int NBUF, bool RAGGED>
 __global__ __launch_bounds__(MAXT) void gemv_kernel(const u32x4_t* __restrict__ wq,
-                                                    const uint32_t* __restrict__ sz,
+                                                    const u32x4_t* __restrict__ sz4,
                                                     const void* __restrict__ xv,
                                                     void* __restrict__ yv, int y_bf16, int N,
                                                     int K, int M, int rows_per_wg) {
     constexpr int XE = XF32 ? 2 * MT : MT;  // bf16 operand rows
+    constexpr int R = kRowsPerStep;
     extern __shared__ float red[];          // [waves][rows_per_wg][XE]
 
     const int S = K >> 5;
@@ -76,15 +120,46 @@ __global__ __launch_bounds__(MAXT) void gemv_kernel(const u32x4_t* __restrict__ 
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int n_waves = T >> 6;
+    const int r0 = blockIdx.x * rows_per_wg;
+    const int r_end = min(N, r0 + rows_per_wg);
+    const int nsteps = (r_end - r0 + R - 1) / R;
 
-    // slice j of this lane is threadIdx.x + j*T (16 bytes of every row)
+    // slice j of this lane is threadIdx.x + j*T (16 bytes of every row).  With a ragged
+    // K the lanes past the last slice read the last slice and their x is zero.
     int sl[SPT];
     bool act[SPT];
+    uint32_t woff[SPT], soff[SPT];
 #pragma unroll
     for (int j = 0; j < SPT; ++j) {
         sl[j] = threadIdx.x + j * T;
-        act[j] = sl[j] < S;
+        act[j] = RAGGED ? sl[j] < S : true;
+        const int slc = RAGGED ? min(sl[j], S - 1) : sl[j];
+        woff[j] = (uint32_t)slc * 16u;
+        soff[j] = (uint32_t)(slc >> 2) * 16u;
     }
+
+    u32x4_t wb[NBUF][R][SPT];
+    u32x4_t sb[NBUF][SPT];
+    const char* wbase = reinterpret_cast<const char*>(wq);
+    const char* sbase = reinterpret_cast<const char*>(sz4);
+    const int64_t row_bytes = (int64_t)S * 16;
+    // loads of one step (four rows; rows past the end repeat the last row and are never stored)
+    auto issue = [&](u32x4_t (&w)[R][SPT], u32x4_t (&sw)[SPT], int step) {
+        const int rb = r0 + step * R;
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr) {
+            const char* rowp = wbase + (int64_t)min(rb + rr, r_end - 1) * row_bytes;
+#pragma unroll
+            for (int j = 0; j < SPT; ++j)
+                w[rr][j] = load_stream(reinterpret_cast<const u32x4_t*>(rowp + woff[j]));
+        }
+        const char* srow = sbase + (int64_t)(rb >> 2) * Kg * 16;
+#pragma unroll
+        for (int j = 0; j < SPT; ++j) sw[j] = *reinterpret_cast<const u32x4_t*>(srow + soff[j]);
+    };
+#pragma unroll
+    for (int b = 0; b < NBUF; ++b)
+        if (b < nsteps) issue(wb[b], sb[b], b);
 
     // ---- x slices in registers, plus sum(x) of each slice
     uint32_t xr[SPT][XE][16];
@@ -93,7 +168,7 @@ __global__ __launch_bounds__(MAXT) void gemv_kernel(const u32x4_t* __restrict__ 
     for (int j = 0; j < SPT; ++j) {
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-            const bool ok = act[j] && m < M;
+            const bool ok = act[j] && m < M;  // zero x for idle lanes and absent rows
             if constexpr (XF32) {
                 const float4* px = reinterpret_cast<const float4*>(
                     static_cast<const float*>(xv) + (int64_t)m * K + (int64_t)sl[j] * 32);
@@ -128,55 +203,30 @@ __global__ __launch_bounds__(MAXT) void gemv_kernel(const u32x4_t* __restrict__ 
         for (int e = 0; e < XE; ++e) sx[j][e] = pair_sum(xr[j][e]);
     }
 
-    const int r0 = blockIdx.x * rows_per_wg;
-    const int r_end = min(N, r0 + rows_per_wg);
-    const bool up32 = (lane & 32) != 0;
-    const bool up16 = (lane & 16) != 0;
+    // constants of the unpack kept in registers so v_and_or_b32 is selected
+    uint32_t nib_mask, bias_bits;
+    asm volatile("s_mov_b32 %0, 0x000F000F" : "=s"(nib_mask));
+    asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(bias_bits));
 
-    const u32x4_t zero4 = {0u, 0u, 0u, 0u};
-    u32x4_t wcur[kRowsPerStep][SPT];
-    uint32_t scur[kRowsPerStep][SPT];
+    auto compute = [&](const u32x4_t (&w)[R][SPT], const u32x4_t (&sw)[SPT], int step) {
+        float acc[R][XE];
 #pragma unroll
-    for (int rr = 0; rr < kRowsPerStep; ++rr) {
-        const int row = r0 + rr;
-#pragma unroll
-        for (int j = 0; j < SPT; ++j) {
-            const bool ok = act[j] && row < r_end;
-            wcur[rr][j] = ok ? load_stream(wq + (int64_t)row * S + sl[j]) : zero4;
-            scur[rr][j] = ok ? sz[(int64_t)row * Kg + (sl[j] >> 2)] : 0u;
-        }
-    }
-
-    for (int rb = r0; rb < r_end; rb += kRowsPerStep) {
-        // prefetch the next four rows
-        u32x4_t wnext[kRowsPerStep][SPT];
-        uint32_t snext[kRowsPerStep][SPT];
-#pragma unroll
-        for (int rr = 0; rr < kRowsPerStep; ++rr) {
-            const int row = rb + kRowsPerStep + rr;
-#pragma unroll
-            for (int j = 0; j < SPT; ++j) {
-                const bool ok = act[j] && row < r_end;
-                wnext[rr][j] = ok ? load_stream(wq + (int64_t)row * S + sl[j]) : zero4;
-                snext[rr][j] = ok ? sz[(int64_t)row * Kg + (sl[j] >> 2)] : 0u;
-            }
-        }
-
-        float acc[kRowsPerStep][XE];
-#pragma unroll
-        for (int rr = 0; rr < kRowsPerStep; ++rr) {
+        for (int rr = 0; rr < R; ++rr)
 #pragma unroll
             for (int e = 0; e < XE; ++e) acc[rr][e] = 0.0f;
 #pragma unroll
-            for (int j = 0; j < SPT; ++j) {
+        for (int j = 0; j < SPT; ++j) {
+#pragma unroll
+            for (int rr = 0; rr < R; ++rr) {
+                const uint32_t szw = sw[j][rr];
+                const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)(szw & 0xFFFFu));
+                const float zb = (float)((szw >> 16) & 0xFFu);  // zero + 128
                 uint32_t pr[16];
 #pragma unroll
                 for (int t = 0; t < 4; ++t)
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
-                        pr[4 * t + q] = ((wcur[rr][j][t] >> (4 * q)) & 0x000F000Fu) | 0x43004300u;
-                const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)(scur[rr][j] & 0xFFFFu));
-                const float zb = (float)(((scur[rr][j] >> 16) & 0xFFu) + 128u);
+                        pr[4 * t + q] = ((w[rr][j][t] >> (4 * q)) & nib_mask) | bias_bits;
 #pragma unroll
                 for (int e = 0; e < XE; ++e) {
                     float d = 0.0f;
@@ -186,35 +236,23 @@ __global__ __launch_bounds__(MAXT) void gemv_kernel(const u32x4_t* __restrict__ 
                 }
             }
         }
-
-        // transposed butterfly: lane keeps row 2*up32 + up16, summed over the wave
+        const int rbase = step * R;
 #pragma unroll
         for (int e = 0; e < XE; ++e) {
-            float k0 = up32 ? acc[2][e] : acc[0][e];
-            float s0 = up32 ? acc[0][e] : acc[2][e];
-            float k1 = up32 ? acc[3][e] : acc[1][e];
-            float s1 = up32 ? acc[1][e] : acc[3][e];
-            k0 += __shfl_xor(s0, 32);
-            k1 += __shfl_xor(s1, 32);
-            float k = up16 ? k1 : k0;
-            const float sd = up16 ? k0 : k1;
-            k += __shfl_xor(sd, 16);
-            k += __shfl_xor(k, 8);
-            k += __shfl_xor(k, 4);
-            k += __shfl_xor(k, 2);
-            k += __shfl_xor(k, 1);
-            if ((lane & 15) == 0) {
-                const int rloc = rb - r0 + (up32 ? 2 : 0) + (up16 ? 1 : 0);
-                red[(wave * rows_per_wg + rloc) * XE + e] = k;
+            const float k = reduce4(acc[0][e], acc[1][e], acc[2][e], acc[3][e]);
+            if ((lane & 15) == 0) red[(wave * rows_per_wg + rbase + (lane >> 4)) * XE + e] = k;
+        }
+    };
+
+    for (int step0 = 0; step0 < nsteps; step0 += NBUF) {
+#pragma unroll
+        for (int b = 0; b < NBUF; ++b) {
+            const int step = step0 + b;
+            if (step < nsteps) {
+                compute(wb[b], sb[b], step);
+                if (step + NBUF < nsteps) issue(wb[b], sb[b], step + NBUF);
             }
         }
-#pragma unroll
-        for (int rr = 0; rr < kRowsPerStep; ++rr)
-#pragma unroll
-            for (int j = 0; j < SPT; ++j) {
-                wcur[rr][j] = wnext[rr][j];
-                scur[rr][j] = snext[rr][j];
-            }
     }
     __syncthreads();
 
@@ -241,54 +279,111 @@ __global__ __launch_bounds__(MAXT) void gemv_kernel(const u32x4_t* __restrict__ 
 
 struct GemvArgs {
     const u32x4_t* wq;
-    const uint32_t* sz;
+    const u32x4_t* sz4;
     const void* x;
     void* y;
     int y_bf16, n, k, m, rows;
 };
 
-template <int MT, bool XF32, int SPT, int MAXT>
-hipError_t launch_one(const GemvArgs& a, dim3 grid, dim3 block, size_t shmem, hipStream_t s) {
-    hipLaunchKernelGGL((gemv_kernel<MT, XF32, SPT, MAXT>), grid, block, shmem, s, a.wq, a.sz, a.x,
-                       a.y, a.y_bf16, a.n, a.k, a.m, a.rows);
+int env_int(const char* name, int dflt) {
+    const char* e = getenv(name);
+    return e ? atoi(e) : dflt;
+}
+
+constexpr int kMaxRowsPerWg = 64;
+
+int compute_units() {
+    static std::atomic<int> cached{0};
+    int v = cached.load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        cus = 256;
+    cached.store(cus, std::memory_order_relaxed);
+    return cus;
+}
+
+// Rows per workgroup chosen so that the grid is one round of resident workgroups:
+// every workgroup starts at once, streams its rows, and no second wave of
+// workgroups pays the start-up latency again.
+template <typename Kern>
+int rows_for(Kern kernel, int block, int n, int xe, std::atomic<int>* cache) {
+    const int waves = block / 64;
+    int resident = cache[waves].load(std::memory_order_relaxed);
+    if (resident == 0) {
+        const size_t smem = (size_t)waves * kMaxRowsPerWg * xe * sizeof(float);
+        int r = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&r, kernel, block, smem) != hipSuccess || r < 1)
+            r = 1;
+        cache[waves].store(r, std::memory_order_relaxed);
+        resident = r;
+    }
+    static const int forced = env_int("W4A16_GEMV_ROWS", 0);
+    static const int rounds = env_int("W4A16_GEMV_ROUNDS", 1);
+    int rows;
+    if (forced > 0) {
+        rows = forced;
+    } else {
+        const long wgs = (long)resident * compute_units() * (rounds > 0 ? rounds : 1);
+        rows = (int)((n + wgs - 1) / wgs);
+    }
+    rows = (rows + kRowsPerStep - 1) / kRowsPerStep * kRowsPerStep;
+    if (rows < kRowsPerStep) rows = kRowsPerStep;
+    if (rows > kMaxRowsPerWg) rows = kMaxRowsPerWg;
+    return rows;
+}
+
+template <int MT, bool XF32, int SPT, int MAXT, int NBUF, bool RAGGED>
+hipError_t launch_var(GemvArgs a, dim3 block, hipStream_t s) {
+    constexpr int XE = XF32 ? 2 * MT : MT;
+    static std::atomic<int> cache[17];
+    auto kern = gemv_kernel<MT, XF32, SPT, MAXT, NBUF, RAGGED>;
+    a.rows = rows_for(kern, (int)block.x, a.n, XE, cache);
+    const dim3 grid((unsigned)((a.n + a.rows - 1) / a.rows));
+    const size_t shmem = (size_t)(block.x / 64) * a.rows * XE * sizeof(float);
+    hipLaunchKernelGGL(kern, grid, block, shmem, s, a.wq, a.sz4, a.x, a.y, a.y_bf16, a.n, a.k, a.m,
+                       a.rows);
     return hipGetLastError();
 }
 
-// Instantiated variants (MT = rows of x per launch, SPT = 16-byte slices per lane):
-//   M=1 bf16:          SPT 1, up to 1024 threads (K <= 32768)
-//   otherwise:         up to 512 threads; SPT 1 for K <= 16384, SPT 2 up to 32768;
-//                      MT up to 8 (bf16, SPT 1), 2 (bf16, SPT 2), 3 (f32, SPT 1), 1 (f32, SPT 2)
-//                      so that the x registers fit the 256-VGPR budget of a 512-thread group.
-int max_mt(bool x_f32, int spt) {
-    if (!x_f32) return spt == 1 ? 8 : 2;
-    return spt == 1 ? 3 : 1;
+template <int MT, bool XF32, int SPT, int MAXT, int NBUF>
+hipError_t launch_one(const GemvArgs& a, dim3 block, hipStream_t s) {
+    const bool ragged = (int)block.x * SPT * 32 != a.k;
+    return ragged ? launch_var<MT, XF32, SPT, MAXT, NBUF, true>(a, block, s)
+                  : launch_var<MT, XF32, SPT, MAXT, NBUF, false>(a, block, s);
 }
 
-hipError_t dispatch(bool x_f32, int spt, int mt, const GemvArgs& a, dim3 grid, dim3 block,
-                    size_t shmem, hipStream_t s) {
-#define W4_CASE(MTV, XF, SP, MX) \
-    if (mt == MTV && x_f32 == XF && spt == SP) return launch_one<MTV, XF, SP, MX>(a, grid, block, shmem, s);
-    if (!x_f32 && mt == 1 && block.x > 512) return launch_one<1, false, 1, 1024>(a, grid, block, shmem, s);
-    W4_CASE(1, false, 1, 512) W4_CASE(2, false, 1, 512) W4_CASE(3, false, 1, 512)
-    W4_CASE(4, false, 1, 512) W4_CASE(5, false, 1, 512) W4_CASE(6, false, 1, 512)
-    W4_CASE(7, false, 1, 512) W4_CASE(8, false, 1, 512)
-    W4_CASE(1, false, 2, 512) W4_CASE(2, false, 2, 512)
-    W4_CASE(1, true, 1, 512) W4_CASE(2, true, 1, 512) W4_CASE(3, true, 1, 512)
-    W4_CASE(1, true, 2, 512)
+// Instantiated variants (MT = rows of x per launch, SPT = 16-byte slices per lane):
+//   M=1 bf16:   SPT 1, up to 1024 threads (K <= 32768), 2 or 3 steps in flight
+//   otherwise:  up to 512 threads; SPT 1 for K <= 16384, SPT 2 up to 32768; 2 steps in
+//               flight (1 for the SPT 2 variants with two x rows); MT up to 4 (bf16, SPT 1),
+//               2 (bf16, SPT 2 / f32, SPT 1), 1 (f32, SPT 2) so that the registers fit the
+//               256-VGPR budget of a 512-thread group
+int max_mt(bool x_f32, int spt) {
+    if (!x_f32) return spt == 1 ? 4 : 2;
+    return spt == 1 ? 2 : 1;
+}
+
+hipError_t dispatch(bool x_f32, int spt, int mt, const GemvArgs& a, dim3 block, hipStream_t s) {
+    static const int nbuf = env_int("W4A16_GEMV_NBUF", 2);
+    if (!x_f32 && mt == 1 && spt == 1) {
+        if (block.x > 512)
+            return nbuf == 3 ? launch_one<1, false, 1, 1024, 3>(a, block, s)
+                             : launch_one<1, false, 1, 1024, 2>(a, block, s);
+        if (nbuf == 3) return launch_one<1, false, 1, 512, 3>(a, block, s);
+        if (nbuf == 4) return launch_one<1, false, 1, 512, 4>(a, block, s);
+        return launch_one<1, false, 1, 512, 2>(a, block, s);
+    }
+#define W4_CASE(MTV, XF, SP, NB) \
+    if (mt == MTV && x_f32 == XF && spt == SP) return launch_one<MTV, XF, SP, 512, NB>(a, block, s);
+    W4_CASE(2, false, 1, 2) W4_CASE(3, false, 1, 2) W4_CASE(4, false, 1, 2)
+    W4_CASE(1, false, 2, 2) W4_CASE(2, false, 2, 1)
+    W4_CASE(1, true, 1, 2) W4_CASE(2, true, 1, 2)
+    W4_CASE(1, true, 2, 1)
 #undef W4_CASE
     return hipErrorInvalidValue;
-}
-
-int rows_per_workgroup(int64_t n) {
-    static const int forced = [] {
-        const char* e = getenv("W4A16_GEMV_ROWS");
-        return e ? atoi(e) : 0;
-    }();
-    int r = forced > 0 ? forced : (int)(n / 512);
-    r = r / kRowsPerStep * kRowsPerStep;
-    if (r < kRowsPerStep) r = kRowsPerStep;
-    if (r > 64) r = 64;
-    return r;
 }
 
 }  // namespace
@@ -296,15 +391,13 @@ int rows_per_workgroup(int64_t n) {
 hipError_t launch_gemv(const uint8_t* prepared, int64_t n, int64_t k, const void* x, bool x_f32,
                        int64_t m, void* y, bool y_bf16, hipStream_t s) {
     const int S = (int)(k / 32);
-    const int rows = rows_per_workgroup(n);
-    const dim3 grid((unsigned)((n + rows - 1) / rows));
     GemvArgs a;
     a.wq = reinterpret_cast<const u32x4_t*>(prepared);
-    a.sz = reinterpret_cast<const uint32_t*>(prepared + sz_offset(n, k));
+    a.sz4 = reinterpret_cast<const u32x4_t*>(prepared + sz_offset(n, k));
     a.y_bf16 = y_bf16 ? 1 : 0;
     a.n = (int)n;
     a.k = (int)k;
-    a.rows = rows;
+    a.rows = 0;
     const bool wide = !x_f32 && m == 1;      // one slice per lane, up to 1024 threads
     const int spt = wide ? 1 : (S <= 512 ? 1 : 2);
     const int waves = (S + 64 * spt - 1) / (64 * spt);
@@ -312,14 +405,12 @@ hipError_t launch_gemv(const uint8_t* prepared, int64_t n, int64_t k, const void
     const int mt_max = max_mt(x_f32, spt);
     for (int64_t m0 = 0; m0 < m; m0 += mt_max) {
         const int mc = (int)((m - m0) < mt_max ? (m - m0) : mt_max);
-        const int xe = x_f32 ? 2 * mc : mc;
-        const size_t shmem = (size_t)waves * rows * xe * sizeof(float);
         a.x = x_f32 ? (const void*)(static_cast<const float*>(x) + m0 * k)
                     : (const void*)(static_cast<const uint16_t*>(x) + m0 * k);
         a.y = y_bf16 ? (void*)(static_cast<uint16_t*>(y) + m0 * n)
                      : (void*)(static_cast<float*>(y) + m0 * n);
         a.m = mc;
-        hipError_t err = dispatch(x_f32, spt, mc, a, grid, block, shmem, s);
+        hipError_t err = dispatch(x_f32, spt, mc, a, block, s);
         if (err != hipSuccess) return err;
     }
     return hipSuccess;

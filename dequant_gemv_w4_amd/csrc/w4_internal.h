@@ -1,6 +1,6 @@
 // Internal definitions shared by the libw4a16 kernels and host code.
 //
-// Prepared ("kernel") layout, format version 1.  The canonical arrays are
+// Prepared ("kernel") layout, format version 2.  The canonical arrays are
 // rearranged so that one 16-byte load feeds 32 codes to a lane and the unpack
 // needs no data movement between lanes (page "LLM Quantization Architecture in
 // Depth" › "Kernels and memory layout: the format is a contract": packed
@@ -15,8 +15,12 @@
 //                         input pair (2j, 2j+1) in the low bits of two 16-bit
 //                         halves, the same order as a bf16 pair of x in memory.
 //   region B, offset A_bytes rounded up to 256:
-//                         N x (K/128) 32-bit words: bits 0..15 the binary16
-//                         scale, bits 16..23 the zero, bits 24..31 zero.
+//                         ceil(N/4) x (K/128) x 4 32-bit words; the word of row
+//                         n and group g is at ((n/4) * (K/128) + g) * 4 + n%4, so
+//                         the words of four consecutive rows of one group form
+//                         one 16-byte load.  Word: bits 0..15 the binary16
+//                         scale, bits 16..23 the zero plus 128 (mod 256), bits
+//                         24..31 zero.  Rows past N are zero words.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -30,8 +34,15 @@ inline __host__ __device__ int64_t packed_bytes(int64_t n, int64_t k) { return n
 inline __host__ __device__ int64_t sz_offset(int64_t n, int64_t k) {
     return (packed_bytes(n, k) + 255) / 256 * 256;
 }
+inline __host__ __device__ int64_t sz_words(int64_t n, int64_t k) {
+    return (n + 3) / 4 * 4 * (k / kGroup);
+}
 inline __host__ __device__ int64_t prepared_total(int64_t n, int64_t k) {
-    return sz_offset(n, k) + n * (k / kGroup) * 4;
+    return sz_offset(n, k) + sz_words(n, k) * 4;
+}
+// index of the scale/zero word of row n, group g
+inline __host__ __device__ int64_t sz_index(int64_t n, int64_t g, int64_t kg) {
+    return ((n >> 2) * kg + g) * 4 + (n & 3);
 }
 
 // canonical word (code i at bits 4i) -> prepared word

@@ -92,9 +92,10 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
 __global__ __launch_bounds__(256) void prepare_kernel(const uint4* __restrict__ packed,
                                                       const uint16_t* __restrict__ scales,
                                                       const uint8_t* __restrict__ zeros,
-                                                      int64_t n_vec, int64_t n_groups,
+                                                      int64_t n_vec, int64_t n_rows, int64_t kg,
                                                       uint4* __restrict__ out_words,
                                                       uint32_t* __restrict__ out_sz) {
+    const int64_t n_words = (n_rows + 3) / 4 * 4 * kg;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_vec; i += stride) {
         uint4 w = packed[i];
@@ -104,17 +105,28 @@ __global__ __launch_bounds__(256) void prepare_kernel(const uint4* __restrict__ 
         w.w = to_kernel_word(w.w);
         out_words[i] = w;
     }
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_groups; i += stride) {
-        out_sz[i] = (uint32_t)scales[i] | ((uint32_t)zeros[i] << 16);
+    // one pass over the destination words: row-group q = i / (4 kg), group g, row 4q + r
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_words; i += stride) {
+        const int64_t q = i / (4 * kg);
+        const int64_t rem = i - q * 4 * kg;
+        const int64_t g = rem >> 2;
+        const int64_t row = 4 * q + (rem & 3);
+        uint32_t v = 0;
+        if (row < n_rows) {
+            const int64_t src = row * kg + g;
+            v = (uint32_t)scales[src] | ((((uint32_t)zeros[src] + 128u) & 0xFFu) << 16);
+        }
+        out_sz[i] = v;
     }
 }
 
 __global__ __launch_bounds__(256) void unprepare_kernel(const uint4* __restrict__ words,
                                                         const uint32_t* __restrict__ sz,
-                                                        int64_t n_vec, int64_t n_groups,
+                                                        int64_t n_vec, int64_t n_rows, int64_t kg,
                                                         uint4* __restrict__ packed,
                                                         uint16_t* __restrict__ scales,
                                                         uint8_t* __restrict__ zeros) {
+    const int64_t n_groups = n_rows * kg;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_vec; i += stride) {
         uint4 w = words[i];
@@ -125,9 +137,10 @@ __global__ __launch_bounds__(256) void unprepare_kernel(const uint4* __restrict_
         packed[i] = w;
     }
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_groups; i += stride) {
-        const uint32_t v = sz[i];
+        const int64_t row = i / kg;
+        const uint32_t v = sz[sz_index(row, i - row * kg, kg)];
         scales[i] = (uint16_t)(v & 0xFFFFu);
-        zeros[i] = (uint8_t)((v >> 16) & 0xFFu);
+        zeros[i] = (uint8_t)(((v >> 16) - 128u) & 0xFFu);
     }
 }
 
@@ -156,10 +169,10 @@ hipError_t launch_quantize(const void* W, bool bf16, int64_t n_groups, uint8_t* 
 hipError_t launch_prepare(const uint8_t* packed, const uint16_t* scales, const uint8_t* zeros,
                           int64_t n, int64_t k, uint8_t* prepared, hipStream_t s) {
     const int64_t n_vec = packed_bytes(n, k) / 16;
-    const int64_t n_groups = n * (k / kGroup);
-    const int64_t blocks = elementwise_blocks(n_vec > n_groups ? n_vec : n_groups);
+    const int64_t n_words = sz_words(n, k);
+    const int64_t blocks = elementwise_blocks(n_vec > n_words ? n_vec : n_words);
     hipLaunchKernelGGL(prepare_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
-                       reinterpret_cast<const uint4*>(packed), scales, zeros, n_vec, n_groups,
+                       reinterpret_cast<const uint4*>(packed), scales, zeros, n_vec, n, k / kGroup,
                        reinterpret_cast<uint4*>(prepared),
                        reinterpret_cast<uint32_t*>(prepared + sz_offset(n, k)));
     return hipGetLastError();
@@ -173,7 +186,7 @@ hipError_t launch_unprepare(const uint8_t* prepared, int64_t n, int64_t k, uint8
     hipLaunchKernelGGL(unprepare_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
                        reinterpret_cast<const uint4*>(prepared),
                        reinterpret_cast<const uint32_t*>(prepared + sz_offset(n, k)), n_vec,
-                       n_groups, reinterpret_cast<uint4*>(packed), scales, zeros);
+                       n, k / kGroup, reinterpret_cast<uint4*>(packed), scales, zeros);
     return hipGetLastError();
 }
 

@@ -48,7 +48,7 @@ extern "C" {
 #endif
 
 #define W4_GROUP 128
-#define W4_FORMAT_VERSION 1
+#define W4_FORMAT_VERSION 2
 #define W4_GEMV_MAX_M 16
 #define W4_GEMV_MAX_K 32768
 

@@ -38,6 +38,11 @@ LLAMA70B_SHAPES = {
     "gate": (28672, 8192), "up": (28672, 8192), "down": (8192, 28672),
 }
 MATRIX_ORDER = ("q", "k", "v", "o", "gate", "up", "down")
+# same-input matrices concatenated along N (one launch per group)
+LLAMA70B_FUSED_SHAPES = {"qkv": (10240, 8192), "o": (8192, 8192), "gate_up": (57344, 8192),
+                         "down": (8192, 28672)}
+FUSED_ORDER = ("qkv", "o", "gate_up", "down")
+FUSED_PARTS = {"qkv": ("q", "k", "v"), "o": ("o",), "gate_up": ("gate", "up"), "down": ("down",)}
 
 
 def seed_for(workload: int, matrix: str, layer: int = 0) -> int:

@@ -21,16 +21,18 @@ def test_library_loads_and_exports_declared_symbols():
 
 
 def test_format_version_and_status_strings():
-    assert w4.w4_format_version() == 1
+    assert w4.w4_format_version() == 2
     assert w4.w4_status_string(0) == "ok"
     assert "gfx950" in w4.w4_status_string(6)
     assert w4.w4_status_string(99) == "unknown status"
 
 
 def test_prepared_bytes_closed_form():
-    # packed bytes rounded up to 256, then one 32-bit scale/zero word per group
+    # packed bytes rounded up to 256, then one 32-bit scale/zero word per group,
+    # rows padded to a multiple of four
     assert w4.w4_prepared_bytes(8192, 8192) == 8192 * 4096 + 8192 * 64 * 4
-    assert w4.w4_prepared_bytes(3, 384) == 768 + 3 * 3 * 4
+    assert w4.w4_prepared_bytes(3, 384) == 768 + 4 * 3 * 4
+    assert w4.w4_prepared_bytes(5, 128) == 512 + 8 * 1 * 4
     assert w4.w4_prepared_bytes(1, 100) == 0     # K not a multiple of 128
     assert w4.w4_prepared_bytes(0, 128) == 0
     assert w4.w4_gemm_workspace_bytes(4096, 28672, 8192) == 0
