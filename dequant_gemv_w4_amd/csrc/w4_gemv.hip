@@ -13,9 +13,12 @@
 //     inputs, a quarter of a group); its x values stay in registers as bf16
 //     pairs for the whole workgroup, so each row costs one 16-byte load per
 //     lane and a wave load covers 1 KiB of contiguous weights;
-//   * a workgroup holds ceil(K/2048) waves and walks rows_per_wg rows, four at
-//     a time; NBUF steps of loads are in flight (static buffer indices, no
-//     register copies), and the first ones are issued before x is loaded;
+//   * a workgroup holds ceil(K/2048) waves and walks rows_per_wg rows in
+//     chunks of CH steps of four rows; x is loaded first, then all loads of a
+//     chunk are issued before any is used (a scheduling barrier keeps them
+//     there), so step c computes while the later steps are still arriving and
+//     the compiler's in-order wait counts stay exact (no load crosses a loop
+//     iteration);
 //   * the scale/zero words of the four rows of a step are one 16-byte load;
 //   * unpack: v_and_or_b32((word >> 4j), 0x000F000F, 0x43004300) turns the two
 //     codes of an input pair into the bf16 values 128+q, and v_dot2_f32_bf16
@@ -104,7 +107,7 @@ __device__ __forceinline__ float reduce4(float a0, float a1, float a2, float a3)
     return k;
 }
 
-template <int MT, bool XF32, int SPT, int MAXT, int NBUF, bool RAGGED>
+template <int MT, bool XF32, int SPT, int MAXT, int CH, bool RAGGED>
 __global__ __launch_bounds__(MAXT) void gemv_kernel(const u32x4_t* __restrict__ wq,
                                                     const u32x4_t* __restrict__ sz4,
                                                     const void* __restrict__ xv,
@@ -122,7 +125,6 @@ __global__ __launch_bounds__(MAXT) void gemv_kernel(const u32x4_t* __restrict__ 
     const int n_waves = T >> 6;
     const int r0 = blockIdx.x * rows_per_wg;
     const int r_end = min(N, r0 + rows_per_wg);
-    const int nsteps = (r_end - r0 + R - 1) / R;
 
     // slice j of this lane is threadIdx.x + j*T (16 bytes of every row).  With a ragged
     // K the lanes past the last slice read the last slice and their x is zero.
@@ -138,37 +140,14 @@ __global__ __launch_bounds__(MAXT) void gemv_kernel(const u32x4_t* __restrict__ 
         soff[j] = (uint32_t)(slc >> 2) * 16u;
     }
 
-    u32x4_t wb[NBUF][R][SPT];
-    u32x4_t sb[NBUF][SPT];
-    const char* wbase = reinterpret_cast<const char*>(wq);
-    const char* sbase = reinterpret_cast<const char*>(sz4);
-    const int64_t row_bytes = (int64_t)S * 16;
-    // loads of one step (four rows; rows past the end repeat the last row and are never stored)
-    auto issue = [&](u32x4_t (&w)[R][SPT], u32x4_t (&sw)[SPT], int step) {
-        const int rb = r0 + step * R;
-#pragma unroll
-        for (int rr = 0; rr < R; ++rr) {
-            const char* rowp = wbase + (int64_t)min(rb + rr, r_end - 1) * row_bytes;
-#pragma unroll
-            for (int j = 0; j < SPT; ++j)
-                w[rr][j] = load_stream(reinterpret_cast<const u32x4_t*>(rowp + woff[j]));
-        }
-        const char* srow = sbase + (int64_t)(rb >> 2) * Kg * 16;
-#pragma unroll
-        for (int j = 0; j < SPT; ++j) sw[j] = *reinterpret_cast<const u32x4_t*>(srow + soff[j]);
-    };
-#pragma unroll
-    for (int b = 0; b < NBUF; ++b)
-        if (b < nsteps) issue(wb[b], sb[b], b);
-
-    // ---- x slices in registers, plus sum(x) of each slice
+    // ---- x slices first: their loads complete before the weight stream that follows
     uint32_t xr[SPT][XE][16];
     float sx[SPT][XE];
 #pragma unroll
     for (int j = 0; j < SPT; ++j) {
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-            const bool ok = act[j] && m < M;  // zero x for idle lanes and absent rows
+            const bool ok = act[j] && (MT == 1 || m < M);  // zero x for idle lanes and absent rows
             if constexpr (XF32) {
                 const float4* px = reinterpret_cast<const float4*>(
                     static_cast<const float*>(xv) + (int64_t)m * K + (int64_t)sl[j] * 32);
@@ -199,60 +178,102 @@ __global__ __launch_bounds__(MAXT) void gemv_kernel(const u32x4_t* __restrict__ 
                 }
             }
         }
-#pragma unroll
-        for (int e = 0; e < XE; ++e) sx[j][e] = pair_sum(xr[j][e]);
     }
+
+    __builtin_amdgcn_sched_barrier(0);  // keep the x loads ahead of the weight stream
 
     // constants of the unpack kept in registers so v_and_or_b32 is selected
     uint32_t nib_mask, bias_bits;
     asm volatile("s_mov_b32 %0, 0x000F000F" : "=s"(nib_mask));
     asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(bias_bits));
 
-    auto compute = [&](const u32x4_t (&w)[R][SPT], const u32x4_t (&sw)[SPT], int step) {
-        float acc[R][XE];
+    const char* wbase = reinterpret_cast<const char*>(wq);
+    const char* sbase = reinterpret_cast<const char*>(sz4);
+    const int64_t row_bytes = (int64_t)S * 16;
+
+    // rows_per_wg is a multiple of CH*4: every chunk is whole; rows past N repeat row N-1
+    // (their sums are never stored)
+    u32x4_t wb[CH][R][SPT];
+    u32x4_t sb[CH][SPT];
+    auto issue_chunk = [&](int c0) {
 #pragma unroll
-        for (int rr = 0; rr < R; ++rr)
+        for (int c = 0; c < CH; ++c) {
+            const int rb = r0 + c0 + c * R;
+            const char* srow = sbase + (int64_t)(min(rb, N - 1) >> 2) * Kg * 16;
 #pragma unroll
-            for (int e = 0; e < XE; ++e) acc[rr][e] = 0.0f;
-#pragma unroll
-        for (int j = 0; j < SPT; ++j) {
+            for (int j = 0; j < SPT; ++j) sb[c][j] = *reinterpret_cast<const u32x4_t*>(srow + soff[j]);
 #pragma unroll
             for (int rr = 0; rr < R; ++rr) {
-                const uint32_t szw = sw[j][rr];
-                const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)(szw & 0xFFFFu));
-                const float zb = (float)((szw >> 16) & 0xFFu);  // zero + 128
-                uint32_t pr[16];
+                const char* rowp = wbase + (int64_t)min(rb + rr, N - 1) * row_bytes;
 #pragma unroll
-                for (int t = 0; t < 4; ++t)
+                for (int j = 0; j < SPT; ++j)
+                    wb[c][rr][j] = load_stream(reinterpret_cast<const u32x4_t*>(rowp + woff[j]));
+            }
+            // loads stay in step order, so step c only waits for its own loads
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // every load of the chunk is issued before any of it is used: step c computes while
+        // the loads of the later steps are still in flight
+    };
+    auto compute_chunk = [&](int c0) {
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        pr[4 * t + q] = ((w[rr][j][t] >> (4 * q)) & nib_mask) | bias_bits;
+        for (int c = 0; c < CH; ++c) {
+            float acc[R][XE];
 #pragma unroll
-                for (int e = 0; e < XE; ++e) {
-                    float d = 0.0f;
+            for (int rr = 0; rr < R; ++rr)
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) d = dot2(pr[i], xr[j][e][i], d);
-                    acc[rr][e] = fmaf(s, fmaf(-zb, sx[j][e], d), acc[rr][e]);
+                for (int e = 0; e < XE; ++e) acc[rr][e] = 0.0f;
+#pragma unroll
+            for (int j = 0; j < SPT; ++j) {
+#pragma unroll
+                for (int rr = 0; rr < R; ++rr) {
+                    const uint32_t szw = sb[c][j][rr];
+                    const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)(szw & 0xFFFFu));
+                    const float zb = (float)((szw >> 16) & 0xFFu);  // zero + 128
+                    uint32_t pr[16];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            pr[4 * t + q] = ((wb[c][rr][j][t] >> (4 * q)) & nib_mask) | bias_bits;
+#pragma unroll
+                    for (int e = 0; e < XE; ++e) {
+                        float d = 0.0f;
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) d = dot2(pr[i], xr[j][e][i], d);
+                        acc[rr][e] = fmaf(s, fmaf(-zb, sx[j][e], d), acc[rr][e]);
+                    }
                 }
             }
-        }
-        const int rbase = step * R;
+            if constexpr (RAGGED) {
+                // lanes past the last slice read real (unrelated) scales; drop their terms
+                bool any_off = false;
 #pragma unroll
-        for (int e = 0; e < XE; ++e) {
-            const float k = reduce4(acc[0][e], acc[1][e], acc[2][e], acc[3][e]);
-            if ((lane & 15) == 0) red[(wave * rows_per_wg + rbase + (lane >> 4)) * XE + e] = k;
+                for (int j = 0; j < SPT; ++j) any_off |= !act[j];
+                if (any_off)
+#pragma unroll
+                    for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+                        for (int e = 0; e < XE; ++e) acc[rr][e] = 0.0f;
+            }
+            const int rbase = c0 + c * R;
+#pragma unroll
+            for (int e = 0; e < XE; ++e) {
+                const float k = reduce4(acc[0][e], acc[1][e], acc[2][e], acc[3][e]);
+                if ((lane & 15) == 0) red[(wave * rows_per_wg + rbase + (lane >> 4)) * XE + e] = k;
+            }
         }
     };
 
-    for (int step0 = 0; step0 < nsteps; step0 += NBUF) {
+    issue_chunk(0);
 #pragma unroll
-        for (int b = 0; b < NBUF; ++b) {
-            const int step = step0 + b;
-            if (step < nsteps) {
-                compute(wb[b], sb[b], step);
-                if (step + NBUF < nsteps) issue(wb[b], sb[b], step + NBUF);
-            }
-        }
+    for (int j = 0; j < SPT; ++j)
+#pragma unroll
+        for (int e = 0; e < XE; ++e) sx[j][e] = pair_sum(xr[j][e]);
+    compute_chunk(0);
+    for (int c0 = CH * R; c0 < rows_per_wg; c0 += CH * R) {
+        issue_chunk(c0);
+        compute_chunk(c0);
     }
     __syncthreads();
 
@@ -305,11 +326,10 @@ int compute_units() {
     return cus;
 }
 
-// Rows per workgroup chosen so that the grid is one round of resident workgroups:
-// every workgroup starts at once, streams its rows, and no second wave of
-// workgroups pays the start-up latency again.
+// Rows per workgroup chosen from the number of resident workgroups: a whole
+// number of rounds (see below), rows a multiple of the chunk.
 template <typename Kern>
-int rows_for(Kern kernel, int block, int n, int xe, std::atomic<int>* cache) {
+int rows_for(Kern kernel, int block, int n, int xe, int chunk_rows, std::atomic<int>* cache) {
     const int waves = block / 64;
     int resident = cache[waves].load(std::memory_order_relaxed);
     if (resident == 0) {
@@ -321,26 +341,29 @@ int rows_for(Kern kernel, int block, int n, int xe, std::atomic<int>* cache) {
         resident = r;
     }
     static const int forced = env_int("W4A16_GEMV_ROWS", 0);
-    static const int rounds = env_int("W4A16_GEMV_ROUNDS", 1);
+    static const int forced_rounds = env_int("W4A16_GEMV_ROUNDS", 0);
+    // measured on MI355X: groups of up to 8 waves stream best with about three rounds of
+    // resident groups (finer work, shorter tail); the 14-wave groups of K ~ 28K with one
+    int rounds = forced_rounds > 0 ? forced_rounds : (waves <= 8 ? 3 : 1);
     int rows;
     if (forced > 0) {
         rows = forced;
     } else {
-        const long wgs = (long)resident * compute_units() * (rounds > 0 ? rounds : 1);
+        const long wgs = (long)resident * compute_units() * rounds;
         rows = (int)((n + wgs - 1) / wgs);
     }
-    rows = (rows + kRowsPerStep - 1) / kRowsPerStep * kRowsPerStep;
-    if (rows < kRowsPerStep) rows = kRowsPerStep;
-    if (rows > kMaxRowsPerWg) rows = kMaxRowsPerWg;
+    rows = (rows + chunk_rows - 1) / chunk_rows * chunk_rows;
+    if (rows < chunk_rows) rows = chunk_rows;
+    if (rows > kMaxRowsPerWg) rows = kMaxRowsPerWg / chunk_rows * chunk_rows;
     return rows;
 }
 
-template <int MT, bool XF32, int SPT, int MAXT, int NBUF, bool RAGGED>
+template <int MT, bool XF32, int SPT, int MAXT, int CH, bool RAGGED>
 hipError_t launch_var(GemvArgs a, dim3 block, hipStream_t s) {
     constexpr int XE = XF32 ? 2 * MT : MT;
     static std::atomic<int> cache[17];
-    auto kern = gemv_kernel<MT, XF32, SPT, MAXT, NBUF, RAGGED>;
-    a.rows = rows_for(kern, (int)block.x, a.n, XE, cache);
+    auto kern = gemv_kernel<MT, XF32, SPT, MAXT, CH, RAGGED>;
+    a.rows = rows_for(kern, (int)block.x, a.n, XE, CH * kRowsPerStep, cache);
     const dim3 grid((unsigned)((a.n + a.rows - 1) / a.rows));
     const size_t shmem = (size_t)(block.x / 64) * a.rows * XE * sizeof(float);
     hipLaunchKernelGGL(kern, grid, block, shmem, s, a.wq, a.sz4, a.x, a.y, a.y_bf16, a.n, a.k, a.m,
@@ -348,18 +371,19 @@ hipError_t launch_var(GemvArgs a, dim3 block, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int MT, bool XF32, int SPT, int MAXT, int NBUF>
+template <int MT, bool XF32, int SPT, int MAXT, int CH>
 hipError_t launch_one(const GemvArgs& a, dim3 block, hipStream_t s) {
     const bool ragged = (int)block.x * SPT * 32 != a.k;
-    return ragged ? launch_var<MT, XF32, SPT, MAXT, NBUF, true>(a, block, s)
-                  : launch_var<MT, XF32, SPT, MAXT, NBUF, false>(a, block, s);
+    return ragged ? launch_var<MT, XF32, SPT, MAXT, CH, true>(a, block, s)
+                  : launch_var<MT, XF32, SPT, MAXT, CH, false>(a, block, s);
 }
 
-// Instantiated variants (MT = rows of x per launch, SPT = 16-byte slices per lane):
-//   M=1 bf16:   SPT 1, up to 1024 threads (K <= 32768), 2 or 3 steps in flight
-//   otherwise:  up to 512 threads; SPT 1 for K <= 16384, SPT 2 up to 32768; 2 steps in
-//               flight (1 for the SPT 2 variants with two x rows); MT up to 4 (bf16, SPT 1),
-//               2 (bf16, SPT 2 / f32, SPT 1), 1 (f32, SPT 2) so that the registers fit the
+// Instantiated variants (MT = rows of x per launch, SPT = 16-byte slices per lane,
+// CH = steps of four rows whose loads are issued together):
+//   M=1 bf16:   SPT 1, up to 1024 threads (K <= 32768), CH 2 or 4
+//   otherwise:  up to 512 threads; SPT 1 for K <= 16384, SPT 2 up to 32768; CH 2 (1 for
+//               the SPT 2 variants with two x rows); MT up to 4 (bf16, SPT 1), 2 (bf16,
+//               SPT 2 / f32, SPT 1), 1 (f32, SPT 2) so that the registers fit the
 //               256-VGPR budget of a 512-thread group
 int max_mt(bool x_f32, int spt) {
     if (!x_f32) return spt == 1 ? 4 : 2;
@@ -367,14 +391,16 @@ int max_mt(bool x_f32, int spt) {
 }
 
 hipError_t dispatch(bool x_f32, int spt, int mt, const GemvArgs& a, dim3 block, hipStream_t s) {
-    static const int nbuf = env_int("W4A16_GEMV_NBUF", 2);
+    static const int chunk = env_int("W4A16_GEMV_CHUNK", 2);
     if (!x_f32 && mt == 1 && spt == 1) {
-        if (block.x > 512)
-            return nbuf == 3 ? launch_one<1, false, 1, 1024, 3>(a, block, s)
-                             : launch_one<1, false, 1, 1024, 2>(a, block, s);
-        if (nbuf == 3) return launch_one<1, false, 1, 512, 3>(a, block, s);
-        if (nbuf == 4) return launch_one<1, false, 1, 512, 4>(a, block, s);
-        return launch_one<1, false, 1, 512, 2>(a, block, s);
+        if (block.x > 512) {
+            if (chunk == 1) return launch_one<1, false, 1, 1024, 1>(a, block, s);
+            return chunk == 4 ? launch_one<1, false, 1, 1024, 4>(a, block, s)
+                              : launch_one<1, false, 1, 1024, 2>(a, block, s);
+        }
+        if (chunk == 1) return launch_one<1, false, 1, 512, 1>(a, block, s);
+        return chunk == 4 ? launch_one<1, false, 1, 512, 4>(a, block, s)
+                          : launch_one<1, false, 1, 512, 2>(a, block, s);
     }
 #define W4_CASE(MTV, XF, SP, NB) \
     if (mt == MTV && x_f32 == XF && spt == SP) return launch_one<MTV, XF, SP, 512, NB>(a, block, s);

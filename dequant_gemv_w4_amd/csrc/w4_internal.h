@@ -67,6 +67,36 @@ __device__ __forceinline__ uint32_t to_canonical_word(uint32_t p) {
     return e | (o << 4);
 }
 
+// ---- GEMV chain plan (device copy written by the host planner, read by chain_kernel)
+// layout: ChainHeader | ChainDesc[n_desc] | int32 stage_items[n_stages]
+struct ChainHeader {
+    int32_t magic;        // kChainMagic
+    int32_t n_desc;
+    int32_t n_stages;
+    int32_t total_items;
+    int32_t grid;         // workgroups (one resident round)
+    int32_t max_k;
+    int32_t spin_limit;   // polls before a stage wait gives up (status bit 1)
+    int32_t reserved;
+};
+struct ChainDesc {
+    const uint8_t* w;     // prepared region A
+    const uint8_t* sz;    // prepared region B
+    const uint16_t* x;    // bf16 [K]
+    void* y;              // [N] f32 or bf16
+    int32_t n, k;
+    int32_t rows;         // rows per item
+    int32_t first_item;   // global index of the first item
+    int32_t n_items;
+    int32_t stage;        // 0 .. n_stages-1, non-decreasing
+    int32_t y_bf16;
+    int32_t reserved;
+};
+constexpr int32_t kChainMagic = 0x57344348;  // "W4CH"
+size_t chain_lds_bytes(int max_k);
+int chain_grid(int max_k);
+hipError_t launch_chain(const ChainHeader& h, const uint8_t* plan_dev, uint32_t* ws, hipStream_t s);
+
 // Launch wrappers (defined in the .hip files); return hipSuccess or the launch error.
 hipError_t launch_quantize(const void* W, bool bf16, int64_t n_groups, uint8_t* packed,
                            uint16_t* scales, uint8_t* zeros, uint32_t* status, hipStream_t s);

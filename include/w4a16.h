@@ -140,6 +140,47 @@ w4_status w4_gemm(const void* prepared, int64_t N, int64_t K,
                   const void* X, int64_t M, void* Y, w4_dtype yt,
                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * GEMV chain -- a decode step's products (M = 1, bf16 x) in one persistent launch.
+ * Entries with the same stage are independent; stage s may read what stages < s
+ * wrote (an x may be an earlier y), so every item of stage s is computed after all
+ * of stage s-1 has been stored, while weight loads run ahead across the boundary
+ * (page "Weight quantization", "Complexity and constants": decode time is bytes
+ * read / bandwidth; "LLM Quantization Architecture in Depth", "Kernels and memory
+ * layout": fused kernels).  Within one stage no y may overlap any x.
+ *
+ *   w4_chain_plan_bytes(count)       host/device plan size for `count` entries.
+ *   w4_chain_plan(gemvs, count, plan_host, plan_bytes)
+ *       validates the entries (host memory) and writes the plan into plan_host
+ *       (host memory, caller-owned); the caller copies it unchanged to device memory
+ *       (plan_dev, 16-B aligned).  stage values must be non-decreasing; K <= 32768.
+ *   w4_chain_workspace_bytes(count)  device workspace size: 32-bit word 0 is a status
+ *       word, the others are counters.  The workspace must be zero-filled once before
+ *       its first use; every completed launch leaves the counters zeroed again.  Bit 0
+ *       of the status word is set (never cleared) if a stage wait gave up after about
+ *       two seconds of polling (results are then incomplete).  Launches sharing one
+ *       workspace must be ordered (same stream).
+ *   w4_chain_run(plan_dev, plan_host, workspace, workspace_bytes, stream)
+ *       launches the chain described by the plan (plan_host is read for the launch
+ *       geometry only).  Results equal w4_gemv's up to f32 summation order.
+ */
+typedef struct w4_chain_gemv {
+    const void* prepared;  /* from w4_prepare, 256-B aligned */
+    const void* x;         /* [K] bfloat16, 16-B aligned */
+    void* y;               /* [N] binary32 or bfloat16 (y_dtype), 4-B aligned */
+    int64_t n;
+    int64_t k;
+    int32_t stage;
+    int32_t y_dtype;       /* W4_F32 or W4_BF16 */
+} w4_chain_gemv;
+
+size_t w4_chain_plan_bytes(int64_t count);
+size_t w4_chain_workspace_bytes(int64_t count);
+w4_status w4_chain_plan(const w4_chain_gemv* gemvs, int64_t count, void* plan_host,
+                        size_t plan_bytes);
+w4_status w4_chain_run(const void* plan_dev, const void* plan_host, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream);
+
 /* Text of a status code (static storage). */
 const char* w4_status_string(w4_status s);
 /* Message of the last W4_ERR_HIP on the calling thread ("" if none). */
