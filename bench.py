@@ -156,14 +156,15 @@ def prefill_gemm(prepared, dev: str, reps: int = 3):
     m, n, k = 4096, 28672, 8192
     X = synth.normal_activations(m, k, 40200, dev)
     Y = torch.empty(m, n, dtype=torch.float32, device=dev)
+    ws = torch.empty(w4.w4_gemm_workspace_bytes(m, n, k), dtype=torch.uint8, device=dev)
     prep = prepared[(0, "gate")]
-    w4.w4_gemm(prep, n, k, X, Y=Y)
+    w4.w4_gemm(prep, n, k, X, Y=Y, workspace=ws)
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record()
     for _ in range(reps):
-        w4.w4_gemm(prep, n, k, X, Y=Y)
+        w4.w4_gemm(prep, n, k, X, Y=Y, workspace=ws)
     end.record()
     end.synchronize()
     ms = start.elapsed_time(end) / reps

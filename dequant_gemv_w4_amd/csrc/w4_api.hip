@@ -137,27 +137,25 @@ w4_status w4_gemv(const void* prepared, int64_t N, int64_t K, const void* x, w4_
 }
 
 size_t w4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-    (void)M;
-    (void)N;
-    (void)K;
-    return 0;
+    if (M < 1 || check_nk(N, K) != W4_OK) return 0;
+    return w4::gemm_workspace(M, K);
 }
 
 w4_status w4_gemm(const void* prepared, int64_t N, int64_t K, const void* X, int64_t M, void* Y,
                   w4_dtype yt, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    (void)workspace;
     if (!prepared || !X || !Y) return W4_ERR_NULL;
     if (yt != W4_F32 && yt != W4_BF16) return W4_ERR_DTYPE;
     w4_status st = check_nk(N, K);
     if (st != W4_OK) return st;
     if (M < 1 || (M + 127) / 128 > 65535) return W4_ERR_SHAPE;
-    if (workspace_bytes < w4_gemm_workspace_bytes(M, N, K)) return W4_ERR_WORKSPACE;
-    if (!aligned(prepared, 256) || !aligned(X, 16) || !aligned(Y, yt == W4_F32 ? 4 : 2))
+    if (!workspace || workspace_bytes < w4_gemm_workspace_bytes(M, N, K)) return W4_ERR_WORKSPACE;
+    if (!aligned(prepared, 256) || !aligned(X, 16) || !aligned(Y, yt == W4_F32 ? 4 : 2) ||
+        !aligned(workspace, 16))
         return W4_ERR_ALIGN;
     st = check_arch();
     if (st != W4_OK) return st;
     hipError_t e = w4::launch_gemm(static_cast<const uint8_t*>(prepared), N, K, X, M, Y,
-                                   yt == W4_BF16, stream);
+                                   yt == W4_BF16, workspace, stream);
     return e == hipSuccess ? W4_OK : hip_fail(e);
 }
 

@@ -126,14 +126,16 @@ w4_status w4_gemv(const void* prepared, int64_t N, int64_t K,
  * w4_gemm -- prefill-sized product Y[M, N] = X[M, K] * w_hat^T for any M >= 1
  * (page "LLM Quantization Architecture in Depth" › "Why fewer bits make
  * decoding faster": prefill is compute bound and weight-only formats must turn
- * weights back into 16-bit values before the matrix units).  Weight tiles are
- * dequantized to bfloat16 in LDS and multiplied on bf16 MFMA with binary32
- * accumulation.
+ * weights back into 16-bit values before the matrix units).  The codes enter
+ * bf16 MFMA as the exact values 128+q; per group the f32 accumulator receives
+ * scale16 * (P - (128+zero) * sum x) (page "Weight quantization", "How it
+ * works": the factored group dot), so no weight is rounded.
  *   prepared  from w4_prepare.
  *   X         [M, K] bfloat16 row-major; 16-B aligned.
  *   Y         [M, N] row-major, binary32 or bfloat16; 4-B aligned.
- *   workspace optional; w4_gemm_workspace_bytes() reports how many bytes the
- *             call needs (0 means none, and workspace may be NULL).
+ *   workspace device scratch of w4_gemm_workspace_bytes(M, N, K) bytes (per-group
+ *             sums of X; K/128 * ceil(M/128)*128 floats), 16-B aligned; contents
+ *             need no initialisation.  Calls sharing a workspace must be ordered.
  */
 size_t w4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 w4_status w4_gemm(const void* prepared, int64_t N, int64_t K,

@@ -35,7 +35,8 @@ def test_prepared_bytes_closed_form():
     assert w4.w4_prepared_bytes(5, 128) == 512 + 8 * 1 * 4
     assert w4.w4_prepared_bytes(1, 100) == 0     # K not a multiple of 128
     assert w4.w4_prepared_bytes(0, 128) == 0
-    assert w4.w4_gemm_workspace_bytes(4096, 28672, 8192) == 0
+    assert w4.w4_gemm_workspace_bytes(4096, 28672, 8192) == 64 * 4096 * 4
+    assert w4.w4_gemm_workspace_bytes(200, 300, 384) == 3 * 256 * 4
 
 
 def _fake(addr=0x100000):
