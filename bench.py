@@ -124,8 +124,8 @@ def time_step(step, steps: int, warmup: int) -> float:
     return start.elapsed_time(end) / steps
 
 
-def per_shape(prepared, layers: int, dev: str, reps: int = 3, fused: bool = False):
-    """Isolated GB/s per matrix shape: the same shape across all layers, back to back."""
+def per_shape(prepared, layers: int, dev: str, reps: int = 3, fused: bool = False, m: int = 1):
+    """Isolated GB/s per matrix shape at batch m: the same shape across all layers, back to back."""
     import synth
     from dequant_gemv_w4_amd.decode import DecodeStep, GemvCall
     import torch
@@ -135,9 +135,9 @@ def per_shape(prepared, layers: int, dev: str, reps: int = 3, fused: bool = Fals
     shapes = synth.LLAMA70B_FUSED_SHAPES if fused else synth.LLAMA70B_SHAPES
     for name in order:
         n, k = shapes[name]
-        x = synth.normal_activations(1, k, 40100, dev)
+        x = synth.normal_activations(m, k, 40100, dev)
         calls = [GemvCall(prepared[(layer, name)], n, k, x,
-                          torch.empty(1, n, dtype=torch.float32, device=dev))
+                          torch.empty(m, n, dtype=torch.float32, device=dev))
                  for layer in range(layers)]
         st = DecodeStep(calls)
         st.capture()

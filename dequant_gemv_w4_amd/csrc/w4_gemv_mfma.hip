@@ -1,0 +1,256 @@
+// Fused dequantizing product for a few activation rows (2 <= M <= 16, bf16 x)
+// on the matrix cores.
+//
+// The same group term as the one-row kernel, y[m, n] = sum_g scale16[n, g] *
+// (sum_{k in g} q[n, k] x[m, k] - zero[n, g] * sum_{k in g} x[m, k]) (page
+// "Weight quantization", section "How it works"), but the M dot products per
+// weight are done by v_mfma_f32_16x16x32_bf16 instead of the vector ALU.  The
+// weight stream stays the bound for every M up to 16: with VALU dot products
+// the work per weight grows with M, and past a few rows the vector units, not
+// HBM, set the pace (page "LLM Quantization Architecture in Depth" › "When it
+// helps and when it does not": batched decode moves towards compute).
+//
+// Mapping (gfx950, wave64):
+//   * the waves of a workgroup split K: wave w takes groups [w*gpw, (w+1)*gpw);
+//     a workgroup owns 16*T consecutive rows (T tiles of 16), and partial sums
+//     of its waves are added through LDS in wave order (deterministic);
+//   * per group, lane l loads 16 bytes of row (tile + l % 16) -- the 32 codes
+//     at k = 32*(l/16) .. +31 of the group -- plus that row's scale/zero word,
+//     and 4 x 16 bytes of activation row m = l % 16 (zero for m >= M);
+//   * MFMA step s (s = 0..3) of a group: A = x rows (lane l supplies row l % 16,
+//     k = 32*(l/16) + 8s .. +7), B = codes of the tile's 16 rows, unpacked by
+//     v_and_or_b32 into the exact bf16 values 128+q (lane l supplies column
+//     l % 16, same k).  Four steps give P[m][n] = sum (128+q) x for the group;
+//   * the group sums S[m] come from the same four steps with B = ones, so a
+//     group whose codes are all 0 gives P = 128*S exactly; the group's term is
+//     scale16 * (P - (128 + zero) * S), two FMAs per output element;
+//   * the 16x16 result sits in lane l as column n = l % 16, rows
+//     m = 4*(l/16) + v (v = 0..3): one scale/zero word per lane and tile.
+#include <atomic>
+#include <cstdlib>
+
+#include "w4_internal.h"
+
+namespace w4 {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kRedStride = 17;  // floats per row of the LDS partial sums (16 + pad)
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+__device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// T: tiles of 16 rows per workgroup; CH: groups whose loads are issued together;
+// NB: load buffers (1, or 2 for loads one chunk ahead)
+template <int T, int CH, int NB, int MAXT>
+__global__ __launch_bounds__(MAXT) void gemv_mfma_kernel(const uint8_t* __restrict__ wq,
+                                                         const uint32_t* __restrict__ sz,
+                                                         const uint16_t* __restrict__ x,
+                                                         void* __restrict__ yv, int y_bf16, int N,
+                                                         int K, int M, int gpw) {
+    constexpr int RW = 16 * T;
+    extern __shared__ float red[];  // [waves][RW][kRedStride]
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int n_waves = blockDim.x >> 6;
+    const int Kg = K >> 7;
+    const int r0 = blockIdx.x * RW;
+    const int col = lane & 15;
+    const int kb = lane >> 4;
+    const int g0 = wave * gpw;
+    const int g1 = min(Kg, g0 + gpw);
+    const int64_t row_bytes = K >> 1;
+
+    // this lane's weight row in each tile; rows past N repeat row N-1 (never stored)
+    const uint8_t* wrow[T];
+    const uint32_t* szrow[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        const int n = min(r0 + 16 * t + col, N - 1);
+        wrow[t] = wq + (int64_t)n * row_bytes + 16 * kb;
+        szrow[t] = sz + (int64_t)(n >> 2) * Kg * 4 + (n & 3);
+    }
+    // rows m >= M of the A operand repeat row M-1: their outputs are computed and dropped
+    const uint16_t* xrow = x + (int64_t)min(col, M - 1) * K + 32 * kb;
+
+    uint32_t nib_mask, bias_bits;
+    asm volatile("s_mov_b32 %0, 0x000F000F" : "=s"(nib_mask));
+    asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(bias_bits));
+    const u32x4_t ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+    const f32x4_t zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+
+    f32x4_t acc[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) acc[t] = zero4;
+
+    // NB buffers of CH groups: with two, the loads of the next chunk are in flight while
+    // the current one is computed
+    u32x4_t wb[NB][CH][T];
+    uint32_t sb[NB][CH][T];
+    u32x4_t xb[NB][CH][4];
+    // loads of groups g .. g+CH-1, clamped to the wave's last group (the repeats are cache
+    // hits and contribute nothing)
+    auto issue = [&](int b, int g) {
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int gc = min(g + c, g1 - 1);
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                xb[b][c][s] = *reinterpret_cast<const u32x4_t*>(xrow + gc * 128 + 8 * s);
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                wb[b][c][t] = __builtin_nontemporal_load(
+                    reinterpret_cast<const u32x4_t*>(wrow[t] + (int64_t)gc * 64));
+                sb[b][c][t] = szrow[t][gc * 4];
+            }
+            __builtin_amdgcn_sched_barrier(0);  // keep the loads in group order
+        }
+    };
+    auto compute = [&](int b, int g) {
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            // a group past the wave's range is computed with scale 0 (no branch, so
+            // the compiler cannot move loads into a conditional block)
+            const float keep = g + c < g1 ? 1.0f : 0.0f;
+            f32x4_t sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                as_bf16x8(xb[b][c][0]), as_bf16x8(ones), zero4, 0, 0, 0);
+#pragma unroll
+            for (int s = 1; s < 4; ++s)
+                sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xb[b][c][s]),
+                                                               as_bf16x8(ones), sacc, 0, 0, 0);
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                f32x4_t p = zero4;
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const uint32_t w = wb[b][c][t][s];
+                    const u32x4_t bw = {(w & nib_mask) | bias_bits,
+                                        ((w >> 4) & nib_mask) | bias_bits,
+                                        ((w >> 8) & nib_mask) | bias_bits,
+                                        ((w >> 12) & nib_mask) | bias_bits};
+                    p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xb[b][c][s]),
+                                                                as_bf16x8(bw), p, 0, 0, 0);
+                }
+                const uint32_t szw = sb[b][c][t];
+                const float sc =
+                    keep * (float)__builtin_bit_cast(_Float16, (uint16_t)(szw & 0xFFFFu));
+                const float zb = (float)((szw >> 16) & 0xFFu);  // zero + 128
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[t][v] = fmaf(sc, fmaf(-zb, sacc[v], p[v]), acc[t][v]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    if (g0 >= g1) {
+        // no groups for this wave (the host sizes the grid so that this does not happen)
+    } else if constexpr (NB == 1) {
+        for (int g = g0; g < g1; g += CH) {
+            issue(0, g);
+            compute(0, g);
+        }
+    } else {
+        issue(0, g0);
+        for (int g = g0; g < g1; g += 2 * CH) {
+            issue(1, g + CH);
+            compute(0, g);
+            issue(0, g + 2 * CH);
+            compute(1, g + CH);
+        }
+    }
+
+    // partial sums of this wave: lane holds column n = col, rows m = 4*kb + v
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int m = 4 * kb + v;
+            if (m < M) red[(wave * RW + 16 * t + col) * kRedStride + m] = acc[t][v];
+        }
+    __syncthreads();
+
+    const int rows_here = min(RW, N - r0);
+    for (int i = threadIdx.x; i < rows_here * M; i += blockDim.x) {
+        const int m = i / rows_here;
+        const int r = i - m * rows_here;
+        float v = 0.0f;
+        for (int w = 0; w < n_waves; ++w) v += red[(w * RW + r) * kRedStride + m];
+        const int64_t o = (int64_t)m * N + r0 + r;
+        if (y_bf16)
+            static_cast<uint16_t*>(yv)[o] = (uint16_t)bf16_bits_rne(v);
+        else
+            static_cast<float*>(yv)[o] = v;
+    }
+}
+
+int env_int(const char* name, int dflt) {
+    const char* e = getenv(name);
+    return e ? atoi(e) : dflt;
+}
+
+template <int T, int CH, int NB, int MAXT>
+hipError_t launch_t(const uint8_t* wq, const uint32_t* sz, const uint16_t* x, void* y, int y_bf16,
+                    int n, int k, int m, int gpw, int waves, hipStream_t s) {
+    const dim3 grid((unsigned)((n + 16 * T - 1) / (16 * T)));
+    const dim3 block((unsigned)(64 * waves));
+    const size_t shmem = (size_t)waves * 16 * T * kRedStride * sizeof(float);
+    hipLaunchKernelGGL((gemv_mfma_kernel<T, CH, NB, MAXT>), grid, block, shmem, s, wq, sz, x, y, y_bf16,
+                       n, k, m, gpw);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// Waves per workgroup: about eight groups of K each, at most 16 waves.  Two tiles (32
+// rows) per workgroup, two groups per load batch, one buffer: the fastest of the
+// settings measured on MI355X at the 70B shapes for M = 2, 8 and 16.
+hipError_t launch_gemv_mfma(const uint8_t* prepared, int64_t n, int64_t k, const uint16_t* x,
+                            int64_t m, void* y, bool y_bf16, hipStream_t s) {
+    const int kg = (int)(k / kGroup);
+    static const int per_wave = env_int("W4A16_MFMA_GPW", 8);
+    static const int forced_t = env_int("W4A16_MFMA_TILES", 0);
+    static const int chunk = env_int("W4A16_MFMA_CHUNK", 2);
+    int waves = (kg + per_wave - 1) / per_wave;
+    if (waves > 16) waves = 16;
+    if (waves < 1) waves = 1;
+    const int gpw = (kg + waves - 1) / waves;
+    waves = (kg + gpw - 1) / gpw;
+    int t = forced_t;
+    if (t != 1 && t != 2 && t != 4) t = 2;
+    const uint8_t* wq = prepared;
+    const uint32_t* sz = reinterpret_cast<const uint32_t*>(prepared + sz_offset(n, k));
+    const int yb = y_bf16 ? 1 : 0;
+    const int N = (int)n, K = (int)k, M = (int)m;
+    static const int nbuf = env_int("W4A16_MFMA_NB", 1);
+    // 1024-thread groups have 128 VGPRs per lane: one double-buffered group, or two
+    // single-buffered groups, of up to two tiles
+    int ch = chunk, nb = nbuf == 1 ? 1 : 2;
+    if (waves > 8) {
+        if (t == 4) t = 2;
+        if (nb == 2) ch = 1;
+        else if (ch > 2) ch = 2;
+    }
+#define W4_MFMA_CASE(TV, CV, NV)                                                                  \
+    if (t == TV && ch == CV && nb == NV)                                                          \
+        return waves <= 8 ? launch_t<TV, CV, NV, 512>(wq, sz, x, y, yb, N, K, M, gpw, waves, s)   \
+                          : launch_t<TV, CV, NV, 1024>(wq, sz, x, y, yb, N, K, M, gpw, waves, s);
+    W4_MFMA_CASE(1, 1, 1) W4_MFMA_CASE(1, 2, 1) W4_MFMA_CASE(2, 1, 1) W4_MFMA_CASE(2, 2, 1)
+    W4_MFMA_CASE(1, 1, 2) W4_MFMA_CASE(2, 1, 2)
+#undef W4_MFMA_CASE
+    if (t == 1 && ch == 4 && nb == 1) return launch_t<1, 4, 1, 512>(wq, sz, x, y, yb, N, K, M, gpw, waves, s);
+    if (t == 1 && ch == 2 && nb == 2) return launch_t<1, 2, 2, 512>(wq, sz, x, y, yb, N, K, M, gpw, waves, s);
+    if (t == 2 && ch == 2 && nb == 2) return launch_t<2, 2, 2, 512>(wq, sz, x, y, yb, N, K, M, gpw, waves, s);
+    if (t == 4 && ch == 1 && nb == 1) return launch_t<4, 1, 1, 512>(wq, sz, x, y, yb, N, K, M, gpw, waves, s);
+    if (t == 4 && ch == 1 && nb == 2) return launch_t<4, 1, 2, 512>(wq, sz, x, y, yb, N, K, M, gpw, waves, s);
+    return launch_t<2, 1, 2, 1024>(wq, sz, x, y, yb, N, K, M, gpw, waves, s);
+}
+
+}  // namespace w4

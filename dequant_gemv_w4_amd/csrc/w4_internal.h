@@ -106,6 +106,8 @@ hipError_t launch_unprepare(const uint8_t* prepared, int64_t n, int64_t k, uint8
                             uint16_t* scales, uint8_t* zeros, hipStream_t s);
 hipError_t launch_gemv(const uint8_t* prepared, int64_t n, int64_t k, const void* x, bool x_f32,
                        int64_t m, void* y, bool y_bf16, hipStream_t s);
+hipError_t launch_gemv_mfma(const uint8_t* prepared, int64_t n, int64_t k, const uint16_t* x,
+                            int64_t m, void* y, bool y_bf16, hipStream_t s);
 size_t gemm_workspace(int64_t m, int64_t k);
 hipError_t launch_gemm(const uint8_t* prepared, int64_t n, int64_t k, const void* X, int64_t m,
                        void* Y, bool y_bf16, void* workspace, hipStream_t s);
