@@ -30,6 +30,8 @@
 // both operands, so each output is a dot product over matching k.  The 32 x 32
 // f32 result sits in lane l as column (l % 32) and rows 8*(v/4) + 4*(l/32) +
 // (v%4) for element v = 0..15.
+#include <cstdlib>
+
 #include "w4_internal.h"
 
 namespace w4 {
@@ -43,7 +45,7 @@ constexpr int BM = 128;
 constexpr int BN = 256;
 constexpr int BK = kGroup;
 constexpr int GT = 512;                  // threads per workgroup
-constexpr int XS = BK + 8;               // bf16 per LDS row of the X tile (16-byte pad)
+constexpr int kXcds = 8;                 // accelerator complex dies of MI355X, each with its own L2
 
 __device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
     const uint32_t u = __float_as_uint(f);
@@ -93,70 +95,104 @@ __global__ __launch_bounds__(256) void xsum_kernel(const uint16_t* __restrict__ 
     }
 }
 
+// One stage of the LDS ring: the operands of one group (K step).
+//   X:  128 rows x 16 chunks of 16 bytes; chunk c of row r sits at slot c ^ (r & 15)
+//   W:  256 columns x 4 pieces of 16 bytes (the 64 code bytes of the group);
+//       piece p of column n sits at slot p ^ ((n >> 2) & 3)
+//   SZ: the scale/zero words of the 256 columns, in column order
+//   S:  the group sums of the 128 rows
+// The swizzles keep the 16-byte reads of the MFMA operands free of bank conflicts.
+constexpr int kStages = 3;
+constexpr int kXBytes = BM * BK * 2;          // 32768
+constexpr int kWBytes = BN * BK / 2;          // 16384
+constexpr int kSzBytes = 1024;                // 256 words (64 lanes x 16 bytes)
+constexpr int kSBytes = 1024;                 // 128 floats, the load covers 256
+constexpr int kStageBytes = kXBytes + kWBytes + kSzBytes + kSBytes;
+
+// 16 bytes per lane from global memory straight into LDS: lane l of the wave writes
+// bytes [16 l, 16 l + 16) after the wave-uniform LDS address.  Issued as inline
+// assembly so that the compiler does not order the LDS reads of other stages
+// behind these loads; the kernel waits for them itself (vmcnt) before the barrier
+// that publishes a stage.
+__device__ __forceinline__ void load_lds16(const void* g, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(g), "s"(lds_addr)
+                 : "memory", "m0");
+}
+
 __global__ __launch_bounds__(GT) void gemm_kernel(const uint8_t* __restrict__ wq,
                                                   const uint32_t* __restrict__ sz,
                                                   const uint16_t* __restrict__ X,
                                                   const float* __restrict__ St, int m_pad,
                                                   void* __restrict__ Y, int y_bf16, int M, int N,
-                                                  int K) {
-    __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM * XS];
-    __shared__ __attribute__((aligned(16))) float ss[2][BM];
+                                                  int K, int tiles_m, int tiles_n, int group_m,
+                                                  int per_xcd) {
+    __shared__ __attribute__((aligned(16))) uint8_t ring[kStages * kStageBytes];
+
+    // Tile order: workgroup b runs on XCD b % kXcds, and each XCD takes a contiguous
+    // range of a grouped order (group_m tiles of M per band, N within the band), so the
+    // workgroups resident on one XCD at a time cover a compact block of tiles and share
+    // their X rows and weight columns in that XCD's L2.
+    const int t = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
+    if (t >= tiles_m * tiles_n) return;
+    const int band = t / (group_m * tiles_n);
+    const int first_m = band * group_m;
+    const int gm = min(tiles_m - first_m, group_m);
+    const int r = t - band * group_m * tiles_n;
+    const int n0 = (r / gm) * BN;
+    const int m0 = (first_m + r % gm) * BM;
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
     const int wm = wave >> 2;        // 0..1: rows 64wm..
     const int wn = wave & 3;         // 0..3: columns 64wn..
-    const int n0 = blockIdx.x * BN;
-    const int m0 = blockIdx.y * BM;
     const int Kg = K / kGroup;
     const int64_t row_bytes = K / 2;
     const int h = lane >> 5;
     const int l32 = lane & 31;
+    const int n_quads = (N + 3) >> 2;
+
+    // ---- per-lane global addresses of the stage loads (group 0; a group adds a fixed step)
+    // X: wave w fills rows 16w .. 16w+15 with four 1 KiB loads of four rows each
+    const uint16_t* xsrc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = 16 * wave + 4 * i + (lane >> 4);
+        const int c = (lane & 15) ^ (row & 15);
+        xsrc[i] = X + (int64_t)min(m0 + row, M - 1) * K + 8 * c;
+    }
+    // W: wave w fills columns 32w .. 32w+31 with two loads of sixteen columns
+    const uint8_t* wsrc[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int col = 32 * wave + 16 * i + (lane >> 2);
+        const int piece = (lane & 3) ^ ((col >> 2) & 3);
+        wsrc[i] = wq + (int64_t)min(n0 + col, N - 1) * row_bytes + 16 * piece;
+    }
+    // SZ (wave 0): lane = column quad; S (wave 1): lane = four rows
+    const uint32_t* szsrc = sz + (int64_t)min((n0 >> 2) + lane, n_quads - 1) * Kg * 4;
+    const float* ssrc = St + min(m0 + 4 * lane, m_pad - 4);
+
+    // LDS address of the ring (wave-uniform)
+    const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring);
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    auto issue_stage = [&](int st, int kg) {
+        const uint32_t base = ring_lds + st * kStageBytes;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) load_lds16(xsrc[i] + kg * BK, base + (4 * wave_u + i) * 1024);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            load_lds16(wsrc[i] + kg * (BK / 2), base + kXBytes + (2 * wave_u + i) * 1024);
+        if (wave_u == 0) load_lds16(szsrc + kg * 4, base + kXBytes + kWBytes);
+        if (wave_u == 1) load_lds16(ssrc + (int64_t)kg * m_pad, base + kXBytes + kWBytes + kSzBytes);
+    };
 
     uint32_t nib_mask, bias_bits;
     asm volatile("s_mov_b32 %0, 0x000F000F" : "=s"(nib_mask));
     asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(bias_bits));
-
-    // weight rows of this lane (one per N tile), clamped inside the matrix
-    int wrow[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) wrow[j] = min(n0 + 64 * wn + 32 * j + l32, N - 1);
-
-    // ---- staging of one group: X tile (global -> registers -> LDS), S, weights, scale/zero
-    uint4 xr[4];             // 512 threads x 4 x 16 B = the 32 KB X tile
-    u32x4_t wr[2][2];        // [N tile][half of the 32 bytes] codes of the next group
-    uint32_t szr[2];
-    float sr = 0.0f;
-    auto load_group = [&](int kg) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int idx = tid + i * GT;       // 0..2047: 128 rows x 16 pieces
-            const int r = idx >> 4;
-            const int c = (idx & 15) * 8;
-            xr[i] = make_uint4(0, 0, 0, 0);
-            if (m0 + r < M)
-                xr[i] = *reinterpret_cast<const uint4*>(X + (int64_t)(m0 + r) * K + kg * BK + c);
-        }
-        if (tid < BM) sr = St[(int64_t)kg * m_pad + m0 + tid];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const uint8_t* p = wq + (int64_t)wrow[j] * row_bytes + kg * (BK / 2) + 32 * h;
-            wr[j][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-            wr[j][1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p + 16));
-            szr[j] = sz[sz_index(wrow[j], kg, Kg)];
-        }
-    };
-    auto store_group = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int idx = tid + i * GT;
-            const int r = idx >> 4;
-            const int c = (idx & 15) * 8;
-            *reinterpret_cast<uint4*>(&xs[buf][r * XS + c]) = xr[i];
-        }
-        if (tid < BM) ss[buf][tid] = sr;
-    };
 
     f32x16_t acc[2][2];
 #pragma unroll
@@ -164,21 +200,38 @@ __global__ __launch_bounds__(GT) void gemm_kernel(const uint8_t* __restrict__ wq
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = (f32x16_t){};
 
-    load_group(0);
-    store_group(0);
-    u32x4_t wc[2][2];
-    uint32_t szc[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        wc[j][0] = wr[j][0];
-        wc[j][1] = wr[j][1];
-        szc[j] = szr[j];
-    }
-    __syncthreads();
+    issue_stage(0, 0);
+    if (Kg > 1) issue_stage(1, 1);
 
     for (int kg = 0; kg < Kg; ++kg) {
-        const int buf = kg & 1;
-        if (kg + 1 < Kg) load_group(kg + 1);
+        // this wave's loads of group kg have landed (at most one later stage, six or seven
+        // loads, may still be in flight); the barrier makes every wave's loads visible and
+        // frees the stage that group kg+2 reuses
+        if (kg + 1 < Kg)
+            __builtin_amdgcn_s_waitcnt(0xF76);  // vmcnt(6)
+        else
+            __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
+        __syncthreads();
+        if (kg + 2 < Kg) issue_stage((kg + 2) % kStages, kg + 2);
+
+        const uint8_t* base = ring + (kg % kStages) * kStageBytes;
+        const uint8_t* xs = base;
+        const uint8_t* ws = base + kXBytes;
+        const uint32_t* szs = reinterpret_cast<const uint32_t*>(base + kXBytes + kWBytes);
+        const float* ss = reinterpret_cast<const float*>(base + kXBytes + kWBytes + kSzBytes);
+
+        // codes of this lane's two columns: pieces 2h and 2h+1 of each
+        u32x4_t wc[2][2];
+        uint32_t szc[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int col = 64 * wn + 32 * j + l32;
+            const int sw = (col >> 2) & 3;
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+                wc[j][e] = *reinterpret_cast<const u32x4_t*>(ws + col * 64 + (((2 * h + e) ^ sw) * 16));
+            szc[j] = szs[col];
+        }
 
         // ---- eight MFMA steps over the group into fresh accumulators P
         f32x16_t P[2][2];
@@ -186,9 +239,11 @@ __global__ __launch_bounds__(GT) void gemm_kernel(const uint8_t* __restrict__ wq
         for (int s = 0; s < 8; ++s) {
             bf16x8_t a[2], b[2];
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
-                a[i] = *reinterpret_cast<const bf16x8_t*>(
-                    &xs[buf][(64 * wm + 32 * i + l32) * XS + 64 * h + 8 * s]);
+            for (int i = 0; i < 2; ++i) {
+                const int row = 64 * wm + 32 * i + l32;
+                const int c = 8 * h + s;
+                a[i] = *reinterpret_cast<const bf16x8_t*>(xs + row * 256 + ((c ^ (row & 15)) * 16));
+            }
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const uint32_t w = wc[j][s >> 2][s & 3];  // codes of k = 64h + 8s .. +7
@@ -220,29 +275,17 @@ __global__ __launch_bounds__(GT) void gemm_kernel(const uint8_t* __restrict__ wq
         for (int i = 0; i < 2; ++i) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const float4 s4 = *reinterpret_cast<const float4*>(
-                    &ss[buf][64 * wm + 32 * i + 8 * q + 4 * h]);
+                const float4 s4 = *reinterpret_cast<const float4*>(&ss[64 * wm + 32 * i + 8 * q + 4 * h]);
                 const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
+                for (int rr = 0; rr < 4; ++rr)
 #pragma unroll
                     for (int j = 0; j < 2; ++j) {
-                        const int v = 4 * q + r;
-                        acc[i][j][v] = fmaf(sc[j], fmaf(-zb[j], sv[r], P[i][j][v]), acc[i][j][v]);
+                        const int v = 4 * q + rr;
+                        acc[i][j][v] = fmaf(sc[j], fmaf(-zb[j], sv[rr], P[i][j][v]), acc[i][j][v]);
                     }
             }
         }
-
-        if (kg + 1 < Kg) {
-            store_group(buf ^ 1);
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                wc[j][0] = wr[j][0];
-                wc[j][1] = wr[j][1];
-                szc[j] = szr[j];
-            }
-        }
-        __syncthreads();
     }
 
 #pragma unroll
@@ -251,10 +294,10 @@ __global__ __launch_bounds__(GT) void gemm_kernel(const uint8_t* __restrict__ wq
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int r = m0 + 64 * wm + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+                const int row = m0 + 64 * wm + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
                 const int c = n0 + 64 * wn + 32 * j + l32;
-                if (r < M && c < N) {
-                    const int64_t o = (int64_t)r * N + c;
+                if (row < M && c < N) {
+                    const int64_t o = (int64_t)row * N + c;
                     if (y_bf16)
                         static_cast<uint16_t*>(Y)[o] = (uint16_t)bf16_bits_rne(acc[i][j][v]);
                     else
@@ -281,11 +324,19 @@ hipError_t launch_gemm(const uint8_t* prepared, int64_t n, int64_t k, const void
                        static_cast<const uint16_t*>(X), (int)m, (int)k, St, m_pad);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const dim3 grid((unsigned)((n + BN - 1) / BN), (unsigned)((m + BM - 1) / BM));
+    static const int group_env = [] {
+        const char* e = getenv("W4A16_GEMM_GROUP_M");
+        return e ? atoi(e) : 8;
+    }();
+    const int tiles_n = (int)((n + BN - 1) / BN);
+    const int tiles_m = (int)((m + BM - 1) / BM);
+    const int group_m = group_env < 1 ? 1 : (group_env > tiles_m ? tiles_m : group_env);
+    const int per_xcd = (tiles_m * tiles_n + kXcds - 1) / kXcds;
+    const dim3 grid((unsigned)(per_xcd * kXcds));
     hipLaunchKernelGGL(gemm_kernel, grid, dim3(GT), 0, s, prepared,
                        reinterpret_cast<const uint32_t*>(prepared + sz_offset(n, k)),
                        static_cast<const uint16_t*>(X), St, m_pad, Y, y_bf16 ? 1 : 0, (int)m,
-                       (int)n, (int)k);
+                       (int)n, (int)k, tiles_m, tiles_n, group_m, per_xcd);
     return hipGetLastError();
 }
 
