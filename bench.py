@@ -31,6 +31,12 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+# HBM bytes per launch of the batch-1 fused step, measured with rocprofv3 counters on the
+# current w4_gemv kernel: FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by what the
+# counter reads for a 256 MiB device copy (FETCH_SIZE x2, WRITE_SIZE x1); average of the four
+# launches of a layer (qkv, o, gate_up, down).  Source: the profile summary
+# profiles/w4_gemv_llama70b_fused_step_hbm_traffic.md
+GEMV_STEP_TRAFFIC_BYTES_PER_LAUNCH = 114034481
 BF16_DENSE_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 METRIC = "W4A16 g128 GEMV achieved HBM GB/s (% of peak), 70B layer shapes, batch 1"
 
@@ -49,6 +55,9 @@ def parse_args():
     ap.add_argument("--skip-extras", action="store_true",
                     help="only the headline step (no batch sweep, per-shape, GEMM, quantizer)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one 256 MiB device-to-device copy (a known-size kernel that "
+                         "scales the byte counters of a profiler run)")
     return ap.parse_args()
 
 
@@ -107,21 +116,44 @@ def make_step(prepared, layers: int, m: int, dev: str, fused: bool = False):
     return DecodeStep(calls)
 
 
-def time_step(step, steps: int, warmup: int) -> float:
-    """Milliseconds per step from HIP events on the launch stream."""
+def time_step(step, steps: int, warmup: int, per_step: list | None = None) -> float:
+    """Milliseconds per step from HIP events on the launch stream.
+
+    The K timed steps run back to back between one start and one end event; when
+    per_step is a list, an event is also recorded after every step and the K
+    individual step times are appended to it (for median and percentiles).
+    """
     import torch
     for _ in range(warmup):
         step.run()
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps)] if per_step is not None else []
     start.record()
-    for _ in range(steps):
+    for i in range(steps):
         step.run()
+        if marks:
+            marks[i].record()
     end.record()
     end.synchronize()
     torch.cuda.synchronize()
+    if marks:
+        prev = start
+        for ev in marks:
+            per_step.append(prev.elapsed_time(ev))
+            prev = ev
     return start.elapsed_time(end) / steps
+
+
+def percentile(values: list, q: float) -> float:
+    v = sorted(values)
+    if not v:
+        return float("nan")
+    pos = (len(v) - 1) * q
+    lo = int(pos)
+    hi = min(lo + 1, len(v) - 1)
+    return v[lo] + (v[hi] - v[lo]) * (pos - lo)
 
 
 def per_shape(prepared, layers: int, dev: str, reps: int = 3, fused: bool = False, m: int = 1):
@@ -244,11 +276,19 @@ def main() -> int:
     log(f"device {torch.cuda.get_device_name(0)}; building {args.layers} fused layers")
     prepared = build_stack(args.layers, dev, fused=True)
 
+    if args.copy_calibration:
+        src = torch.full((256 << 20,), 3, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     step = make_step(prepared, args.layers, 1, dev, fused=True)
     if not args.no_graph:
         step.capture()
         log("captured the step into a graph")
-    ms = time_step(step, args.steps, args.warmup)
+    step_ms: list = []
+    ms = time_step(step, args.steps, args.warmup, per_step=step_ms)
     nbytes = step.algorithmic_bytes()
     gbs = nbytes / (ms * 1e-3) / 1e9
     launches = len(step.calls)
@@ -281,13 +321,17 @@ def main() -> int:
         },
         "tokens_per_s_equiv": round(1000.0 / ms, 2),
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "step_ms_median_p10_p90": [round(percentile(step_ms, 0.5), 4),
+                                   round(percentile(step_ms, 0.1), 4),
+                                   round(percentile(step_ms, 0.9), 4)],
         "roofline": {
             "bound": "hbm",
             "achieved": round(gbs, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": GEMV_STEP_TRAFFIC_BYTES_PER_LAUNCH,
+            "traffic_unit": "bytes per launch (HBM, counter-measured)",
             "kernel": "w4_gemv (gemv_kernel, M=1 bf16 variants)",
             "per_launch": f"{nbytes / launches / 1e6:.2f} MB algorithmic in "
                           f"{ms * 1000 / launches:.2f} us average (step time / launches)",
