@@ -191,6 +191,214 @@ __global__ __launch_bounds__(MAXT) void gemv_mfma_kernel(const uint8_t* __restri
     }
 }
 
+// Variant for K <= 8192 (at most eight groups per wave, at most eight waves).
+//   * Each wave keeps the A operands of its groups (x, four MFMA steps per group) and their
+//     group sums in registers, then walks all rows of the workgroup in steps of 16.
+//   * Weights and scale/zero words go straight from global memory into a ring in LDS that
+//     belongs to the wave (global_load_lds: lane l's bytes land at slot + 16 l, and lane l
+//     reads them back), two row steps ahead, so the bytes in flight do not take registers.
+//     The loads of a row step are issued in a fixed order (scale/zero of groups 0-3, codes of
+//     groups 0-3, scale/zero of groups 4-7, codes of groups 4-7) and each group waits for
+//     an exact count of later loads.
+//   * Scale/zero: lane (col, kb) loads the word of group g + kb of its row; three permlane
+//     swaps give every lane of the column the words of all four groups.
+//   * Partial sums of the waves meet in LDS after every row step (double-buffered, one
+//     barrier per step).
+constexpr int kXrGroups = 8;                        // groups per wave
+constexpr int kXrSlotBytes = 1024;                  // one group of one 16-row tile
+constexpr int kXrSzBytes = 256;                     // one scale/zero word per lane
+constexpr int kXrWaveRing = 16 * kXrSlotBytes + 4 * kXrSzBytes;   // two row steps
+constexpr int kXrRedBytes = 2 * 16 * kRedStride * 4;              // per wave: two row steps
+
+__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(g), "s"(lds_addr)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma4(const void* g, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+                 :
+                 : "v"(g), "s"(lds_addr)
+                 : "memory", "m0");
+}
+
+// s_waitcnt immediate waiting for vmcnt <= n only (gfx9 encoding)
+constexpr int vm_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
+
+// wait until the codes of group j of the current row step (and its scale/zero words) have
+// landed: later loads are the rest of this row step (8,7,6,5,3,2,1,0 for j = 0..7) plus the
+// ten loads of the next row step when it is in flight
+__device__ __forceinline__ void wait_group(int j, bool more) {
+    if (more) {
+        switch (j) {
+            case 0: __builtin_amdgcn_s_waitcnt(vm_imm(18)); break;
+            case 1: __builtin_amdgcn_s_waitcnt(vm_imm(17)); break;
+            case 2: __builtin_amdgcn_s_waitcnt(vm_imm(16)); break;
+            case 3: __builtin_amdgcn_s_waitcnt(vm_imm(15)); break;
+            case 4: __builtin_amdgcn_s_waitcnt(vm_imm(13)); break;
+            case 5: __builtin_amdgcn_s_waitcnt(vm_imm(12)); break;
+            case 6: __builtin_amdgcn_s_waitcnt(vm_imm(11)); break;
+            default: __builtin_amdgcn_s_waitcnt(vm_imm(10)); break;
+        }
+    } else {
+        switch (j) {
+            case 0: __builtin_amdgcn_s_waitcnt(vm_imm(8)); break;
+            case 1: __builtin_amdgcn_s_waitcnt(vm_imm(7)); break;
+            case 2: __builtin_amdgcn_s_waitcnt(vm_imm(6)); break;
+            case 3: __builtin_amdgcn_s_waitcnt(vm_imm(5)); break;
+            case 4: __builtin_amdgcn_s_waitcnt(vm_imm(3)); break;
+            case 5: __builtin_amdgcn_s_waitcnt(vm_imm(2)); break;
+            case 6: __builtin_amdgcn_s_waitcnt(vm_imm(1)); break;
+            default: __builtin_amdgcn_s_waitcnt(vm_imm(0)); break;
+        }
+    }
+    asm volatile("" ::: "memory");  // LDS reads of the slot stay after the wait
+}
+
+// barrier for LDS data only: no fence, so no wait for the ring's loads in flight
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// v: one word per lane; returns b[j] = v of lane (l % 16) + 16 j, for every lane l
+__device__ __forceinline__ void bcast_rows(uint32_t v, uint32_t (&b)[4]) {
+    const auto h = __builtin_amdgcn_permlane32_swap(v, v, false, false);   // (r0 r1 r0 r1), (r2 r3 r2 r3)
+    const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)h[0], (uint32_t)h[0], false, false);
+    const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)h[1], (uint32_t)h[1], false, false);
+    b[0] = (uint32_t)lo[0];
+    b[1] = (uint32_t)lo[1];
+    b[2] = (uint32_t)hi[0];
+    b[3] = (uint32_t)hi[1];
+}
+
+__global__ __launch_bounds__(512) void gemv_mfma_xr_kernel(const uint8_t* __restrict__ wq,
+                                                         const uint32_t* __restrict__ sz,
+                                                         const uint16_t* __restrict__ x,
+                                                         void* __restrict__ yv, int y_bf16, int N,
+                                                         int K, int M, int gpw, int R) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // rings, then partial sums
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int n_waves = blockDim.x >> 6;
+    const int Kg = K >> 7;
+    const int r0 = blockIdx.x * R;
+    const int col = lane & 15;
+    const int kb = lane >> 4;
+    const int g0 = wave * gpw;
+    const int ng = min(Kg - g0, gpw);   // >= 1: the host sizes the block so every wave has groups
+    const int64_t row_bytes = K >> 1;
+    const int steps = R >> 4;
+
+    const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+    const uint32_t ring = __builtin_amdgcn_readfirstlane(smem_lds + wave * kXrWaveRing);
+    const uint8_t* ring_p = smem + wave * kXrWaveRing;
+    float* red = reinterpret_cast<float*>(smem + n_waves * kXrWaveRing);   // [2][waves][16][stride]
+
+    uint32_t nib_mask, bias_bits;
+    asm volatile("s_mov_b32 %0, 0x000F000F" : "=s"(nib_mask));
+    asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(bias_bits));
+    const u32x4_t ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+    const f32x4_t zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+
+    // loads of row step t into the ring half t & 1; rows past N repeat row N-1 (never stored)
+    auto issue_step = [&](int t) {
+        const int n = min(r0 + 16 * t + col, N - 1);
+        const uint8_t* wrow = wq + (int64_t)n * row_bytes + 16 * kb + (int64_t)g0 * 64;
+        const uint32_t* szrow = sz + (int64_t)(n >> 2) * Kg * 4 + (n & 3) + (int64_t)g0 * 4;
+        const uint32_t wb = ring + (t & 1) * 8 * kXrSlotBytes;
+        const uint32_t sb = ring + 16 * kXrSlotBytes + (t & 1) * 2 * kXrSzBytes;
+        lds_dma4(szrow + min(kb, ng - 1) * 4, sb);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) lds_dma16(wrow + (int64_t)min(c, ng - 1) * 64, wb + c * kXrSlotBytes);
+        lds_dma4(szrow + min(4 + kb, ng - 1) * 4, sb + kXrSzBytes);
+#pragma unroll
+        for (int c = 4; c < 8; ++c) lds_dma16(wrow + (int64_t)min(c, ng - 1) * 64, wb + c * kXrSlotBytes);
+    };
+    issue_step(0);
+
+    // ---- x of this wave's groups (A operands) and their sums, once per workgroup
+    u32x4_t xa[kXrGroups][4];
+    const uint16_t* xrow = x + (int64_t)min(col, M - 1) * K + 32 * kb;
+#pragma unroll
+    for (int gi = 0; gi < kXrGroups; ++gi)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            xa[gi][s] = *reinterpret_cast<const u32x4_t*>(xrow + (g0 + min(gi, ng - 1)) * 128 + 8 * s);
+    f32x4_t sx[kXrGroups];
+#pragma unroll
+    for (int gi = 0; gi < kXrGroups; ++gi) {
+        sx[gi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[gi][0]), as_bf16x8(ones),
+                                                         zero4, 0, 0, 0);
+#pragma unroll
+        for (int s = 1; s < 4; ++s)
+            sx[gi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[gi][s]), as_bf16x8(ones),
+                                                             sx[gi], 0, 0, 0);
+    }
+
+    for (int t = 0; t < steps; ++t) {
+        const bool more = t + 1 < steps;
+        if (more) issue_step(t + 1);
+        const uint8_t* wslots = ring_p + (t & 1) * 8 * kXrSlotBytes;
+        const uint8_t* sslots = ring_p + 16 * kXrSlotBytes + (t & 1) * 2 * kXrSzBytes;
+        f32x4_t acc = zero4;
+        uint32_t szw[4];
+#pragma unroll
+        for (int j = 0; j < kXrGroups; ++j) {
+            wait_group(j, more);
+            if (j % 4 == 0)
+                bcast_rows(*reinterpret_cast<const uint32_t*>(sslots + (j / 4) * kXrSzBytes + 4 * lane),
+                           szw);
+            const u32x4_t w4 = *reinterpret_cast<const u32x4_t*>(wslots + j * kXrSlotBytes + 16 * lane);
+            f32x4_t p = zero4;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const uint32_t w = w4[s];
+                const u32x4_t bw = {(w & nib_mask) | bias_bits, ((w >> 4) & nib_mask) | bias_bits,
+                                    ((w >> 8) & nib_mask) | bias_bits,
+                                    ((w >> 12) & nib_mask) | bias_bits};
+                p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[j][s]), as_bf16x8(bw), p,
+                                                            0, 0, 0);
+            }
+            // a group past the wave's range is computed with scale 0 (no branch)
+            const uint32_t word = szw[j % 4];
+            const float keep = j < ng ? 1.0f : 0.0f;
+            const float sc = keep * (float)__builtin_bit_cast(_Float16, (uint16_t)(word & 0xFFFFu));
+            const float zb = (float)((word >> 16) & 0xFFu);  // zero + 128
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[v] = fmaf(sc, fmaf(-zb, sx[j][v], p[v]), acc[v]);
+        }
+        // partial sums of this row step: lane holds column (row) col, rows m = 4 kb + v
+        float* rb = red + ((t & 1) * n_waves + wave) * 16 * kRedStride;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int m = 4 * kb + v;
+            if (m < M) rb[col * kRedStride + m] = acc[v];
+        }
+        lds_barrier();
+        for (int i = tid; i < 16 * M; i += blockDim.x) {
+            const int r = i & 15;
+            const int m = i >> 4;
+            const int row = r0 + 16 * t + r;
+            if (row < N) {
+                const float* rs = red + (t & 1) * n_waves * 16 * kRedStride;
+                float v = 0.0f;
+                for (int w = 0; w < n_waves; ++w) v += rs[(w * 16 + r) * kRedStride + m];
+                const int64_t o = (int64_t)m * N + row;
+                if (y_bf16)
+                    static_cast<uint16_t*>(yv)[o] = (uint16_t)bf16_bits_rne(v);
+                else
+                    static_cast<float*>(yv)[o] = v;
+            }
+        }
+    }
+}
+
 int env_int(const char* name, int dflt) {
     const char* e = getenv(name);
     return e ? atoi(e) : dflt;
@@ -212,9 +420,60 @@ hipError_t launch_t(const uint8_t* wq, const uint32_t* sz, const uint16_t* x, vo
 // Waves per workgroup: about eight groups of K each, at most 16 waves.  Two tiles (32
 // rows) per workgroup, two groups per load batch, one buffer: the fastest of the
 // settings measured on MI355X at the 70B shapes for M = 2, 8 and 16.
+// Rows per workgroup of the ring kernel: one round of workgroups (one per CU), a multiple
+// of 16.  The ring pays off from three row steps on; below that the streaming kernel is
+// used (measured on MI355X at the 70B shapes: o 8192x8192 streams faster, qkv and gate_up
+// run faster on the ring).
+static int xr_rows(int n) {
+    static std::atomic<int> cus{0};
+    int cu = cus.load(std::memory_order_relaxed);
+    if (cu == 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cu <= 0)
+            cu = 256;
+        cus.store(cu, std::memory_order_relaxed);
+    }
+    static const int rounds_env = env_int("W4A16_XR_ROUNDS", 1);
+    const long wgs = (long)cu * (rounds_env > 0 ? rounds_env : 1);
+    const int r = (int)((n + wgs - 1) / wgs);
+    return (r + 15) / 16 * 16;
+}
+
+// K <= 8192 and at least three row steps per workgroup: the ring kernel.
+static hipError_t launch_xr(const uint8_t* wq, const uint32_t* sz, const uint16_t* x, void* y, int yb,
+                     int n, int k, int m, int R, hipStream_t s) {
+    const int kg = k / kGroup;
+    const int waves = (kg + kXrGroups - 1) / kXrGroups;
+    const int gpw = (kg + waves - 1) / waves;
+    const size_t shmem = (size_t)waves * (kXrWaveRing + kXrRedBytes);
+    if (shmem > 65536) {
+        static std::atomic<int> raised{0};
+        if (!raised.load(std::memory_order_relaxed)) {
+            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_mfma_xr_kernel),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               (int)(8 * (kXrWaveRing + kXrRedBytes)));
+            if (e != hipSuccess) return e;
+            raised.store(1, std::memory_order_relaxed);
+        }
+    }
+    const dim3 grid((unsigned)((n + R - 1) / R));
+    hipLaunchKernelGGL(gemv_mfma_xr_kernel, grid, dim3((unsigned)(64 * waves)), shmem, s, wq, sz,
+                       x, y, yb, n, k, m, gpw, R);
+    return hipGetLastError();
+}
+
 hipError_t launch_gemv_mfma(const uint8_t* prepared, int64_t n, int64_t k, const uint16_t* x,
                             int64_t m, void* y, bool y_bf16, hipStream_t s) {
     const int kg = (int)(k / kGroup);
+    static const int use_xr = env_int("W4A16_GEMV_XR", 1);
+    if (use_xr && kg <= kXrGroups * 8) {
+        const int R = xr_rows((int)n);
+        if (R >= 48 || use_xr == 2)
+            return launch_xr(prepared, reinterpret_cast<const uint32_t*>(prepared + sz_offset(n, k)),
+                             x, y, y_bf16 ? 1 : 0, (int)n, (int)k, (int)m, R, s);
+    }
     static const int per_wave = env_int("W4A16_MFMA_GPW", 8);
     static const int forced_t = env_int("W4A16_MFMA_TILES", 0);
     static const int chunk = env_int("W4A16_MFMA_CHUNK", 2);

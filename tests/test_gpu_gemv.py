@@ -148,3 +148,62 @@ def test_deterministic_repeat():
     y1 = _run(prep, 8192, 8192, x).clone()
     y2 = _run(prep, 8192, 8192, x)
     assert torch.equal(y1, y2)
+
+
+# ---- batched rows on the ring kernel (K <= 8192 and enough rows per workgroup): ragged
+# group counts (K = 1152: a wave with four of its eight groups), ragged N, several M
+
+@pytest.mark.parametrize("n,k,m", [(12300, 1152, 2), (12300, 1152, 16), (12289, 4096, 5)])
+def test_batched_ring_shapes_full(n, k, m):
+    rng = np.random.default_rng(n + k + m)
+    w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
+    x = torch.from_numpy(rng.standard_normal((m, k)).astype(np.float32)).to(torch.bfloat16)
+    prep, _ = _quant_prepare(torch.from_numpy(w).to(DEV))
+    y = _run(prep, n, k, x.to(DEV))
+    yr, bound, _ = _ref_from_oracle(w, to_np32(x))
+    r = assert_within(to_np32(y), yr, bound, f"ring N={n} K={k} M={m}")
+    print(f"N={n} K={k} M={m}: worst err/bound {r:.3e}")
+
+
+def test_batched_ring_sampled_rows_k8192():
+    n, k, m = 13000, 8192, 16
+    W = synth.normal_weights(n, k, 777, DEV)
+    x16 = synth.normal_activations(m, k, 778, DEV)
+    prep, _ = _quant_prepare(W)
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, 15, 16, n - 1], rng.choice(n, 256, replace=False)]))
+    p, s, z = oracle.quantize_ref(to_np32(W[torch.from_numpy(rows).to(DEV)]))
+    x32 = to_np32(x16)
+    for mm in (2, 8, 16):
+        y = to_np32(_run(prep, n, k, x16[:mm].contiguous()))
+        assert_within(y[:, rows], oracle.gemv_ref(p, s, z, x32[:mm]),
+                      oracle.tolerance_ref(p, s, z, x32[:mm]), f"ring sampled M={mm}")
+
+
+def test_batched_ring_one_hot_exact():
+    rng = np.random.default_rng(11)
+    n, k, m = 12300, 1152, 16
+    W = torch.from_numpy((0.02 * rng.standard_normal((n, k))).astype(np.float32)).to(DEV)
+    prep, (p, s, z) = _quant_prepare(W)
+    cols = rng.choice(k, m, replace=False)
+    x = torch.zeros(m, k, dtype=torch.bfloat16, device=DEV)
+    for i, c in enumerate(cols):
+        x[i, c] = 1.0
+    y = to_np32(_run(prep, n, k, x))
+    wh = oracle.dequant_ref(p.cpu().numpy(), s.cpu().numpy(), z.cpu().numpy())
+    for i, c in enumerate(cols):
+        assert np.array_equal(y[i].astype(np.float64), wh[:, c]), f"column {c}"
+
+
+def test_batched_ring_zero_rows_exact():
+    rng = np.random.default_rng(12)
+    n, k, m = 12300, 1152, 3
+    w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
+    w[::3] = 0.0
+    w[1, :512] = 0.0
+    x = torch.from_numpy(rng.standard_normal((m, k)).astype(np.float32)).to(torch.bfloat16)
+    prep, _ = _quant_prepare(torch.from_numpy(w).to(DEV))
+    y = to_np32(_run(prep, n, k, x.to(DEV)))
+    assert np.all(y[:, ::3] == 0.0)
+    yr, bound, _ = _ref_from_oracle(w, to_np32(x))
+    assert_within(y, yr, bound, "ring rows with zero groups")
