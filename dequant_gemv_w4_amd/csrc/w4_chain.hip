@@ -14,25 +14,37 @@
 // stage and workgroup w takes items w, w+G, w+2G, ... in order (G = the grid,
 // one round of resident workgroups, so every workgroup is running).  A unit is
 // four rows times one 16-byte slice per lane (256 lanes = 8192 inputs); a row of
-// K inputs takes ceil(K/8192) units.  Four units of loads are in flight.
+// K inputs takes ceil(K/8192) units.
+//
+// Loads: every wave has a ring of kRing units in LDS.  The codes and scale/zero
+// words of a unit go straight from global memory to the ring (global_load_lds:
+// lane l's bytes land at slot + 16 l and lane l reads them back, so the ring
+// needs no barrier), kRing units ahead of the arithmetic, across item and stage
+// boundaries.  A unit is five loads and the wait before a unit is an exact count.
 //
 // Per unit and lane the arithmetic is that of gemv_kernel: v_and_or_b32 builds
 // bf16 128+q pairs, v_dot2c_f32_bf16 accumulates D = sum (128+q) x, the slice
 // sum S (same dot2 sequence with the pair (1,1)) removes the offset and the
 // zero, scale16 * (D - (128 + zero) * S) is the slice's share of the group term
 // (page "Weight quantization", section "How it works": one multiply per group).
-// x and the slice sums sit in LDS; rows are reduced across the wave with
-// permlane swaps and DPP, across waves through LDS; no floating-point atomics.
+// x slices sit in registers (loaded when a GEMV starts); rows are reduced across
+// the wave with permlane swaps and DPP, across waves through LDS; no
+// floating-point atomics.
 //
-// Synchronisation: after storing its rows a workgroup fences (release, device
-// scope) and adds 1 to done[stage]; before the first item of a new stage it
-// waits until done[stage-1] equals that stage's item count (acquire).  The wait
-// is bounded: after spin_limit polls it sets a status bit and continues, so no
-// launch can hang.  The last workgroup to finish resets the counters, leaving
-// the workspace zeroed for the next launch.
+// Synchronisation across workgroups (on MI355X the L2 of each XCD is private):
+// rows are stored with device-scope stores (written through), x is read with
+// device-scope loads, and the per-stage counters are device-scope atomics, so no
+// L2 write-back or invalidate is needed.  After its rows of a stage are stored a
+// workgroup waits for those stores (an exact count: only ring loads issued after
+// them may still be in flight) and adds its item count to done[stage]; before the
+// first item of a new stage it waits until done[stage-1] equals that stage's item
+// count.  The wait is bounded: after spin_limit polls it sets a status bit and
+// continues, so no launch can hang.  The last workgroup to finish resets the
+// counters, leaving the workspace zeroed for the next launch.
 #include <atomic>
 #include <cstdlib>
 #include <cstring>
+#include <type_traits>
 #include <vector>
 
 #include "w4_internal.h"
@@ -45,8 +57,13 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int CT = 256;   // threads per workgroup
 constexpr int CW = CT / 64;
-constexpr int NB = 4;     // units of loads in flight
+#ifndef W4_CHAIN_RING
+#define W4_CHAIN_RING 7
+#endif
+constexpr int kRing = W4_CHAIN_RING;    // units in flight per wave
+constexpr int kUnitBytes = 5 * 1024;    // per wave: codes of four rows + their scale/zero words
 constexpr int kMaxItemRows = 64;
+constexpr int kMaxPasses = 4;           // K <= 32768: at most four 16-byte slices per lane
 
 __device__ __forceinline__ float dot2(uint32_t w, uint32_t x, float acc) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w),
@@ -110,7 +127,8 @@ struct Geo {        // geometry of one descriptor (read from the plan)
 };
 
 __device__ __forceinline__ Geo geo_of(const ChainDesc* __restrict__ descs, int d) {
-    const ChainDesc& c = descs[d];
+    // the index is wave-uniform: scalar loads, which do not count against vmcnt
+    const ChainDesc& c = descs[__builtin_amdgcn_readfirstlane(d)];
     Geo g;
     g.w = c.w;
     g.sz = c.sz;
@@ -156,15 +174,57 @@ __device__ __forceinline__ void advance(Cursor& c, Geo& g, const ChainDesc* __re
     seek(c, g, descs, n_desc, total);
 }
 
+// 16 bytes per lane from global memory straight into LDS: lane l of the wave writes
+// bytes [16 l, 16 l + 16) after the wave-uniform LDS address.  Inline assembly, so the
+// compiler neither orders other LDS reads behind it nor waits for it; the kernel counts
+// these loads itself (vmcnt).
+__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(g), "s"(lds_addr)
+                 : "memory", "m0");
+}
+
+// wait until at most 5 n vector-memory operations of this wave are outstanding: the unit
+// computed next was issued n units before the newest one, and every unit is five loads
+__device__ __forceinline__ void wait_units(int n) {
+    switch (n) {
+        case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;             // vmcnt(0)
+        case 1: __builtin_amdgcn_s_waitcnt(0x0F75); break;             // vmcnt(5)
+        case 2: __builtin_amdgcn_s_waitcnt(0x0F7A); break;             // vmcnt(10)
+        case 3: __builtin_amdgcn_s_waitcnt(0x0F7F); break;             // vmcnt(15)
+        case 4: __builtin_amdgcn_s_waitcnt(0x4F74); break;             // vmcnt(20)
+        case 5: __builtin_amdgcn_s_waitcnt(0x4F79); break;             // vmcnt(25)
+        default: __builtin_amdgcn_s_waitcnt(0x4F7E); break;            // vmcnt(30)
+    }
+    asm volatile("" ::: "memory");  // LDS reads of the unit stay after the wait
+}
+
+// device-scope stores (write through to memory, so other XCDs read them with
+// device-scope loads); inline assembly, like the ring loads, so the compiler's wait
+// counts stay out of the unit loop; release_items waits for them explicitly
+typedef __attribute__((address_space(1))) uint32_t gu32;
+typedef __attribute__((address_space(1))) uint16_t gu16;
+__device__ __forceinline__ void store_dev32(uint32_t* p, uint32_t v) {
+    asm volatile("global_store_dword %0, %1, off sc1" : : "v"((gu32*)p), "v"(v) : "memory");
+}
+__device__ __forceinline__ void store_dev16(uint16_t* p, uint32_t v) {
+    asm volatile("global_store_short %0, %1, off sc1" : : "v"((gu16*)p), "v"(v) : "memory");
+}
+
+// barrier for LDS data only (no fence: the ring's loads in flight are not waited for)
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 __global__ __launch_bounds__(CT) void chain_kernel(const ChainDesc* __restrict__ descs,
                                                    const int32_t* __restrict__ stage_items,
                                                    uint32_t* __restrict__ ws, int n_desc,
-                                                   int n_stages, int total, int max_k,
-                                                   int spin_limit) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    uint16_t* xs = reinterpret_cast<uint16_t*>(smem);                         // [max_k] bf16
-    float* sxs = reinterpret_cast<float*>(smem + (size_t)max_k * 2);          // [max_k/32]
-    float* red = sxs + max_k / 32;                                           // [CW][kMaxItemRows]
+                                                   int n_stages, int total, int spin_limit) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // rings, then row sums
 
     uint32_t* status = ws;                // word 0: bit 0 = a stage wait gave up
     uint32_t* exit_count = ws + 1;        // word 1: workgroups that finished
@@ -175,46 +235,58 @@ __global__ __launch_bounds__(CT) void chain_kernel(const ChainDesc* __restrict__
     const int lane = tid & 63;
     const int grid = gridDim.x;
 
+    const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+    const uint32_t ring = __builtin_amdgcn_readfirstlane(smem_lds + wave * kRing * kUnitBytes);
+    const uint8_t* ring_p = smem + wave * kRing * kUnitBytes;
+    float* red = reinterpret_cast<float*>(smem + CW * kRing * kUnitBytes);  // [CW][kMaxItemRows]
+
     uint32_t nib_mask, bias_bits;
     asm volatile("s_mov_b32 %0, 0x000F000F" : "=s"(nib_mask));
     asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(bias_bits));
 
-    // ---- load cursor and compute cursor
+    // ---- issue cursor (loads run kRing units ahead) and compute cursor
     Cursor ic{(int)blockIdx.x, 0, 0, 0};
     Geo ig = geo_of(descs, 0);
     seek(ic, ig, descs, n_desc, total);
     Cursor cc = ic;
     Geo cg = ig;
+    int issued = 0, computed = 0;   // units of this workgroup (the same in every wave)
+    int units_since_store = 0;       // units issued after this wave's latest row stores
 
-    u32x4_t wb[NB][4];
-    u32x4_t sb[NB];
-    auto issue = [&](u32x4_t (&w)[4], u32x4_t& s) {
+    auto issue_unit = [&]() {
         const int S = ig.k >> 5;
         const int r0 = (ic.item - ig.first) * ig.rows + ic.step * 4;
-        const int rlast = ig.n - 1;
-        const int sl = min(tid + ic.pass * CT, S - 1);
+        const int sl = min(tid + ic.pass * CT, S - 1);   // lanes past the last slice repeat it
         const int64_t row_bytes = (int64_t)ig.k / 2;
+        const uint32_t slot =
+            __builtin_amdgcn_readfirstlane(ring + (uint32_t)(issued % kRing) * kUnitBytes);
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const uint8_t* p = ig.w + (int64_t)min(r0 + rr, rlast) * row_bytes + (uint32_t)sl * 16u;
-            w[rr] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-        }
-        const uint8_t* q = ig.sz + ((int64_t)(r0 >> 2) * (ig.k >> 7) + (sl >> 2)) * 16;
-        s = *reinterpret_cast<const u32x4_t*>(q);
+        for (int rr = 0; rr < 4; ++rr)
+            lds_dma16(ig.w + (int64_t)min(r0 + rr, ig.n - 1) * row_bytes + (uint32_t)sl * 16u,
+                      slot + rr * 1024);
+        lds_dma16(ig.sz + ((int64_t)(r0 >> 2) * (ig.k >> 7) + (sl >> 2)) * 16, slot + 4096);
+        ++issued;
+        ++units_since_store;
+        advance(ic, ig, descs, n_desc, total, grid);
     };
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-        if (ic.item >= 0) {
-            issue(wb[b], sb[b]);
-            advance(ic, ig, descs, n_desc, total, grid);
-        }
-    }
+    for (int b = 0; b < kRing && ic.item >= 0; ++b) issue_unit();
 
     int cur_stage = 0;
     const uint16_t* cur_x = nullptr;
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
     int items_this_stage = 0;
+    uint32_t xr[kMaxPasses][16];   // x slices of this lane (bf16 pairs), one per pass
+    float sx[kMaxPasses];          // their sums, by the same dot2 sequence as the weights
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
 
+    // stores of this workgroup are complete before the count that publishes them: only the
+    // ring loads issued after the latest stores may still be in flight
+    auto release_items = [&](int s, int count) {
+        wait_units(min(units_since_store, kRing - 1));
+        lds_barrier();
+        if (tid == 0 && count > 0)
+            __hip_atomic_fetch_add(done + s, (uint32_t)count, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+    };
     auto wait_stage = [&](int s) {  // every item of stage s stored
         if (tid == 0) {
             const uint32_t need = (uint32_t)stage_items[s];
@@ -222,84 +294,79 @@ __global__ __launch_bounds__(CT) void chain_kernel(const ChainDesc* __restrict__
             while (__hip_atomic_load(done + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
                 __builtin_amdgcn_s_sleep(2);
                 if (++polls > spin_limit) {
-                    atomicOr(status, 1u);
+                    __hip_atomic_fetch_or(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     break;
                 }
             }
         }
-        __syncthreads();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        lds_barrier();
     };
-
-    auto release_items = [&](int s, int count) {  // this workgroup stored `count` items of stage s
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        __syncthreads();
-        if (tid == 0 && count > 0)
-            __hip_atomic_fetch_add(done + s, (uint32_t)count, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-    };
-
-    auto compute = [&](const u32x4_t (&w)[4], const u32x4_t& s) {
+    // x of the current GEMV: device-scope loads, which read what other workgroups stored
+    auto load_x = [&]() {
         const int S = cg.k >> 5;
-        const int passes = passes_of(cg);
+        const gu32* xw = (const gu32*)reinterpret_cast<const uint32_t*>(cg.x);
+#pragma unroll
+        for (int p = 0; p < kMaxPasses; ++p) {
+            const int sl = tid + p * CT;
+            const bool ok = sl < S;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                xr[p][i] = ok ? __hip_atomic_load((gu32*)(xw + (int64_t)sl * 16 + i), __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT)
+                              : 0u;
+            float d = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) d = dot2(0x3F803F80u, xr[p][i], d);
+            sx[p] = d;
+        }
+    };
+
+    auto unit_math = [&](auto pass_c) {
+        constexpr int P = decltype(pass_c)::value;
+        const uint8_t* slot = ring_p + (computed % kRing) * kUnitBytes;
+        const u32x4_t s4 = *reinterpret_cast<const u32x4_t*>(slot + 4096 + 16 * lane);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const u32x4_t w4 = *reinterpret_cast<const u32x4_t*>(slot + rr * 1024 + 16 * lane);
+            const uint32_t szw = s4[rr];
+            const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)(szw & 0xFFFFu));
+            const float zb = (float)((szw >> 16) & 0xFFu);
+            float d = 0.0f;
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    d = dot2(((w4[t] >> (4 * q)) & nib_mask) | bias_bits, xr[P][4 * t + q], d);
+            acc[rr] = fmaf(sc, fmaf(-zb, sx[P], d), acc[rr]);
+        }
+    };
+
+    while (cc.item >= 0) {
         if (cc.step == 0 && cc.pass == 0) {
-            // ---- first unit of an item: stage order, then x of this GEMV into LDS
+            // ---- first unit of an item: stage order, then x of this GEMV
             if (cg.stage != cur_stage) {
                 release_items(cur_stage, items_this_stage);
                 items_this_stage = 0;
                 for (int st = cur_stage; st < cg.stage; ++st) wait_stage(st);
                 cur_stage = cg.stage;
-                cur_x = nullptr;  // x of a later stage may be rewritten by an earlier one
+                cur_x = nullptr;  // x of a later stage may be written by an earlier one
             }
             if (cg.x != cur_x) {
-                __syncthreads();  // every wave is done with the previous x
-                for (int sl = tid; sl < S; sl += CT) {
-                    const uint4* px = reinterpret_cast<const uint4*>(cg.x + (int64_t)sl * 32);
-                    uint32_t v[16];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const uint4 t = px[q];
-                        v[4 * q] = t.x;
-                        v[4 * q + 1] = t.y;
-                        v[4 * q + 2] = t.z;
-                        v[4 * q + 3] = t.w;
-                        reinterpret_cast<uint4*>(xs + (int64_t)sl * 32)[q] = t;
-                    }
-                    float d = 0.0f;
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) d = dot2(0x3F803F80u, v[i], d);
-                    sxs[sl] = d;
-                }
-                __syncthreads();
+                load_x();
                 cur_x = cg.x;
             }
         }
-        const int sl = tid + cc.pass * CT;
-        if (sl < S) {
-            uint32_t xr[16];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint4 t = reinterpret_cast<const uint4*>(xs + (int64_t)sl * 32)[q];
-                xr[4 * q] = t.x;
-                xr[4 * q + 1] = t.y;
-                xr[4 * q + 2] = t.z;
-                xr[4 * q + 3] = t.w;
-            }
-            const float sx = sxs[sl];
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const uint32_t szw = s[rr];
-                const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)(szw & 0xFFFFu));
-                const float zb = (float)((szw >> 16) & 0xFFu);
-                float d = 0.0f;
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        d = dot2(((w[rr][t] >> (4 * q)) & nib_mask) | bias_bits, xr[4 * t + q], d);
-                acc[rr] = fmaf(sc, fmaf(-zb, sx, d), acc[rr]);
-            }
+        wait_units(issued - computed - 1);
+        const int passes = passes_of(cg);
+        switch (cc.pass) {
+            case 0: unit_math(std::integral_constant<int, 0>{}); break;
+            case 1: unit_math(std::integral_constant<int, 1>{}); break;
+            case 2: unit_math(std::integral_constant<int, 2>{}); break;
+            default: unit_math(std::integral_constant<int, 3>{}); break;
         }
+        // a lane past the last slice of the row (ragged K) holds x = 0 and sum 0: it adds
+        // exactly 0 to its rows
+        ++computed;
         if (cc.pass == passes - 1) {
             const float k = reduce4(acc[0], acc[1], acc[2], acc[3]);
             if ((lane & 15) == 0) red[wave * kMaxItemRows + cc.step * 4 + (lane >> 4)] = k;
@@ -307,38 +374,27 @@ __global__ __launch_bounds__(CT) void chain_kernel(const ChainDesc* __restrict__
             const int nrows = item_rows(cg, cc.item);
             if (cc.step == (nrows + 3) / 4 - 1) {
                 // ---- last unit of the item: combine the waves and store the rows
-                __syncthreads();
+                lds_barrier();
                 if (tid < nrows) {
                     float v = 0.0f;
 #pragma unroll
                     for (int wv = 0; wv < CW; ++wv) v += red[wv * kMaxItemRows + tid];
                     const int64_t row = (int64_t)(cc.item - cg.first) * cg.rows + tid;
                     if (cg.y_bf16)
-                        static_cast<uint16_t*>(cg.y)[row] = (uint16_t)bf16_bits_rne(v);
+                        store_dev16(static_cast<uint16_t*>(cg.y) + row, bf16_bits_rne(v));
                     else
-                        static_cast<float*>(cg.y)[row] = v;
+                        store_dev32(static_cast<uint32_t*>(cg.y) + row, __float_as_uint(v));
                 }
-                __syncthreads();  // red is reused by the next item
+                units_since_store = 0;
+                lds_barrier();  // red is reused by the next item
                 ++items_this_stage;
             }
         }
-    };
-
-    while (cc.item >= 0) {
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            if (cc.item < 0) break;
-            compute(wb[b], sb[b]);
-            if (ic.item >= 0) {
-                issue(wb[b], sb[b]);
-                advance(ic, ig, descs, n_desc, total, grid);
-            }
-            advance(cc, cg, descs, n_desc, total, grid);
-        }
+        // refill the slot just consumed (its LDS reads are complete: their values were used)
+        if (ic.item >= 0) issue_unit();
+        advance(cc, cg, descs, n_desc, total, grid);
     }
     release_items(cur_stage, items_this_stage);
-    // a workgroup without items in the later stages still counts nothing there: the
-    // totals per stage only include items that exist, so waiting workgroups proceed
 
     // ---- the last workgroup out resets the counters for the next launch
     __syncthreads();
@@ -364,8 +420,8 @@ int chain_compute_units() {
 
 }  // namespace
 
-size_t chain_lds_bytes(int max_k) {
-    return (size_t)max_k * 2 + (size_t)(max_k / 32) * 4 + (size_t)CW * kMaxItemRows * 4;
+size_t chain_lds_bytes(int) {
+    return (size_t)CW * kRing * kUnitBytes + (size_t)CW * kMaxItemRows * 4;
 }
 
 static hipError_t allow_lds(size_t lds) {
@@ -394,7 +450,7 @@ hipError_t launch_chain(const ChainHeader& h, const uint8_t* plan_dev, uint32_t*
     hipError_t e = allow_lds(lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(chain_kernel, dim3((unsigned)h.grid), dim3(CT), lds, s, descs, stage_items,
-                       ws, h.n_desc, h.n_stages, h.total_items, h.max_k, h.spin_limit);
+                       ws, h.n_desc, h.n_stages, h.total_items, h.spin_limit);
     return hipGetLastError();
 }
 
