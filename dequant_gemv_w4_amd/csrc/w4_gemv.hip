@@ -416,9 +416,10 @@ hipError_t dispatch(bool x_f32, int spt, int mt, const GemvArgs& a, dim3 block, 
 
 hipError_t launch_gemv(const uint8_t* prepared, int64_t n, int64_t k, const void* x, bool x_f32,
                        int64_t m, void* y, bool y_bf16, hipStream_t s) {
-    // two or more bf16 rows: the matrix-core kernel reads the weights once for all rows
+    // three or more bf16 rows: the matrix-core kernels read the weights once for all rows
+    // (at two rows the dot2 kernel below is faster at every 70B shape, measured on MI355X)
     static const int use_mfma = env_int("W4A16_GEMV_MFMA", 1);
-    if (!x_f32 && m >= 2 && use_mfma)
+    if (!x_f32 && m >= 3 && use_mfma)
         return launch_gemv_mfma(prepared, n, k, static_cast<const uint16_t*>(x), m, y, y_bf16, s);
     const int S = (int)(k / 32);
     GemvArgs a;
