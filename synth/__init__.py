@@ -223,3 +223,29 @@ def prefill_operands(device="cpu", m: int = 4096, n: int = 28672, k: int = 8192)
     w = normal_weights(n, k, seed, device)
     x = normal_activations(m, k, seed + 50, device)
     return w, x
+
+
+def page_error_matrix(seed: int = 11, rows: int = 256, cols: int = 1024) -> np.ndarray:
+    """Seeded 256 x 1024 test matrix of page "Quantization", section "Code" (fp64).
+
+    Row r is Gaussian with standard deviation 0.02 * exp(g_r), g_r ~ N(0, 0.5);
+    then eight entries become +-0.6 outliers.  Draws come from Python's seeded
+    Mersenne-Twister generator in the page's order: per row the deviation draw and
+    the row's values; per outlier its sign, its row and its column (the page's
+    one-line assignment evaluates the value before the subscripts).
+    """
+    import math
+    import random
+
+    rng = random.Random(seed)
+    w = np.empty((rows, cols), dtype=np.float64)
+    for r in range(rows):
+        sd = 0.02 * math.exp(rng.gauss(0.0, 0.5))
+        w[r] = [rng.gauss(0.0, sd) for _ in range(cols)]
+    for _ in range(8):
+        sign = rng.choice((-1, 1))
+        r = rng.randrange(rows)
+        c = rng.randrange(cols)
+        w[r, c] = sign * 0.6
+    return w
+

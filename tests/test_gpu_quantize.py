@@ -123,3 +123,21 @@ def test_prepare_unprepare_round_trip_random_bytes():
         assert torch.equal(z2, zeros)
         # the prepared words are a permutation of the canonical nibbles
         assert not torch.equal(prep[: packed.numel()], packed.flatten()) or n * k < 256
+
+
+def test_page_error_matrix_bit_exact_and_its_error():
+    """The seeded 256 x 1024 matrix of page "Quantization", section "Code" (eight 0.6
+    outliers) quantized by the library: bit-exact codes, so the asymmetric g128 error of
+    the product path is the oracle's (the page's "Try it" item 1 asks for it)."""
+    from oracle import quant_error
+
+    w32 = synth.page_error_matrix().astype(np.float32)
+    gpu, st = _gpu_quant(torch.from_numpy(w32).to(DEV))
+    assert st == 0
+    ref = oracle.quantize_ref(w32)
+    assert_quant_equal(gpu, ref, "page error matrix")
+    db, rel = quant_error.sqnr_db(w32.astype(np.float64), oracle.dequant_ref(*gpu))
+    print(f"asymmetric g128 on the page matrix: SQNR {db:.2f} dB, relative RMS {100 * rel:.2f}%")
+    sym_db = [r[2] for r in quant_error.table(synth.page_error_matrix()) if r[0] == "INT4 group 128"][0]
+    assert db > sym_db
+

@@ -18,6 +18,7 @@ import pytest
 
 import oracle
 import synth
+from oracle import quant_error
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -427,3 +428,75 @@ def test_regression_snapshot_of_single_layer():
         assert " ".join(f"{v:04x}" for v in s16.view(np.uint16)[i][:8]) == snap[f"s16_head_{r}"]
         assert " ".join(str(v) for v in z[i][:8]) == snap[f"zero_head_{r}"]
         assert float.fromhex(snap[f"y_{r}"]) == y[i]
+
+
+# ---------------------------------------------------------------------------
+# Error harness: page "Quantization", section "Code" (its printed table) and
+# "Try it", item 1 (asymmetric scales per group of 128)
+# ---------------------------------------------------------------------------
+
+def _page_error_table():
+    rows = []
+    with open(os.path.join(GOLDEN, "page_error_table.txt")) as fh:
+        for line in fh:
+            if line.startswith("#") or not line.strip():
+                continue
+            rows.append([f.strip() for f in line.split("|")])
+    return rows
+
+
+def test_error_harness_reproduces_page_table():
+    """Every printed figure of the page's table, at the page's precision."""
+    got = quant_error.table(synth.page_error_matrix())
+    want = _page_error_table()
+    assert [g[0] for g in got] == [r[0] for r in want]
+    for (name, bits, db, rel, gb, ms), r in zip(got, want):
+        assert [f"{bits:.2f}", f"{db:.1f}", f"{100 * rel:.2f}", f"{gb:.0f}", f"{ms:.1f}"] == r[1:], name
+
+
+def _e4m3_values():
+    """All finite E4M3 values >= 0 from the bit fields (4 exponent, 3 mantissa, bias 7)."""
+    vals = []
+    for e in range(16):
+        for m in range(8):
+            if e == 15 and m == 7:
+                continue   # the NaN code
+            vals.append((m / 8) * 2.0 ** -6 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7))
+    return np.array(sorted(vals))
+
+
+def test_e4m3_rounding_is_nearest_value_ties_to_even():
+    grid = _e4m3_values()
+    assert grid[-1] == 448.0 and grid[1] == 2.0 ** -9
+    rng = np.random.default_rng(3)
+    t = np.concatenate([rng.uniform(0, 460, 4000), 2.0 ** rng.uniform(-12, 8, 4000),
+                        (grid[:-1] + grid[1:]) / 2, grid])
+    got = quant_error.e4m3_round(t)
+    for v, r in zip(t, got):
+        a = min(v, 448.0)
+        d = np.abs(grid - a)
+        idx = np.flatnonzero(d == d.min())
+        # a tie goes to the even mantissa field; in the sorted grid each binade holds the
+        # fields 0..7 in order, so the field's parity is the index's parity
+        if len(idx) == 2:
+            idx = [i for i in idx if i % 2 == 0]
+        assert r == grid[idx[0]], v
+    assert np.array_equal(quant_error.e4m3_round(-t), -got)
+
+
+def test_asymmetric_g128_step_and_error_against_symmetric():
+    """Try it, item 1.  The page prints no answer, so the value itself is unpinned; what is
+    fixed: with the range widened to hold 0, hi - lo <= 2 max|w|, so the asymmetric step
+    (hi - lo) / 15 is at most 14/15 of the symmetric step max|w| / 7 in every group, and
+    the reconstruction error must beat the symmetric group-128 row of the table."""
+    w = synth.page_error_matrix()
+    w32, w_hat, packed, s16, zeros = quant_error.asym_w4(w)
+    g = w32.astype(np.float64).reshape(w.shape[0], -1, 128)
+    sym_step = np.abs(g).max(axis=2) / 7
+    asym_step = s16.view(np.float16).astype(np.float64)
+    assert np.all(asym_step <= sym_step * (14 / 15) * (1 + 2.0 ** -10))
+    db, rel = quant_error.sqnr_db(w32.astype(np.float64), w_hat)
+    sym_db = [r[2] for r in quant_error.table(w) if r[0] == "INT4 group 128"][0]
+    assert db > sym_db + 0.5
+    assert 0.09 < rel < 0.1224
+
