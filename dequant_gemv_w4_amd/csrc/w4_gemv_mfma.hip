@@ -1,4 +1,5 @@
-// Fused dequantizing product for a few activation rows (2 <= M <= 16, bf16 x)
+// Fused dequantizing product for a few activation rows (bf16 x, up to 16 rows; w4_gemv
+// sends 3 <= M <= 16 here)
 // on the matrix cores.
 //
 // The same group term as the one-row kernel, y[m, n] = sum_g scale16[n, g] *
