@@ -179,6 +179,72 @@ def per_shape(prepared, layers: int, dev: str, reps: int = 3, fused: bool = Fals
     return out
 
 
+def page_layer(dev: str, reps: int = 5, copies: int = 64):
+    """The page's single layer: W 4096x4096 and binary32 x from its xorshift draws, M=1.
+
+    ``copies`` prepared copies (64 x 8.8 MB, past the 256 MB MALL) are multiplied back to
+    back in one graph, so every call streams its weights from HBM.
+    """
+    import torch
+
+    import dequant_gemv_w4_amd as w4
+    import synth
+    from dequant_gemv_w4_amd.decode import DecodeStep, GemvCall
+
+    w, x = synth.page_single_layer(4096, 4096)
+    p, s, z = w4.w4_quantize(torch.from_numpy(w).to(dev))
+    prep = w4.w4_prepare(p, s, z)
+    xt = torch.from_numpy(x).to(dev)
+    calls = [GemvCall(prep.clone(), 4096, 4096, xt, torch.empty(1, 4096, dtype=torch.float32, device=dev))
+             for _ in range(copies)]
+    st = DecodeStep(calls)
+    st.capture()
+    ms = time_step(st, reps, 1)
+    gbs = st.algorithmic_bytes() / (ms * 1e-3) / 1e9
+    return {"N": 4096, "K": 4096, "x": "binary32", "copies": copies,
+            "us_per_call": round(ms * 1000 / copies, 2), "GB/s": round(gbs, 1),
+            "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
+
+
+def llama7b_layers(dev: str, layers: int = 6, reps: int = 5, fused: bool = False):
+    """7B-shaped layers with 1 % outlier channels (x20 in W columns and x), bf16 x, M=1.
+
+    ``layers`` distinct layers (6 x 106 MB, past the MALL) per step.  Unfused: seven
+    w4_gemv calls per layer, each matrix with its own activation row.  Fused: the
+    same-input matrices are concatenated along N (q|k|v 12288x4096, gate|up 22016x4096,
+    each matrix keeping its own outlier columns) and share the first one's activation
+    row, four calls per layer as in a real layer.
+    """
+    import torch
+
+    import dequant_gemv_w4_amd as w4
+    import synth
+    from dequant_gemv_w4_amd.decode import DecodeStep, GemvCall
+
+    groups = ((("q", "k", "v"), ("o",), ("gate", "up"), ("down",)) if fused
+              else tuple((name,) for name in synth.MATRIX_ORDER))
+    calls = []
+    for layer in range(layers):
+        for group in groups:
+            parts = [synth.llama7b_layer_matrix(name, layer, dev) for name in group]
+            W = torch.cat([w for w, _ in parts]) if len(parts) > 1 else parts[0][0]
+            x = parts[0][1]
+            n, k = W.shape
+            p, s, z = w4.w4_quantize(W)
+            calls.append(GemvCall(w4.w4_prepare(p, s, z), n, k, x,
+                                  torch.empty(1, n, dtype=torch.float32, device=dev)))
+            del W, parts, p, s, z
+    st = DecodeStep(calls)
+    st.capture()
+    ms = time_step(st, reps, 1)
+    us_layer = ms * 1000 / layers
+    gbs = st.algorithmic_bytes() / (ms * 1e-3) / 1e9
+    return {"layers_per_step": layers, "launches_per_layer": len(groups),
+            "us_per_layer": round(us_layer, 2), "GB/s": round(gbs, 1),
+            "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+            "tokens_per_s_equiv_32_layers": round(1e6 / (32 * us_layer), 1)}
+
+
 def prefill_gemm(prepared, dev: str, reps: int = 3):
     import torch
 
@@ -238,10 +304,12 @@ def cpu_baseline():
     W = synth.normal_weights(n, k, synth.seed_for(4, "o", 0), "cpu").numpy()
     x = synth.normal_activations(1, k, 40002, "cpu").float().numpy()
     p, s, z = oracle.quantize_ref(W)
-    reps = 3
+    # repetitions until about 10 s of host work
+    reps = 0
     t0 = time.perf_counter()
-    for _ in range(reps):
+    while reps < 3 or time.perf_counter() - t0 < 10.0:
         oracle.gemv_ref(p, s, z, x)
+        reps += 1
     dt = (time.perf_counter() - t0) / reps
     nbytes = n * k // 2 + (n * k // 128) * 3 + k * 2 + n * 4
     threads = 1
@@ -370,6 +438,12 @@ def main() -> int:
         del unfused
         torch.cuda.empty_cache()
         result["quantizer"] = quantizer_rate(dev)
+        result["page_single_layer_m1"] = page_layer(dev)
+        log(f"page layer: {result['page_single_layer_m1']}")
+        result["llama7b_layer_m1"] = llama7b_layers(dev)
+        log(f"7B layers: {result['llama7b_layer_m1']}")
+        result["llama7b_layer_fused_m1"] = llama7b_layers(dev, fused=True)
+        log(f"7B layers, fused: {result['llama7b_layer_fused_m1']}")
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle sample")
