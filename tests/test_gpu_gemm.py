@@ -68,3 +68,46 @@ def test_gemm_deterministic():
     y2 = w4.w4_gemm(prep, 512, 2048, X)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
+
+
+def test_one_hot_rows_and_zero_weight_rows_exact():
+    """The group term is folded as scale16 * (P - (128 + zero) * S) with S from the same MFMA
+    steps as P (page "Weight quantization", section "How it works"), so a one-hot row of X
+    returns a dequantized weight column exactly, and weight rows that are all zero give
+    exactly 0 for any X."""
+    rng = np.random.default_rng(41)
+    n, k, m = 300, 1024, 130
+    w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
+    w[::7] = 0.0
+    w[1, :256] = 0.0
+    prep = _prep(torch.from_numpy(w).to(DEV))
+    p, s, z = oracle.quantize_ref(w)
+    wh = oracle.dequant_ref(p, s, z)
+    cols = rng.choice(k, m, replace=True)
+    X = torch.zeros(m, k, dtype=torch.bfloat16)
+    X[torch.arange(m), torch.from_numpy(cols)] = 1.0
+    Y = to_np32(w4.w4_gemm(prep, n, k, X.to(DEV)))
+    for i, c in enumerate(cols):
+        assert np.array_equal(Y[i].astype(np.float64), wh[:, c]), f"row {i} (column {c})"
+    Xr = torch.from_numpy(rng.standard_normal((m, k)).astype(np.float32)).to(torch.bfloat16)
+    Yr = to_np32(w4.w4_gemm(prep, n, k, Xr.to(DEV)))
+    assert np.all(Yr[:, ::7] == 0.0)
+    x32 = to_np32(Xr)
+    assert_within(Yr, oracle.gemv_ref(p, s, z, x32), oracle.tolerance_ref(p, s, z, x32), "random X")
+
+
+def test_bf16_output():
+    rng = np.random.default_rng(43)
+    n, k, m = 384, 2048, 200
+    w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
+    X = torch.from_numpy(rng.standard_normal((m, k)).astype(np.float32)).to(torch.bfloat16)
+    prep = _prep(torch.from_numpy(w).to(DEV))
+    Y = w4.w4_gemm(prep, n, k, X.to(DEV), out_dtype=torch.bfloat16)
+    assert Y.dtype == torch.bfloat16
+    p, s, z = oracle.quantize_ref(w)
+    x32 = to_np32(X)
+    yr = oracle.gemv_ref(p, s, z, x32)
+    # the bf16 store adds at most half an ulp of bf16 (2^-9 relative)
+    assert_within(to_np32(Y), yr, oracle.tolerance_ref(p, s, z, x32), "bf16 Y",
+                  extra=np.abs(yr) * 2.0 ** -8)
+

@@ -207,3 +207,40 @@ def test_batched_ring_zero_rows_exact():
     assert np.all(y[:, ::3] == 0.0)
     yr, bound, _ = _ref_from_oracle(w, to_np32(x))
     assert_within(y, yr, bound, "ring rows with zero groups")
+
+
+def test_decode_step_graph_replays_match_eager():
+    """A captured decode step (every w4_gemv of two 70B-shaped layers, M=1 and M=4) gives,
+    on every replay, the bits of the eager launches; eager work and synchronizations run
+    between the replays."""
+    from dequant_gemv_w4_amd.decode import DecodeStep, GemvCall
+
+    shapes = synth.LLAMA70B_FUSED_SHAPES
+    preps = {}
+    for layer in range(2):
+        for name in synth.FUSED_ORDER:
+            n, k = shapes[name]
+            W = synth.normal_weights(n, k, synth.seed_for(3, synth.FUSED_PARTS[name][0], layer) + 7, DEV)
+            preps[(layer, name)] = _quant_prepare(W)[0]
+            del W
+    for m in (1, 4):
+        xs = {8192: synth.normal_activations(m, 8192, 901, DEV),
+              28672: synth.normal_activations(m, 28672, 902, DEV)}
+        calls = [GemvCall(preps[(layer, name)], shapes[name][0], shapes[name][1],
+                          xs[shapes[name][1]],
+                          torch.empty(m, shapes[name][0], dtype=torch.float32, device=DEV))
+                 for layer in range(2) for name in synth.FUSED_ORDER]
+        step = DecodeStep(calls)
+        step.run_eager()
+        torch.cuda.synchronize()
+        eager = [c.y.clone() for c in calls]
+        step.capture()
+        for rep in range(3):
+            for c in calls:
+                c.y.fill_(float("nan"))
+            torch.cuda.synchronize()
+            step.run()
+            torch.cuda.synchronize()
+            for i, c in enumerate(calls):
+                assert torch.equal(c.y, eager[i]), f"M={m} replay {rep} call {i}"
+
