@@ -416,10 +416,14 @@ hipError_t dispatch(bool x_f32, int spt, int mt, const GemvArgs& a, dim3 block, 
 
 hipError_t launch_gemv(const uint8_t* prepared, int64_t n, int64_t k, const void* x, bool x_f32,
                        int64_t m, void* y, bool y_bf16, hipStream_t s) {
-    // three or more bf16 rows: the matrix-core kernels read the weights once for all rows
-    // (at two rows the dot2 kernel below is faster at every 70B shape, measured on MI355X)
+    // bf16 rows: the matrix-core kernels read the weights once for all rows.  The dot2
+    // kernel below is faster (measured on MI355X at the 70B shapes) at two rows everywhere,
+    // and at three or four rows while it needs a single pass over the weights (K <= 16384)
+    // and N is at most 16384 (M=3: qkv 14.4 against 17.8 us, o 12.4 against 13.8 us; gate_up
+    // and down stay on the matrix cores)
     static const int use_mfma = env_int("W4A16_GEMV_MFMA", 1);
-    if (!x_f32 && m >= 3 && use_mfma)
+    const bool dot2_wins = m <= 2 || (m <= 4 && k <= 16384 && n <= 16384);
+    if (!x_f32 && !dot2_wins && use_mfma)
         return launch_gemv_mfma(prepared, n, k, static_cast<const uint16_t*>(x), m, y, y_bf16, s);
     const int S = (int)(k / 32);
     GemvArgs a;

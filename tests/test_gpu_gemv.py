@@ -153,7 +153,7 @@ def test_deterministic_repeat():
 # ---- batched rows on the ring kernel (K <= 8192 and enough rows per workgroup): ragged
 # group counts (K = 1152: a wave with four of its eight groups), ragged N, several M
 
-@pytest.mark.parametrize("n,k,m", [(12300, 1152, 3), (12300, 1152, 16), (12289, 4096, 5)])
+@pytest.mark.parametrize("n,k,m", [(20000, 1152, 3), (12300, 1152, 16), (12289, 4096, 5)])
 def test_batched_ring_shapes_full(n, k, m):
     rng = np.random.default_rng(n + k + m)
     w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
@@ -166,7 +166,7 @@ def test_batched_ring_shapes_full(n, k, m):
 
 
 def test_batched_ring_sampled_rows_k8192():
-    n, k, m = 13000, 8192, 16
+    n, k, m = 20000, 8192, 16
     W = synth.normal_weights(n, k, 777, DEV)
     x16 = synth.normal_activations(m, k, 778, DEV)
     prep, _ = _quant_prepare(W)
@@ -197,7 +197,7 @@ def test_batched_ring_one_hot_exact():
 
 def test_batched_ring_zero_rows_exact():
     rng = np.random.default_rng(12)
-    n, k, m = 12300, 1152, 3
+    n, k, m = 20000, 1152, 3
     w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
     w[::3] = 0.0
     w[1, :512] = 0.0
