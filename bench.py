@@ -245,7 +245,7 @@ def llama7b_layers(dev: str, layers: int = 6, reps: int = 5, fused: bool = False
             "tokens_per_s_equiv_32_layers": round(1e6 / (32 * us_layer), 1)}
 
 
-def prefill_gemm(prepared, dev: str, reps: int = 3):
+def prefill_gemm(prepared, dev: str, reps: int = 10, warmup: int = 3):
     import torch
 
     import dequant_gemv_w4_amd as w4
@@ -256,7 +256,8 @@ def prefill_gemm(prepared, dev: str, reps: int = 3):
     Y = torch.empty(m, n, dtype=torch.float32, device=dev)
     ws = torch.empty(w4.w4_gemm_workspace_bytes(m, n, k), dtype=torch.uint8, device=dev)
     prep = prepared[(0, "gate")]
-    w4.w4_gemm(prep, n, k, X, Y=Y, workspace=ws)
+    for _ in range(warmup):   # the first calls after idle run slower (clock ramp)
+        w4.w4_gemm(prep, n, k, X, Y=Y, workspace=ws)
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
