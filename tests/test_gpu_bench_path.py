@@ -1,0 +1,55 @@
+"""Parity of the decode step exactly as the benchmark builds and times it.
+
+The benchmark draws each layer's weights on the GPU, quantizes and prepares them with
+q|k|v and gate|up concatenated along N, captures the step into a graph and replays it.
+Here two such layers are built with the benchmark's own functions, the step is replayed
+at M = 1, 4 and 16, and sampled rows of every output are checked against the oracle on
+the same weight rows (drawn again from the same seeds) and the same activations.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import bench
+import oracle
+import synth
+from _util import assert_within, to_np32
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def test_bench_step_sampled_rows_against_oracle():
+    layers = 2
+    prepared = bench.build_stack(layers, DEV, fused=True)
+    rng = np.random.default_rng(77)
+    order = synth.FUSED_ORDER
+    shapes = synth.LLAMA70B_FUSED_SHAPES
+    # the sampled weight rows, drawn again exactly as build_stack drew them
+    refs = {}
+    for layer in range(layers):
+        for name in order:
+            n, k = shapes[name]
+            seed = synth.seed_for(4, synth.FUSED_PARTS[name][0], layer) + 10000
+            W = synth.normal_weights(n, k, seed, DEV)
+            rows = np.unique(np.concatenate([[0, n - 1], rng.choice(n, 62, replace=False)]))
+            refs[(layer, name)] = (rows, oracle.quantize_ref(to_np32(W[torch.from_numpy(rows).to(DEV)])))
+            del W
+    for m in (1, 4, 16):
+        step = bench.make_step(prepared, layers, m, DEV, fused=True)
+        step.capture()
+        for _ in range(2):
+            step.run()
+        torch.cuda.synchronize()
+        worst = 0.0
+        for i, call in enumerate(step.calls):
+            layer, name = divmod(i, len(order))
+            rows, (p, s, z) = refs[(layer, order[name])]
+            x32 = to_np32(call.x)
+            r = assert_within(to_np32(call.y)[:, rows], oracle.gemv_ref(p, s, z, x32),
+                              oracle.tolerance_ref(p, s, z, x32),
+                              f"bench step M={m} layer {layer} {order[name]}")
+            worst = max(worst, r)
+        print(f"M={m}: worst err/bound {worst:.3e}")
+        del step
