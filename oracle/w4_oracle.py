@@ -229,6 +229,46 @@ def quantize_ref(w: np.ndarray, group: int = GROUP):
     return packed, s16, z
 
 
+# ---------------------------------------------------------------------------
+# Symmetric variant (page "Quantization" › "How it really works" › "The mechanics: scale,
+# round, clamp"; page "LLM Quantization Architecture in Depth" › "Number formats, scales
+# and granularity"): one step per group of 128, step = max|w| / 7 (1 for an all-zero
+# group), code = clamp(round(w / step), -8, 7) with halves to even (the rounding of both
+# pages' examples), one binary32 operation per step.  It is stored in the method's own
+# format as code + 8 with zero 8, so w_hat = (stored - zero) * scale16 is unchanged.
+# ---------------------------------------------------------------------------
+SYM_ZERO = 8
+SYM_TOP = 7
+
+
+def quantize_symmetric_ref(w: np.ndarray, group: int = GROUP):
+    """Symmetric 4-bit quantization of W [N, K] (binary32) in the canonical arrays.
+
+    Returns (packed uint8 [N, K/2], scales float16 [N, K/group], zeros uint8 [N, K/group],
+    all zeros 8).  A quotient that is NaN (a step that underflows to 0 on 0/0) clamps to
+    -8, and +-inf clamp to the ends, as the C fmin/fmax clamp does.
+    """
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    if w.ndim != 2:
+        raise ValueError("W must be 2-D [N, K]")
+    n, k = w.shape
+    if k % group or group % 2:
+        raise ValueError("K must be a multiple of the group size")
+    if not np.all(np.isfinite(w)):
+        raise ValueError("non-finite weight")
+    g = w.reshape(n, k // group, group)
+    amax = np.abs(g).max(axis=2)
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore", under="ignore"):
+        s = np.where(amax > 0, amax / np.float32(SYM_TOP), np.float32(1.0)).astype(np.float32)
+        t = g / s[:, :, None]
+        q = np.fmin(np.fmax(np.rint(t), np.float32(-SYM_TOP - 1)), np.float32(SYM_TOP))
+        s16 = s.astype(np.float16)
+    codes = (q.astype(np.int16) + SYM_ZERO).astype(np.uint8).reshape(n, k)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    zeros = np.full((n, k // group), SYM_ZERO, dtype=np.uint8)
+    return packed, s16, zeros
+
+
 def unpack_codes(packed: np.ndarray) -> np.ndarray:
     """Codes [N, K] from packed bytes [N, K/2]: low nibble = even index."""
     packed = np.asarray(packed, dtype=np.uint8)

@@ -500,3 +500,84 @@ def test_asymmetric_g128_step_and_error_against_symmetric():
     assert db > sym_db + 0.5
     assert 0.09 < rel < 0.1224
 
+
+# ---------------------------------------------------------------------------
+# Symmetric variant: page "Quantization" › "How it really works" (scale, round, clamp),
+# stored as code + 8 with zero 8
+# ---------------------------------------------------------------------------
+
+def brute_round_even(t: Fraction) -> int:
+    """Integer nearest to t; at an exact half the even one (search, no formula)."""
+    base = math.floor(t)
+    cands = [base - 1, base, base + 1, base + 2]
+    dist = [abs(Fraction(c) - t) for c in cands]
+    m = min(dist)
+    tied = [c for c, d in zip(cands, dist) if d == m]
+    return [c for c in tied if c % 2 == 0][0] if len(tied) > 1 else tied[0]
+
+
+def reference_symmetric_group(vals):
+    amax = max(abs(v) for v in vals)
+    s = exact_f32(Fraction(amax) / 7) if amax > 0 else 1.0
+    assert s > 0, "test grid avoids step underflow"
+    codes = []
+    for v in vals:
+        t = exact_f32(Fraction(v) / Fraction(s))
+        codes.append(min(max(brute_round_even(Fraction(t)), -8), 7) + 8)
+    return s, codes
+
+
+def _sym_check(rows):
+    w = np.array(rows, dtype=np.float32)
+    g = w.shape[1]
+    p, s16, z = oracle.quantize_symmetric_ref(w, group=g)
+    codes = oracle.unpack_codes(p)
+    assert np.all(z == 8)
+    for i, row in enumerate(rows):
+        s, want = reference_symmetric_group([float(np.float32(v)) for v in row])
+        assert list(codes[i]) == want, (row, list(codes[i]), want)
+        with np.errstate(over="ignore"):   # steps beyond binary16 range round to inf on both sides
+            assert s16[i, 0] == np.float16(s)
+
+
+def test_symmetric_brute_force_pairs_and_quads_with_ties():
+    grid = [0.0, 3.5, -3.5, 2.5, -0.5, 0.5, 7.0, -7.0, 1.5, 6.5, -6.5, 1e-30, 2.0 ** -140, 0.1]
+    _sym_check([[a, b] for a in grid for b in grid])
+    rng = np.random.default_rng(9)
+    quads = []
+    for _ in range(2000):
+        kind = rng.integers(3)
+        if kind == 0:      # multiples of 1/2 with the largest magnitude 7: exact half ties
+            v = rng.integers(-14, 15, 4) / 2.0
+            v[rng.integers(4)] = 7.0 * rng.choice([-1, 1])
+        elif kind == 1:
+            v = rng.standard_normal(4) * 10.0 ** rng.uniform(-30, 30)
+        else:
+            v = np.round(rng.standard_normal(4) * 8) / 8
+        quads.append([float(np.float32(x)) for x in v])
+    _sym_check(quads)
+
+
+def test_symmetric_invariants_and_page_table_row():
+    rng = np.random.default_rng(10)
+    w = (0.02 * rng.standard_normal((64, 1024))).astype(np.float32)
+    w[3, 5] = 0.7
+    w[7, :128] = 0.0
+    p, s16, z = oracle.quantize_symmetric_ref(w)
+    codes = oracle.unpack_codes(p).astype(np.int64)
+    g = w.astype(np.float64).reshape(64, 8, 128)
+    amax = np.abs(g).max(axis=2)
+    s32 = np.where(amax > 0, (amax.astype(np.float32) / np.float32(7)).astype(np.float64), 1.0)
+    q = codes.reshape(64, 8, 128) - 8
+    assert q.min() >= -7 and q.max() <= 7            # |w / step| <= 7: the clamp never acts
+    assert np.all(np.abs(q * s32[:, :, None] - g) <= s32[:, :, None] / 2 * (1 + 1e-6))
+    assert np.all(codes[w == 0.0] == 8)               # zero stays exactly representable
+    top = np.abs(g) == amax[:, :, None]
+    assert np.all(np.abs(q[top & (amax[:, :, None] > 0)]) == 7)
+    # the page's symmetric group-128 row on its own matrix, with the stored binary16 step
+    wp = synth.page_error_matrix()
+    p, s16, z = oracle.quantize_symmetric_ref(wp.astype(np.float32))
+    db, rel = quant_error.sqnr_db(wp, oracle.dequant_ref(p, s16, z))
+    row = [r for r in _page_error_table() if r[0] == "INT4 group 128"][0]
+    assert [f"{db:.1f}", f"{100 * rel:.2f}"] == row[2:4]
+
