@@ -16,7 +16,7 @@ import re
 
 __all__ = [
     "W4Error", "lib", "declared_symbols",
-    "w4_quantize", "w4_prepared_bytes", "w4_prepare", "w4_unprepare",
+    "w4_quantize", "w4_quantize_symmetric", "w4_prepared_bytes", "w4_prepare", "w4_unprepare",
     "w4_gemv", "w4_gemm_workspace_bytes", "w4_gemm",
     "w4_status_string", "w4_last_hip_error", "w4_format_version",
     "W4ChainGemv", "w4_chain_plan_bytes", "w4_chain_workspace_bytes", "w4_chain_plan",
@@ -63,6 +63,8 @@ def lib() -> ctypes.CDLL:
     i32 = ctypes.c_int
     L.w4_quantize.argtypes = [vp, i32, i64, i64, vp, vp, vp, vp, vp]
     L.w4_quantize.restype = i32
+    L.w4_quantize_symmetric.argtypes = [vp, i32, i64, i64, vp, vp, vp, vp, vp]
+    L.w4_quantize_symmetric.restype = i32
     L.w4_prepared_bytes.argtypes = [i64, i64]
     L.w4_prepared_bytes.restype = sz
     L.w4_prepare.argtypes = [vp, vp, vp, i64, i64, vp, sz, vp]
@@ -164,6 +166,15 @@ def w4_quantize(W, packed=None, scales=None, zeros=None, status=None):
     Returns (packed uint8 [N, K/2], scales float16 [N, K/128], zeros uint8 [N, K/128]).
     ``status`` may be an int32 tensor of one element; W4 status bits are OR-ed into it.
     """
+    return _quantize("w4_quantize", W, packed, scales, zeros, status)
+
+
+def w4_quantize_symmetric(W, packed=None, scales=None, zeros=None, status=None):
+    """Symmetric variant (step max|w|/7, halves to even), same arrays; every zero is 8."""
+    return _quantize("w4_quantize_symmetric", W, packed, scales, zeros, status)
+
+
+def _quantize(fn_name, W, packed, scales, zeros, status):
     import torch
     _require(W, (torch.float32, torch.bfloat16), None, "W")
     if W.dim() != 2:
@@ -185,8 +196,9 @@ def w4_quantize(W, packed=None, scales=None, zeros=None, status=None):
         _require(status, (torch.int32,), None, "status")
         st_ptr = _ptr(status)
     wt = W4_BF16 if W.dtype == torch.bfloat16 else W4_F32
-    _check(lib().w4_quantize(_ptr(W), wt, N, K, _ptr(packed), _ptr(scales), _ptr(zeros),
-                             st_ptr, _stream(W)), "w4_quantize")
+    fn = getattr(lib(), fn_name)
+    _check(fn(_ptr(W), wt, N, K, _ptr(packed), _ptr(scales), _ptr(zeros), st_ptr, _stream(W)),
+           fn_name)
     return packed, scales, zeros
 
 

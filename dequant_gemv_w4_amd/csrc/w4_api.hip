@@ -68,9 +68,9 @@ const char* w4_last_hip_error(void) { return g_last_hip_error.c_str(); }
 
 int w4_format_version(void) { return W4_FORMAT_VERSION; }
 
-w4_status w4_quantize(const void* W, w4_dtype wt, int64_t N, int64_t K, uint8_t* packed,
-                      uint16_t* scales_f16, uint8_t* zeros, uint32_t* d_status,
-                      hipStream_t stream) {
+static w4_status quantize_common(const void* W, w4_dtype wt, int64_t N, int64_t K,
+                                 uint8_t* packed, uint16_t* scales_f16, uint8_t* zeros,
+                                 uint32_t* d_status, bool symmetric, hipStream_t stream) {
     if (!W || !packed || !scales_f16 || !zeros) return W4_ERR_NULL;
     if (wt != W4_F32 && wt != W4_BF16) return W4_ERR_DTYPE;
     w4_status st = check_nk(N, K);
@@ -80,9 +80,21 @@ w4_status w4_quantize(const void* W, w4_dtype wt, int64_t N, int64_t K, uint8_t*
         return W4_ERR_ALIGN;
     st = check_arch();
     if (st != W4_OK) return st;
-    hipError_t e = w4::launch_quantize(W, wt == W4_BF16, N * (K / W4_GROUP), packed, scales_f16,
-                                       zeros, d_status, stream);
+    hipError_t e = w4::launch_quantize(W, wt == W4_BF16, symmetric, N * (K / W4_GROUP), packed,
+                                       scales_f16, zeros, d_status, stream);
     return e == hipSuccess ? W4_OK : hip_fail(e);
+}
+
+w4_status w4_quantize(const void* W, w4_dtype wt, int64_t N, int64_t K, uint8_t* packed,
+                      uint16_t* scales_f16, uint8_t* zeros, uint32_t* d_status,
+                      hipStream_t stream) {
+    return quantize_common(W, wt, N, K, packed, scales_f16, zeros, d_status, false, stream);
+}
+
+w4_status w4_quantize_symmetric(const void* W, w4_dtype wt, int64_t N, int64_t K,
+                                uint8_t* packed, uint16_t* scales_f16, uint8_t* zeros,
+                                uint32_t* d_status, hipStream_t stream) {
+    return quantize_common(W, wt, N, K, packed, scales_f16, zeros, d_status, true, stream);
 }
 
 size_t w4_prepared_bytes(int64_t N, int64_t K) {

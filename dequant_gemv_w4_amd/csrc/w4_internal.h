@@ -98,8 +98,9 @@ int chain_grid(int max_k);
 hipError_t launch_chain(const ChainHeader& h, const uint8_t* plan_dev, uint32_t* ws, hipStream_t s);
 
 // Launch wrappers (defined in the .hip files); return hipSuccess or the launch error.
-hipError_t launch_quantize(const void* W, bool bf16, int64_t n_groups, uint8_t* packed,
-                           uint16_t* scales, uint8_t* zeros, uint32_t* status, hipStream_t s);
+hipError_t launch_quantize(const void* W, bool bf16, bool symmetric, int64_t n_groups,
+                           uint8_t* packed, uint16_t* scales, uint8_t* zeros, uint32_t* status,
+                           hipStream_t s);
 hipError_t launch_prepare(const uint8_t* packed, const uint16_t* scales, const uint8_t* zeros,
                           int64_t n, int64_t k, uint8_t* prepared, hipStream_t s);
 hipError_t launch_unprepare(const uint8_t* prepared, int64_t n, int64_t k, uint8_t* packed,

@@ -6,6 +6,11 @@
 // for an empty range, binary32 arithmetic, Rust-style rounding of halves away
 // from zero, the even input index in the low nibble).
 //
+// Symmetric variant (page "Quantization" › "How it really works" › "The mechanics:
+// scale, round, clamp"): step = max|w| / 7 (1 for an all-zero group), code =
+// clamp(round(w / step), -8, 7) with halves to even (rintf), stored as code + 8 with
+// zero 8, so the products' (stored - zero) * scale16 holds unchanged.
+//
 // Work split: 32 lanes own one group (4 consecutive weights each, one 16-byte
 // load), a wave owns two groups, a 256-thread block eight.  The group's
 // minimum and maximum are a 32-lane butterfly; every lane then derives the
@@ -40,7 +45,7 @@ __device__ __forceinline__ void load4(const void* __restrict__ W, int64_t idx, f
     }
 }
 
-template <bool BF16>
+template <bool BF16, bool SYM>
 __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ W, int64_t n_groups,
                                                        uint16_t* __restrict__ packed16,
                                                        uint16_t* __restrict__ scales,
@@ -67,13 +72,26 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
         lo = fminf(lo, __shfl_xor(lo, d, 32));
         hi = fmaxf(hi, __shfl_xor(hi, d, 32));
     }
-    lo = fminf(lo, 0.0f);  // zero stays exactly representable
-    hi = fmaxf(hi, 0.0f);
-    const float s = (hi > lo) ? (hi - lo) / 15.0f : 1.0f;   // IEEE division
-    const float zc = clamp_code_keep_nan(roundf(-lo / s));  // roundf: halves away from zero
+    float s, zc;
     uint32_t c[4];
+    bool nonempty;
+    if constexpr (SYM) {
+        const float amax = fmaxf(fabsf(lo), fabsf(hi));
+        nonempty = amax > 0.0f;
+        s = nonempty ? amax / 7.0f : 1.0f;    // IEEE division
+        zc = 8.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) c[i] = to_code(roundf(v[i] / s) + zc);
+        for (int i = 0; i < 4; ++i)   // rintf: halves to even; a NaN quotient clamps to -8
+            c[i] = (uint32_t)(fminf(fmaxf(rintf(v[i] / s), -8.0f), 7.0f) + 8.0f);
+    } else {
+        lo = fminf(lo, 0.0f);  // zero stays exactly representable
+        hi = fmaxf(hi, 0.0f);
+        nonempty = hi > lo;
+        s = nonempty ? (hi - lo) / 15.0f : 1.0f;   // IEEE division
+        zc = clamp_code_keep_nan(roundf(-lo / s));  // roundf: halves away from zero
+#pragma unroll
+        for (int i = 0; i < 4; ++i) c[i] = to_code(roundf(v[i] / s) + zc);
+    }
 
     if (!valid) return;
     packed16[gi * (kGroup / 4) + lane] = (uint16_t)(c[0] | (c[1] << 4) | (c[2] << 8) | (c[3] << 12));
@@ -84,7 +102,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
         zeros[gi] = (uint8_t)to_code(zc);
         uint32_t flags = 0;
         if ((s16 & 0x7FFFu) == 0x7C00u) flags |= 2u;          // W4_STATUS_SCALE_OVERFLOW
-        if ((s16 & 0x7FFFu) == 0 && hi > lo) flags |= 4u;     // W4_STATUS_SCALE_ZERO
+        if ((s16 & 0x7FFFu) == 0 && nonempty) flags |= 4u;   // W4_STATUS_SCALE_ZERO
         if (flags && status) atomicOr(status, flags);
     }
 }
@@ -153,16 +171,15 @@ int64_t elementwise_blocks(int64_t work) {
 
 }  // namespace
 
-hipError_t launch_quantize(const void* W, bool bf16, int64_t n_groups, uint8_t* packed,
-                           uint16_t* scales, uint8_t* zeros, uint32_t* status, hipStream_t s) {
+hipError_t launch_quantize(const void* W, bool bf16, bool symmetric, int64_t n_groups,
+                           uint8_t* packed, uint16_t* scales, uint8_t* zeros, uint32_t* status,
+                           hipStream_t s) {
     const int64_t blocks = (n_groups + 7) / 8;
     uint16_t* p16 = reinterpret_cast<uint16_t*>(packed);
-    if (bf16)
-        hipLaunchKernelGGL(quantize_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, W,
-                           n_groups, p16, scales, zeros, status);
-    else
-        hipLaunchKernelGGL(quantize_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, W,
-                           n_groups, p16, scales, zeros, status);
+    auto kern = bf16 ? (symmetric ? quantize_kernel<true, true> : quantize_kernel<true, false>)
+                     : (symmetric ? quantize_kernel<false, true> : quantize_kernel<false, false>);
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, s, W, n_groups, p16, scales,
+                       zeros, status);
     return hipGetLastError();
 }
 

@@ -89,6 +89,20 @@ w4_status w4_quantize(const void* W, w4_dtype wt, int64_t N, int64_t K,
                       uint32_t* d_status, hipStream_t stream);
 
 /*
+ * w4_quantize_symmetric -- the symmetric variant (page "Quantization" › "How it
+ * really works" › "The mechanics: scale, round, clamp"): per group of 128 the step
+ * is max|w| / 7 (1 for an all-zero group), each code is round(w / step) with halves
+ * to even, clamped to [-8, 7]; one binary32 operation per step.  Written in the same
+ * canonical arrays as w4_quantize: stored code = code + 8, every zero = 8, scale =
+ * the step rounded to binary16 -- so w4_prepare, w4_gemv and w4_gemm take the result
+ * unchanged ((stored - zero) * scale16 is the dequantized weight).
+ * Arguments, alignment, errors and d_status bits as w4_quantize.
+ */
+w4_status w4_quantize_symmetric(const void* W, w4_dtype wt, int64_t N, int64_t K,
+                                uint8_t* packed, uint16_t* scales_f16, uint8_t* zeros,
+                                uint32_t* d_status, hipStream_t stream);
+
+/*
  * Kernel layout ("pre-shuffled" weights with interleaved scale and zero: page
  * "LLM Quantization Architecture in Depth" › "Kernels and memory layout: the
  * format is a contract"; the stage list's "Memory Layout" on the

@@ -70,9 +70,16 @@ def test_validation_errors_before_device_work():
     assert L.w4_gemv(_fake(), 4, 128, _fake(0x100008), 1, 1, _fake(), 0, s) == 3
     # destination too small
     assert L.w4_prepare(_fake(), _fake(), _fake(), 4, 128, _fake(), 10, s) == 9
+    # the symmetric quantizer validates exactly as w4_quantize
+    assert L.w4_quantize_symmetric(NULL, 0, 4, 128, _fake(), _fake(), _fake(), NULL, s) == 1
+    assert L.w4_quantize_symmetric(_fake(), 7, 4, 128, _fake(), _fake(), _fake(), NULL, s) == 4
+    assert L.w4_quantize_symmetric(_fake(), 0, 4, 100, _fake(), _fake(), _fake(), NULL, s) == 2
+    assert L.w4_quantize_symmetric(_fake(0x100004), 0, 4, 128, _fake(), _fake(), _fake(), NULL, s) == 3
 
 
 def test_python_layer_rejects_cpu_tensors():
     torch = pytest.importorskip("torch")
     with pytest.raises(ValueError):
         w4.w4_quantize(torch.zeros(4, 128))
+    with pytest.raises(ValueError):
+        w4.w4_quantize_symmetric(torch.zeros(4, 128))

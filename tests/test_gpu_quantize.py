@@ -141,3 +141,72 @@ def test_page_error_matrix_bit_exact_and_its_error():
     sym_db = [r[2] for r in quant_error.table(synth.page_error_matrix()) if r[0] == "INT4 group 128"][0]
     assert db > sym_db
 
+
+# ---- symmetric variant (page "Quantization" › "How it really works"): bit-exact codes,
+# scales and zeros, and the products of the unchanged GEMV/GEMM kernels on its output
+
+def _gpu_quant_sym(W):
+    status = torch.zeros(1, dtype=torch.int32, device=W.device)
+    p, s, z = w4.w4_quantize_symmetric(W, status=status)
+    torch.cuda.synchronize()
+    return quant_arrays_np(p, s, z), int(status.item())
+
+
+def test_symmetric_bit_exact_edges_and_page_matrix():
+    rng = np.random.default_rng(21)
+    rows = []
+    # exact half ties (largest magnitude 7 makes the step 1), zeros, one sign, subnormals
+    t = rng.integers(-14, 15, 128).astype(np.float32) / 2
+    t[0] = 7.0
+    rows.append(t)
+    rows.append(np.zeros(128, dtype=np.float32))
+    rows.append(np.abs(rng.standard_normal(128)).astype(np.float32))
+    rows.append(-np.abs(rng.standard_normal(128)).astype(np.float32))
+    rows.append((rng.standard_normal(128) * 1e-39).astype(np.float32))
+    rows.append(np.array([2.0 ** -149, 0.0, -(2.0 ** -148), 0.0] * 32, dtype=np.float32))
+    o = (0.02 * rng.standard_normal(128)).astype(np.float32)
+    o[9] = -3.0
+    rows.append(o)
+    w = np.stack([np.concatenate([r, (0.02 * rng.standard_normal(128)).astype(np.float32)])
+                  for r in rows])
+    gpu, st = _gpu_quant_sym(torch.from_numpy(w).to(DEV))
+    assert_quant_equal(gpu, oracle.quantize_symmetric_ref(w), "symmetric edge groups")
+    wp = synth.page_error_matrix().astype(np.float32)
+    gpu, st = _gpu_quant_sym(torch.from_numpy(wp).to(DEV))
+    assert st == 0
+    assert_quant_equal(gpu, oracle.quantize_symmetric_ref(wp), "symmetric page matrix")
+
+
+def test_symmetric_70b_rows_bit_exact_and_bf16_input():
+    W = synth.normal_weights(28672, 8192, synth.seed_for(3, "gate"), DEV)
+    rng = np.random.default_rng(22)
+    rows = np.unique(np.concatenate([[0, 28671], rng.choice(28672, 254, replace=False)]))
+    gpu, st = _gpu_quant_sym(W)
+    assert st == 0
+    ref = oracle.quantize_symmetric_ref(to_np32(W[torch.from_numpy(rows).to(DEV)]))
+    assert_quant_equal(tuple(a[rows] for a in gpu), ref, "symmetric 70B gate rows")
+    Wb = W[:256].to(torch.bfloat16)
+    gpu, st = _gpu_quant_sym(Wb)
+    assert_quant_equal(gpu, oracle.quantize_symmetric_ref(to_np32(Wb)), "symmetric bf16 W")
+
+
+def test_symmetric_weights_through_gemv_and_gemm():
+    from _util import assert_within
+    rng = np.random.default_rng(23)
+    n, k = 1000, 2048
+    w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
+    p, s, z = w4.w4_quantize_symmetric(torch.from_numpy(w).to(DEV))
+    prep = w4.w4_prepare(p, s, z)
+    rp, rs, rz = oracle.quantize_symmetric_ref(w)
+    for m in (1, 3, 8, 16):
+        x = torch.from_numpy(rng.standard_normal((m, k)).astype(np.float32)).to(torch.bfloat16)
+        x32 = to_np32(x)
+        y = to_np32(w4.w4_gemv(prep, n, k, x.to(DEV)))
+        assert_within(y, oracle.gemv_ref(rp, rs, rz, x32), oracle.tolerance_ref(rp, rs, rz, x32),
+                      f"symmetric GEMV M={m}")
+    X = torch.from_numpy(rng.standard_normal((130, k)).astype(np.float32)).to(torch.bfloat16)
+    x32 = to_np32(X)
+    Y = to_np32(w4.w4_gemm(prep, n, k, X.to(DEV)))
+    assert_within(Y, oracle.gemv_ref(rp, rs, rz, x32), oracle.tolerance_ref(rp, rs, rz, x32),
+                  "symmetric GEMM")
+
