@@ -245,7 +245,7 @@ def llama7b_layers(dev: str, layers: int = 6, reps: int = 5, fused: bool = False
             "tokens_per_s_equiv_32_layers": round(1e6 / (32 * us_layer), 1)}
 
 
-def prefill_gemm(prepared, dev: str, reps: int = 10, warmup: int = 3):
+def prefill_gemm(prepared, dev: str, reps: int = 20, warmup: int = 10):
     import torch
 
     import dequant_gemv_w4_amd as w4
