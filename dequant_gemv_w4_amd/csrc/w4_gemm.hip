@@ -57,9 +57,17 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint32_t a, uint32_t b, uint32_t c
     return __builtin_bit_cast(bf16x8_t, v);
 }
 
+__device__ __forceinline__ void load_lds16(const void* g, uint32_t lds_addr);
+
 // ---- pre-pass: S^T[g][m] = sum of x[m, 128g .. 128g+127] by the MFMA sequence of the GEMM
+// (the same A operands in the same MFMA steps, B = ones).  Each wave stages its 32 rows x
+// 128 inputs in LDS with loads of 4 rows x 256 contiguous bytes (chunk c of row r at slot
+// c ^ (r & 15)), then reads the A operands from there: one load per lane straight into
+// the MFMA lane order would touch 64 lines per instruction.  Rows past M repeat row M-1
+// (their sums are never used).
 __global__ __launch_bounds__(256) void xsum_kernel(const uint16_t* __restrict__ X, int M, int K,
                                                    float* __restrict__ St, int m_pad) {
+    __shared__ __attribute__((aligned(16))) uint8_t stage[4][32 * 256];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int Kg = K / kGroup;
@@ -68,16 +76,25 @@ __global__ __launch_bounds__(256) void xsum_kernel(const uint16_t* __restrict__ 
     if (tile >= n_mt * Kg) return;
     const int mt = tile % n_mt;
     const int g = tile / n_mt;
-    const int row = mt * 32 + (lane & 31);
+    const uint32_t base = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)stage[wave]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int r = 4 * i + (lane >> 4);
+        const int c = (lane & 15) ^ (r & 15);
+        const int row = min(mt * 32 + r, M - 1);
+        load_lds16(X + (int64_t)row * K + g * kGroup + 8 * c, base + i * 1024);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's rows have landed
+    asm volatile("" ::: "memory");
+    const int r = lane & 31;
     const int h = lane >> 5;
     const bf16x8_t ones = as_bf16x8(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
     f32x16_t acc;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (row < M)
-            v = *reinterpret_cast<const uint4*>(X + (int64_t)row * K + g * kGroup + 64 * h + 8 * s);
-        const bf16x8_t a = as_bf16x8(v.x, v.y, v.z, v.w);
+        const int c = 8 * h + s;
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&stage[wave][r * 256 + ((c ^ (r & 15)) * 16)]);
         if (s == 0) {
             const f32x16_t zero = {};
             acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, ones, zero, 0, 0, 0);
@@ -89,8 +106,8 @@ __global__ __launch_bounds__(256) void xsum_kernel(const uint16_t* __restrict__ 
     if ((lane & 31) == 0) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-            const int r = mt * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-            St[(int64_t)g * m_pad + r] = acc[v];
+            const int rr = mt * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+            St[(int64_t)g * m_pad + rr] = acc[v];
         }
     }
 }
