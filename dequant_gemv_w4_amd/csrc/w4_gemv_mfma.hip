@@ -16,8 +16,12 @@
 //     a workgroup owns 16*T consecutive rows (T tiles of 16), and partial sums
 //     of its waves are added through LDS in wave order (deterministic);
 //   * per group, lane l loads 16 bytes of row (tile + l % 16) -- the 32 codes
-//     at k = 32*(l/16) .. +31 of the group -- plus that row's scale/zero word,
-//     and 4 x 16 bytes of activation row m = l % 16 (zero for m >= M);
+//     at k = 32*(l/16) .. +31 of the group -- plus that row's scale/zero word;
+//     the wave brings x of the group (16 rows x 128 inputs, rows m >= M repeat
+//     row M-1) into its LDS stage with four loads of 4 rows x 256 contiguous
+//     bytes and reads lane l's 4 x 16 bytes of row l % 16 from there (loading
+//     them straight into the lane order touched 32 lines per instruction and
+//     left the address unit stalled three quarters of its busy time);
 //   * MFMA step s (s = 0..3) of a group: A = x rows (lane l supplies row l % 16,
 //     k = 32*(l/16) + 8s .. +7), B = codes of the tile's 16 rows, unpacked by
 //     v_and_or_b32 into the exact bf16 values 128+q (lane l supplies column
@@ -48,8 +52,11 @@ __device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_addr);
+constexpr int kXStageBytes = 16 * 256;   // x of one group: 16 rows x 128 inputs (bf16)
+
 // T: tiles of 16 rows per workgroup; CH: groups whose loads are issued together;
-// NB: load buffers (1, or 2 for loads one chunk ahead)
+// NB: load buffers (1: the x stages in LDS are single-buffered)
 template <int T, int CH, int NB, int MAXT>
 __global__ __launch_bounds__(MAXT) void gemv_mfma_kernel(const uint8_t* __restrict__ wq,
                                                          const uint32_t* __restrict__ sz,
@@ -57,7 +64,10 @@ __global__ __launch_bounds__(MAXT) void gemv_mfma_kernel(const uint8_t* __restri
                                                          void* __restrict__ yv, int y_bf16, int N,
                                                          int K, int M, int gpw) {
     constexpr int RW = 16 * T;
-    extern __shared__ float red[];  // [waves][RW][kRedStride]
+    // per wave CH x stages during the group loop; afterwards the same bytes hold the
+    // partial sums [waves][RW][kRedStride]
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    float* red = reinterpret_cast<float*>(smem);
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -79,8 +89,18 @@ __global__ __launch_bounds__(MAXT) void gemv_mfma_kernel(const uint8_t* __restri
         wrow[t] = wq + (int64_t)n * row_bytes + 16 * kb;
         szrow[t] = sz + (int64_t)(n >> 2) * Kg * 4 + (n & 3);
     }
-    // rows m >= M of the A operand repeat row M-1: their outputs are computed and dropped
-    const uint16_t* xrow = x + (int64_t)min(col, M - 1) * K + 32 * kb;
+    // x of a group reaches this wave's LDS stage with loads of 4 rows x 256 contiguous
+    // bytes (chunk c of row r at slot c ^ (r & 15)); rows m >= M repeat row M-1, their
+    // outputs are computed and dropped
+    const uint32_t xstage = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem + wave * CH * kXStageBytes);
+    const uint8_t* xstage_p = smem + wave * CH * kXStageBytes;
+    const uint16_t* xsrc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 4 * i + (lane >> 4);
+        xsrc[i] = x + (int64_t)min(r, M - 1) * K + 8 * ((lane & 15) ^ (r & 15));
+    }
 
     uint32_t nib_mask, bias_bits;
     asm volatile("s_mov_b32 %0, 0x000F000F" : "=s"(nib_mask));
@@ -94,24 +114,23 @@ __global__ __launch_bounds__(MAXT) void gemv_mfma_kernel(const uint8_t* __restri
 
     // NB buffers of CH groups: with two, the loads of the next chunk are in flight while
     // the current one is computed
+    static_assert(NB == 1, "x staging uses one buffer");
     u32x4_t wb[NB][CH][T];
     uint32_t sb[NB][CH][T];
-    u32x4_t xb[NB][CH][4];
     // loads of groups g .. g+CH-1, clamped to the wave's last group (the repeats are cache
-    // hits and contribute nothing)
+    // hits and contribute nothing); per group: codes, scale/zero words, then x (4 loads)
     auto issue = [&](int b, int g) {
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             const int gc = min(g + c, g1 - 1);
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                xb[b][c][s] = *reinterpret_cast<const u32x4_t*>(xrow + gc * 128 + 8 * s);
 #pragma unroll
             for (int t = 0; t < T; ++t) {
                 wb[b][c][t] = __builtin_nontemporal_load(
                     reinterpret_cast<const u32x4_t*>(wrow[t] + (int64_t)gc * 64));
                 sb[b][c][t] = szrow[t][gc * 4];
             }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) lds_dma16(xsrc[i] + gc * 128, xstage + c * kXStageBytes + i * 1024);
             __builtin_amdgcn_sched_barrier(0);  // keep the loads in group order
         }
     };
@@ -121,11 +140,22 @@ __global__ __launch_bounds__(MAXT) void gemv_mfma_kernel(const uint8_t* __restri
             // a group past the wave's range is computed with scale 0 (no branch, so
             // the compiler cannot move loads into a conditional block)
             const float keep = g + c < g1 ? 1.0f : 0.0f;
+            // x of group c has landed: later loads are those of groups c+1 .. CH-1
+            switch (CH - 1 - c) {
+                case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+                default: __builtin_amdgcn_s_waitcnt((((2 * T + 4) & 15) | (((2 * T + 4) >> 4) << 14)) | 0x70 | 0xF00); break;
+            }
+            asm volatile("" ::: "memory");
+            u32x4_t xb_c[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                xb_c[s] = *reinterpret_cast<const u32x4_t*>(
+                    xstage_p + c * kXStageBytes + col * 256 + (((4 * kb + s) ^ col) * 16));
             f32x4_t sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                as_bf16x8(xb[b][c][0]), as_bf16x8(ones), zero4, 0, 0, 0);
+                as_bf16x8(xb_c[0]), as_bf16x8(ones), zero4, 0, 0, 0);
 #pragma unroll
             for (int s = 1; s < 4; ++s)
-                sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xb[b][c][s]),
+                sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xb_c[s]),
                                                                as_bf16x8(ones), sacc, 0, 0, 0);
 #pragma unroll
             for (int t = 0; t < T; ++t) {
@@ -137,7 +167,7 @@ __global__ __launch_bounds__(MAXT) void gemv_mfma_kernel(const uint8_t* __restri
                                         ((w >> 4) & nib_mask) | bias_bits,
                                         ((w >> 8) & nib_mask) | bias_bits,
                                         ((w >> 12) & nib_mask) | bias_bits};
-                    p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xb[b][c][s]),
+                    p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xb_c[s]),
                                                                 as_bf16x8(bw), p, 0, 0, 0);
                 }
                 const uint32_t szw = sb[b][c][t];
@@ -151,23 +181,13 @@ __global__ __launch_bounds__(MAXT) void gemv_mfma_kernel(const uint8_t* __restri
         }
     };
 
-    if (g0 >= g1) {
-        // no groups for this wave (the host sizes the grid so that this does not happen)
-    } else if constexpr (NB == 1) {
-        for (int g = g0; g < g1; g += CH) {
-            issue(0, g);
-            compute(0, g);
-        }
-    } else {
-        issue(0, g0);
-        for (int g = g0; g < g1; g += 2 * CH) {
-            issue(1, g + CH);
-            compute(0, g);
-            issue(0, g + 2 * CH);
-            compute(1, g + CH);
-        }
+    // (a wave without groups skips the loop; the host sizes the grid so that none is)
+    for (int g = g0; g < g1; g += CH) {
+        issue(0, g);
+        compute(0, g);
     }
 
+    __syncthreads();   // every wave is done with its x stages: the LDS now takes the sums
     // partial sums of this wave: lane holds column n = col, rows m = 4*kb + v
 #pragma unroll
     for (int t = 0; t < T; ++t)
@@ -416,7 +436,18 @@ hipError_t launch_t(const uint8_t* wq, const uint32_t* sz, const uint16_t* x, vo
                     int n, int k, int m, int gpw, int waves, hipStream_t s) {
     const dim3 grid((unsigned)((n + 16 * T - 1) / (16 * T)));
     const dim3 block((unsigned)(64 * waves));
-    const size_t shmem = (size_t)waves * 16 * T * kRedStride * sizeof(float);
+    const size_t red_bytes = (size_t)waves * 16 * T * kRedStride * sizeof(float);
+    const size_t x_bytes = (size_t)waves * CH * kXStageBytes;
+    const size_t shmem = red_bytes > x_bytes ? red_bytes : x_bytes;
+    if (shmem > 65536) {
+        static std::atomic<int> raised{0};
+        if (!raised.load(std::memory_order_relaxed)) {
+            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_mfma_kernel<T, CH, NB, MAXT>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+            if (e != hipSuccess) return e;
+            raised.store(1, std::memory_order_relaxed);
+        }
+    }
     hipLaunchKernelGGL((gemv_mfma_kernel<T, CH, NB, MAXT>), grid, block, shmem, s, wq, sz, x, y, y_bf16,
                        n, k, m, gpw);
     return hipGetLastError();
@@ -489,34 +520,21 @@ hipError_t launch_gemv_mfma(const uint8_t* prepared, int64_t n, int64_t k, const
     if (waves < 1) waves = 1;
     const int gpw = (kg + waves - 1) / waves;
     waves = (kg + gpw - 1) / gpw;
-    int t = forced_t;
-    if (t != 1 && t != 2 && t != 4) t = 2;
+    // tiles of 16 rows per workgroup (1 or 2) and groups per load batch (1 or 2)
+    const int t = forced_t == 1 ? 1 : 2;
+    const int ch = chunk == 1 ? 1 : 2;
     const uint8_t* wq = prepared;
     const uint32_t* sz = reinterpret_cast<const uint32_t*>(prepared + sz_offset(n, k));
     const int yb = y_bf16 ? 1 : 0;
     const int N = (int)n, K = (int)k, M = (int)m;
-    static const int nbuf = env_int("W4A16_MFMA_NB", 1);
-    // 1024-thread groups have 128 VGPRs per lane: one double-buffered group, or two
-    // single-buffered groups, of up to two tiles
-    int ch = chunk, nb = nbuf == 1 ? 1 : 2;
-    if (waves > 8) {
-        if (t == 4) t = 2;
-        if (nb == 2) ch = 1;
-        else if (ch > 2) ch = 2;
-    }
-#define W4_MFMA_CASE(TV, CV, NV)                                                                  \
-    if (t == TV && ch == CV && nb == NV)                                                          \
-        return waves <= 8 ? launch_t<TV, CV, NV, 512>(wq, sz, x, y, yb, N, K, M, gpw, waves, s)   \
-                          : launch_t<TV, CV, NV, 1024>(wq, sz, x, y, yb, N, K, M, gpw, waves, s);
-    W4_MFMA_CASE(1, 1, 1) W4_MFMA_CASE(1, 2, 1) W4_MFMA_CASE(2, 1, 1) W4_MFMA_CASE(2, 2, 1)
-    W4_MFMA_CASE(1, 1, 2) W4_MFMA_CASE(2, 1, 2)
-#undef W4_MFMA_CASE
-    if (t == 1 && ch == 4 && nb == 1) return launch_t<1, 4, 1, 512>(wq, sz, x, y, yb, N, K, M, gpw, waves, s);
-    if (t == 1 && ch == 2 && nb == 2) return launch_t<1, 2, 2, 512>(wq, sz, x, y, yb, N, K, M, gpw, waves, s);
-    if (t == 2 && ch == 2 && nb == 2) return launch_t<2, 2, 2, 512>(wq, sz, x, y, yb, N, K, M, gpw, waves, s);
-    if (t == 4 && ch == 1 && nb == 1) return launch_t<4, 1, 1, 512>(wq, sz, x, y, yb, N, K, M, gpw, waves, s);
-    if (t == 4 && ch == 1 && nb == 2) return launch_t<4, 1, 2, 512>(wq, sz, x, y, yb, N, K, M, gpw, waves, s);
-    return launch_t<2, 1, 2, 1024>(wq, sz, x, y, yb, N, K, M, gpw, waves, s);
+    if (t == 1 && ch == 1) return waves <= 8 ? launch_t<1, 1, 1, 512>(wq, sz, x, y, yb, N, K, M, gpw, waves, s)
+                                             : launch_t<1, 1, 1, 1024>(wq, sz, x, y, yb, N, K, M, gpw, waves, s);
+    if (t == 1) return waves <= 8 ? launch_t<1, 2, 1, 512>(wq, sz, x, y, yb, N, K, M, gpw, waves, s)
+                                  : launch_t<1, 2, 1, 1024>(wq, sz, x, y, yb, N, K, M, gpw, waves, s);
+    if (ch == 1) return waves <= 8 ? launch_t<2, 1, 1, 512>(wq, sz, x, y, yb, N, K, M, gpw, waves, s)
+                                   : launch_t<2, 1, 1, 1024>(wq, sz, x, y, yb, N, K, M, gpw, waves, s);
+    return waves <= 8 ? launch_t<2, 2, 1, 512>(wq, sz, x, y, yb, N, K, M, gpw, waves, s)
+                      : launch_t<2, 2, 1, 1024>(wq, sz, x, y, yb, N, K, M, gpw, waves, s);
 }
 
 }  // namespace w4
