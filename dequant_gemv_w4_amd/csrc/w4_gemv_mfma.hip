@@ -214,7 +214,9 @@ __global__ __launch_bounds__(MAXT) void gemv_mfma_kernel(const uint8_t* __restri
 
 // Variant for K <= 8192 (at most eight groups per wave, at most eight waves).
 //   * Each wave keeps the A operands of its groups (x, four MFMA steps per group) and their
-//     group sums in registers, then walks all rows of the workgroup in steps of 16.
+//     group sums in registers, then walks all rows of the workgroup in steps of 16.  The A
+//     operands arrive through the wave's ring before the weights do, in two rounds of four
+//     groups, with loads of 4 rows x 256 contiguous bytes.
 //   * Weights and scale/zero words go straight from global memory into a ring in LDS that
 //     belongs to the wave (global_load_lds: lane l's bytes land at slot + 16 l, and lane l
 //     reads them back), two row steps ahead, so the bytes in flight do not take registers.
@@ -346,16 +348,36 @@ __global__ __launch_bounds__(512) void gemv_mfma_xr_kernel(const uint8_t* __rest
 #pragma unroll
         for (int d = 4; d < 8; ++d) code_load(d);
     };
-    issue_step(0);
-
-    // ---- x of this wave's groups (A operands) and their sums, once per workgroup
+    // ---- x of this wave's groups (A operands) and their sums, once per workgroup.  x goes
+    // through the (still empty) ring in two rounds of four groups, with loads of 4 rows x 256
+    // contiguous bytes (chunk c of row r at slot c ^ (r & 15)); loading it straight into the
+    // MFMA lane order made each load touch 32 lines
     u32x4_t xa[kXrGroups][4];
-    const uint16_t* xrow = x + (int64_t)min(col, M - 1) * K + 32 * kb;
 #pragma unroll
-    for (int gi = 0; gi < kXrGroups; ++gi)
+    for (int half = 0; half < 2; ++half) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-            xa[gi][s] = *reinterpret_cast<const u32x4_t*>(xrow + (g0 + min(gi, ng - 1)) * 128 + 8 * s);
+        for (int q = 0; q < 4; ++q) {
+            const int gc = g0 + min(4 * half + q, ng - 1);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * i + (lane >> 4);
+                const uint16_t* src = x + (int64_t)min(r, M - 1) * K + gc * 128 + 8 * ((lane & 15) ^ (r & 15));
+                lds_dma16(src, ring + q * 4096 + i * 1024);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(vm_imm(0));
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                xa[4 * half + q][s] = *reinterpret_cast<const u32x4_t*>(
+                    ring_p + q * 4096 + col * 256 + (((4 * kb + s) ^ col) * 16));
+        // the reads have returned before the next loads overwrite the ring
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+        asm volatile("" ::: "memory");
+    }
+    issue_step(0);
     f32x4_t sx[kXrGroups];
 #pragma unroll
     for (int gi = 0; gi < kXrGroups; ++gi) {
@@ -502,16 +524,18 @@ static hipError_t launch_xr(const uint8_t* wq, const uint32_t* sz, const uint16_
     return hipGetLastError();
 }
 
+bool gemv_ring_takes(int64_t n, int64_t k) {
+    static const int use_xr = env_int("W4A16_GEMV_XR", 1);
+    if (!use_xr || k / kGroup > kXrGroups * 8) return false;
+    return use_xr == 2 || xr_rows((int)n) >= 48;
+}
+
 hipError_t launch_gemv_mfma(const uint8_t* prepared, int64_t n, int64_t k, const uint16_t* x,
                             int64_t m, void* y, bool y_bf16, hipStream_t s) {
     const int kg = (int)(k / kGroup);
-    static const int use_xr = env_int("W4A16_GEMV_XR", 1);
-    if (use_xr && kg <= kXrGroups * 8) {
-        const int R = xr_rows((int)n);
-        if (R >= 48 || use_xr == 2)
-            return launch_xr(prepared, reinterpret_cast<const uint32_t*>(prepared + sz_offset(n, k)),
-                             x, y, y_bf16 ? 1 : 0, (int)n, (int)k, (int)m, R, s);
-    }
+    if (gemv_ring_takes(n, k))
+        return launch_xr(prepared, reinterpret_cast<const uint32_t*>(prepared + sz_offset(n, k)),
+                         x, y, y_bf16 ? 1 : 0, (int)n, (int)k, (int)m, xr_rows((int)n), s);
     static const int per_wave = env_int("W4A16_MFMA_GPW", 8);
     static const int forced_t = env_int("W4A16_MFMA_TILES", 0);
     static const int chunk = env_int("W4A16_MFMA_CHUNK", 2);

@@ -109,6 +109,10 @@ hipError_t launch_gemv(const uint8_t* prepared, int64_t n, int64_t k, const void
                        int64_t m, void* y, bool y_bf16, hipStream_t s);
 hipError_t launch_gemv_mfma(const uint8_t* prepared, int64_t n, int64_t k, const uint16_t* x,
                             int64_t m, void* y, bool y_bf16, hipStream_t s);
+// Whether launch_gemv_mfma runs the shape on the ring kernel (x held in registers, weights
+// streamed through a per-wave LDS ring): K of at most 64 groups and at least 48 rows per
+// workgroup when one workgroup runs per compute unit.
+bool gemv_ring_takes(int64_t n, int64_t k);
 size_t gemm_workspace(int64_t m, int64_t k);
 hipError_t launch_gemm(const uint8_t* prepared, int64_t n, int64_t k, const void* X, int64_t m,
                        void* Y, bool y_bf16, void* workspace, hipStream_t s);

@@ -153,7 +153,8 @@ def test_deterministic_repeat():
 # ---- batched rows on the ring kernel (K <= 8192 and enough rows per workgroup): ragged
 # group counts (K = 1152: a wave with four of its eight groups), ragged N, several M
 
-@pytest.mark.parametrize("n,k,m", [(20000, 1152, 3), (12300, 1152, 16), (12289, 4096, 5)])
+@pytest.mark.parametrize("n,k,m", [(20000, 1152, 3), (12300, 1152, 4), (12300, 1152, 16),
+                                   (12289, 4096, 5)])
 def test_batched_ring_shapes_full(n, k, m):
     rng = np.random.default_rng(n + k + m)
     w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
@@ -174,7 +175,7 @@ def test_batched_ring_sampled_rows_k8192():
     rows = np.unique(np.concatenate([[0, 15, 16, n - 1], rng.choice(n, 256, replace=False)]))
     p, s, z = oracle.quantize_ref(to_np32(W[torch.from_numpy(rows).to(DEV)]))
     x32 = to_np32(x16)
-    for mm in (3, 8, 16):
+    for mm in (3, 4, 8, 16):
         y = to_np32(_run(prep, n, k, x16[:mm].contiguous()))
         assert_within(y[:, rows], oracle.gemv_ref(p, s, z, x32[:mm]),
                       oracle.tolerance_ref(p, s, z, x32[:mm]), f"ring sampled M={mm}")
