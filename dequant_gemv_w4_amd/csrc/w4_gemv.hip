@@ -417,16 +417,16 @@ hipError_t dispatch(bool x_f32, int spt, int mt, const GemvArgs& a, dim3 block, 
 hipError_t launch_gemv(const uint8_t* prepared, int64_t n, int64_t k, const void* x, bool x_f32,
                        int64_t m, void* y, bool y_bf16, hipStream_t s) {
     // bf16 rows: the matrix-core kernels read the weights once for all rows.  The dot2
-    // kernel below is faster (measured on MI355X at the 70B shapes) at two rows everywhere,
-    // at three rows while it needs a single pass over the weights (K <= 16384) and N is at
-    // most 16384 (qkv 14.4 against 15.4 us, o 12.7 against 14.4 us), and at four rows on
-    // such shapes unless the matrix-core ring kernel takes them (o 13.8 against 14.5 us
-    // stays here, qkv 15.5 against 16.3 us goes to the ring).  gate_up and down stay on the
-    // matrix cores.
+    // kernel below does M times the vector work per weight; it stays faster (measured on
+    // MI355X at the 70B shapes) at one row, at two rows while it needs a single pass over
+    // the weights (K <= 16384; down 8192x28672 at M = 2: 36.4 us here against 26.0 us on the
+    // matrix cores), and at three rows on shapes with K and N <= 16384 that the ring kernel
+    // takes (qkv 10240x8192: 14.4 against 15.3 us; o 8192x8192 streams faster, 11.2 against
+    // 12.2 us).
     static const int use_mfma = env_int("W4A16_GEMV_MFMA", 1);
-    const bool one_pass = k <= 16384 && n <= 16384;
-    const bool dot2_wins =
-        m <= 2 || (one_pass && (m == 3 || (m == 4 && !gemv_ring_takes(n, k))));
+    const bool one_pass = k <= 16384;
+    const bool dot2_wins = m == 1 || (m == 2 && one_pass) ||
+                           (m == 3 && one_pass && n <= 16384 && gemv_ring_takes(n, k));
     if (!x_f32 && !dot2_wins && use_mfma)
         return launch_gemv_mfma(prepared, n, k, static_cast<const uint16_t*>(x), m, y, y_bf16, s);
     const int S = (int)(k / 32);

@@ -1,6 +1,5 @@
 // Fused dequantizing product for a few activation rows (bf16 x, up to 16 rows; w4_gemv
-// sends 3 <= M <= 16 here)
-// on the matrix cores.
+// sends most shapes with 2 <= M <= 16 here) on the matrix cores.
 //
 // The same group term as the one-row kernel, y[m, n] = sum_g scale16[n, g] *
 // (sum_{k in g} q[n, k] x[m, k] - zero[n, g] * sum_{k in g} x[m, k]) (page
@@ -15,13 +14,17 @@
 //   * the waves of a workgroup split K: wave w takes groups [w*gpw, (w+1)*gpw);
 //     a workgroup owns 16*T consecutive rows (T tiles of 16), and partial sums
 //     of its waves are added through LDS in wave order (deterministic);
-//   * per group, lane l loads 16 bytes of row (tile + l % 16) -- the 32 codes
-//     at k = 32*(l/16) .. +31 of the group -- plus that row's scale/zero word;
-//     the wave brings x of the group (16 rows x 128 inputs, rows m >= M repeat
-//     row M-1) into its LDS stage with four loads of 4 rows x 256 contiguous
-//     bytes and reads lane l's 4 x 16 bytes of row l % 16 from there (loading
-//     them straight into the lane order touched 32 lines per instruction and
-//     left the address unit stalled three quarters of its busy time);
+//   * a wave works through its groups a pair at a time.  The codes of a pair
+//     reach the wave's LDS with loads of 8 rows x 128 contiguous bytes (eight
+//     full lines; a load in the MFMA lane order, 16 rows x 64 bytes, touches
+//     sixteen half lines), x of each group (16 rows x 128 inputs) with loads
+//     of 4 rows x 256 contiguous bytes, and the scale/zero words go straight
+//     to registers.  XOR swizzles of the 16-byte chunks let each lane read
+//     its MFMA operands back with no bank conflicts.  The loads of the next
+//     pair are issued as soon as the current pair is read out of LDS, so they
+//     are in flight while the current pair is computed.  With the codes
+//     loaded straight into the lane order and no overlap, the 70B down shape
+//     (8192 x 28672) took 40-45 us per call at M = 4..16, now 27-38 us;
 //   * MFMA step s (s = 0..3) of a group: A = x rows (lane l supplies row l % 16,
 //     k = 32*(l/16) + 8s .. +7), B = codes of the tile's 16 rows, unpacked by
 //     v_and_or_b32 into the exact bf16 values 128+q (lane l supplies column
@@ -32,6 +35,7 @@
 //   * the 16x16 result sits in lane l as column n = l % 16, rows
 //     m = 4*(l/16) + v (v = 0..3): one scale/zero word per lane and tile.
 #include <atomic>
+#include <type_traits>
 #include <cstdlib>
 
 #include "w4_internal.h"
@@ -55,17 +59,18 @@ __device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
 __device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_addr);
 constexpr int kXStageBytes = 16 * 256;   // x of one group: 16 rows x 128 inputs (bf16)
 
-// T: tiles of 16 rows per workgroup; CH: groups whose loads are issued together;
-// NB: load buffers (1: the x stages in LDS are single-buffered)
-template <int T, int CH, int NB, int MAXT>
-__global__ __launch_bounds__(MAXT) void gemv_mfma_kernel(const uint8_t* __restrict__ wq,
+// T: tiles of 16 rows per workgroup; CH: groups whose loads are issued together (a pair)
+template <int T, int CH>
+__global__ __launch_bounds__(512) void gemv_mfma_kernel(const uint8_t* __restrict__ wq,
                                                          const uint32_t* __restrict__ sz,
                                                          const uint16_t* __restrict__ x,
                                                          void* __restrict__ yv, int y_bf16, int N,
                                                          int K, int M, int gpw) {
+    static_assert(CH == 2, "codes are staged a group pair at a time");
     constexpr int RW = 16 * T;
-    // per wave CH x stages during the group loop; afterwards the same bytes hold the
-    // partial sums [waves][RW][kRedStride]
+    constexpr int kWaveBytes = CH * kXStageBytes + 2 * T * 1024;
+    // per wave CH x stages and 2T code blocks during the group loop; afterwards the same
+    // bytes hold the partial sums [waves][RW][kRedStride]
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     float* red = reinterpret_cast<float*>(smem);
 
@@ -80,21 +85,40 @@ __global__ __launch_bounds__(MAXT) void gemv_mfma_kernel(const uint8_t* __restri
     const int g1 = min(Kg, g0 + gpw);
     const int64_t row_bytes = K >> 1;
 
-    // this lane's weight row in each tile; rows past N repeat row N-1 (never stored)
-    const uint8_t* wrow[T];
+    const uint32_t xstage = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem + wave * kWaveBytes);
+    const uint32_t cstage = xstage + CH * kXStageBytes;
+    const uint8_t* xstage_p = smem + wave * kWaveBytes;
+    const uint8_t* cstage_p = xstage_p + CH * kXStageBytes;
+
+    // Codes of a group pair reach LDS as 2T loads of 8 rows x 128 contiguous bytes (eight
+    // full lines).  In the load for rows 8d .. 8d+7 of tile t, lane l takes row 8d + (l >> 3),
+    // group h = ((l >> 2) & 1) ^ d of the pair and 16-byte piece p = (l & 3) ^ (l >> 4), so
+    // that the reads in MFMA lane order below hit 16 distinct bank quads per 16 lanes.
+    // Rows past N repeat row N-1 (never stored).
+    const uint8_t* csrc[T][2];
+    int chalf[2];
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+        chalf[d] = ((lane >> 2) & 1) ^ d;
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            const int n = min(r0 + 16 * t + 8 * d + (lane >> 3), N - 1);
+            csrc[t][d] = wq + (int64_t)n * row_bytes + 16 * ((lane & 3) ^ (lane >> 4));
+        }
+    }
+    // scale/zero word of this lane's row (column col of the MFMA tile) in each tile
     const uint32_t* szrow[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
         const int n = min(r0 + 16 * t + col, N - 1);
-        wrow[t] = wq + (int64_t)n * row_bytes + 16 * kb;
         szrow[t] = sz + (int64_t)(n >> 2) * Kg * 4 + (n & 3);
     }
-    // x of a group reaches this wave's LDS stage with loads of 4 rows x 256 contiguous
-    // bytes (chunk c of row r at slot c ^ (r & 15)); rows m >= M repeat row M-1, their
-    // outputs are computed and dropped
-    const uint32_t xstage = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem + wave * CH * kXStageBytes);
-    const uint8_t* xstage_p = smem + wave * CH * kXStageBytes;
+    // x of a group reaches the x stage with loads of 4 rows x 256 contiguous bytes (chunk c
+    // of row r at slot c ^ (r & 15)); rows m >= M repeat row M-1.  Only the first ceil(M/4)
+    // quads of rows are loaded: MFMA rows past them read stale stage bytes and give only
+    // outputs m >= M, which are dropped.
+    const int xquads = (M + 3) >> 2;
     const uint16_t* xsrc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -112,62 +136,73 @@ __global__ __launch_bounds__(MAXT) void gemv_mfma_kernel(const uint8_t* __restri
 #pragma unroll
     for (int t = 0; t < T; ++t) acc[t] = zero4;
 
-    // NB buffers of CH groups: with two, the loads of the next chunk are in flight while
-    // the current one is computed
-    static_assert(NB == 1, "x staging uses one buffer");
-    u32x4_t wb[NB][CH][T];
-    uint32_t sb[NB][CH][T];
-    // loads of groups g .. g+CH-1, clamped to the wave's last group (the repeats are cache
-    // hits and contribute nothing); per group: codes, scale/zero words, then x (4 loads)
-    auto issue = [&](int b, int g) {
+    uint32_t sb[2][CH][T];
+    // loads of the pair g, g+1 (a group past the wave's range repeats its last group: a cache
+    // hit that contributes nothing): codes, scale/zero words, x
+    auto issue = [&](auto bc, int g) {
+        constexpr int b = decltype(bc)::value;
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int d = 0; d < 2; ++d)
+                lds_dma16(csrc[t][d] + (int64_t)min(g + chalf[d], g1 - 1) * 64,
+                          cstage + (2 * t + d) * 1024);
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             const int gc = min(g + c, g1 - 1);
 #pragma unroll
-            for (int t = 0; t < T; ++t) {
-                wb[b][c][t] = __builtin_nontemporal_load(
-                    reinterpret_cast<const u32x4_t*>(wrow[t] + (int64_t)gc * 64));
-                sb[b][c][t] = szrow[t][gc * 4];
-            }
+            for (int t = 0; t < T; ++t) sb[b][c][t] = szrow[t][gc * 4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) lds_dma16(xsrc[i] + gc * 128, xstage + c * kXStageBytes + i * 1024);
-            __builtin_amdgcn_sched_barrier(0);  // keep the loads in group order
+            for (int i = 0; i < 4; ++i)
+                if (i < xquads) lds_dma16(xsrc[i] + gc * 128, xstage + c * kXStageBytes + i * 1024);
         }
+        __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the compute
     };
-    auto compute = [&](int b, int g) {
+    auto step = [&](auto bc, int g) {
+        constexpr int b = decltype(bc)::value;
+        // every load of this pair has landed (the next pair's are not issued yet)
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        asm volatile("" ::: "memory");
+        u32x4_t xb[CH][4];
+        u32x4_t wb[CH][T];
 #pragma unroll
-        for (int c = 0; c < CH; ++c) {
-            // a group past the wave's range is computed with scale 0 (no branch, so
-            // the compiler cannot move loads into a conditional block)
-            const float keep = g + c < g1 ? 1.0f : 0.0f;
-            // x of group c has landed: later loads are those of groups c+1 .. CH-1
-            switch (CH - 1 - c) {
-                case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-                default: __builtin_amdgcn_s_waitcnt((((2 * T + 4) & 15) | (((2 * T + 4) >> 4) << 14)) | 0x70 | 0xF00); break;
-            }
-            asm volatile("" ::: "memory");
-            u32x4_t xb_c[4];
+        for (int c = 0; c < CH; ++c)
 #pragma unroll
             for (int s = 0; s < 4; ++s)
-                xb_c[s] = *reinterpret_cast<const u32x4_t*>(
+                xb[c][s] = *reinterpret_cast<const u32x4_t*>(
                     xstage_p + c * kXStageBytes + col * 256 + (((4 * kb + s) ^ col) * 16));
+        const int cd = col >> 3, cr = col & 7;
+#pragma unroll
+        for (int c = 0; c < CH; ++c)
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+                wb[c][t] = *reinterpret_cast<const u32x4_t*>(
+                    cstage_p + (2 * t + cd) * 1024 + 16 * (8 * cr + 4 * (c ^ cd) + (kb ^ (cr >> 1))));
+        // the stages are read out before the next pair lands in them
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        asm volatile("" ::: "memory");
+        if (g + CH < g1) issue(std::integral_constant<int, b ^ 1>{}, g + CH);
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            // a group past the wave's range is computed with scale 0 (no branch)
+            const float keep = g + c < g1 ? 1.0f : 0.0f;
             f32x4_t sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                as_bf16x8(xb_c[0]), as_bf16x8(ones), zero4, 0, 0, 0);
+                as_bf16x8(xb[c][0]), as_bf16x8(ones), zero4, 0, 0, 0);
 #pragma unroll
             for (int s = 1; s < 4; ++s)
-                sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xb_c[s]),
+                sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xb[c][s]),
                                                                as_bf16x8(ones), sacc, 0, 0, 0);
 #pragma unroll
             for (int t = 0; t < T; ++t) {
                 f32x4_t p = zero4;
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
-                    const uint32_t w = wb[b][c][t][s];
+                    const uint32_t w = wb[c][t][s];
                     const u32x4_t bw = {(w & nib_mask) | bias_bits,
                                         ((w >> 4) & nib_mask) | bias_bits,
                                         ((w >> 8) & nib_mask) | bias_bits,
                                         ((w >> 12) & nib_mask) | bias_bits};
-                    p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xb_c[s]),
+                    p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xb[c][s]),
                                                                 as_bf16x8(bw), p, 0, 0, 0);
                 }
                 const uint32_t szw = sb[b][c][t];
@@ -177,17 +212,21 @@ __global__ __launch_bounds__(MAXT) void gemv_mfma_kernel(const uint8_t* __restri
 #pragma unroll
                 for (int v = 0; v < 4; ++v) acc[t][v] = fmaf(sc, fmaf(-zb, sacc[v], p[v]), acc[t][v]);
             }
-            __builtin_amdgcn_sched_barrier(0);
         }
+        __builtin_amdgcn_sched_barrier(0);
     };
 
     // (a wave without groups skips the loop; the host sizes the grid so that none is)
-    for (int g = g0; g < g1; g += CH) {
-        issue(0, g);
-        compute(0, g);
+    if (g0 < g1) {
+        issue(std::integral_constant<int, 0>{}, g0);
+        for (int g = g0; g < g1; g += 2 * CH) {
+            step(std::integral_constant<int, 0>{}, g);
+            if (g + CH >= g1) break;
+            step(std::integral_constant<int, 1>{}, g + CH);
+        }
     }
 
-    __syncthreads();   // every wave is done with its x stages: the LDS now takes the sums
+    __syncthreads();   // every wave is done with its stages: the LDS now takes the sums
     // partial sums of this wave: lane holds column n = col, rows m = 4*kb + v
 #pragma unroll
     for (int t = 0; t < T; ++t)
@@ -453,33 +492,34 @@ int env_int(const char* name, int dflt) {
     return e ? atoi(e) : dflt;
 }
 
-template <int T, int CH, int NB, int MAXT>
+template <int T>
 hipError_t launch_t(const uint8_t* wq, const uint32_t* sz, const uint16_t* x, void* y, int y_bf16,
                     int n, int k, int m, int gpw, int waves, hipStream_t s) {
     const dim3 grid((unsigned)((n + 16 * T - 1) / (16 * T)));
     const dim3 block((unsigned)(64 * waves));
     const size_t red_bytes = (size_t)waves * 16 * T * kRedStride * sizeof(float);
-    const size_t x_bytes = (size_t)waves * CH * kXStageBytes;
-    const size_t shmem = red_bytes > x_bytes ? red_bytes : x_bytes;
+    const size_t stage_bytes = (size_t)waves * (2 * kXStageBytes + 2 * T * 1024);
+    const size_t shmem = red_bytes > stage_bytes ? red_bytes : stage_bytes;
     if (shmem > 65536) {
         static std::atomic<int> raised{0};
         if (!raised.load(std::memory_order_relaxed)) {
-            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_mfma_kernel<T, CH, NB, MAXT>),
+            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_mfma_kernel<T, 2>),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
             if (e != hipSuccess) return e;
             raised.store(1, std::memory_order_relaxed);
         }
     }
-    hipLaunchKernelGGL((gemv_mfma_kernel<T, CH, NB, MAXT>), grid, block, shmem, s, wq, sz, x, y, y_bf16,
+    hipLaunchKernelGGL((gemv_mfma_kernel<T, 2>), grid, block, shmem, s, wq, sz, x, y, y_bf16,
                        n, k, m, gpw);
     return hipGetLastError();
 }
 
 }  // namespace
 
-// Waves per workgroup: about eight groups of K each, at most 16 waves.  Two tiles (32
-// rows) per workgroup, two groups per load batch, one buffer: the fastest of the
-// settings measured on MI355X at the 70B shapes for M = 2, 8 and 16.
+// Streaming kernel: waves per workgroup about eight groups of K each, at most eight
+// (12 KB of LDS stages per wave; on the 70B down shape eight waves of 28 groups ran faster
+// than sixteen of 14), two tiles (32 rows) per workgroup: the fastest of the settings
+// measured on MI355X at the 70B shapes.
 // Rows per workgroup of the ring kernel: one round of workgroups (one per CU), a multiple
 // of 16.  The ring pays off from three row steps on; below that the streaming kernel is
 // used (measured on MI355X at the 70B shapes: o 8192x8192 streams faster, qkv and gate_up
@@ -538,27 +578,18 @@ hipError_t launch_gemv_mfma(const uint8_t* prepared, int64_t n, int64_t k, const
                          x, y, y_bf16 ? 1 : 0, (int)n, (int)k, (int)m, xr_rows((int)n), s);
     static const int per_wave = env_int("W4A16_MFMA_GPW", 8);
     static const int forced_t = env_int("W4A16_MFMA_TILES", 0);
-    static const int chunk = env_int("W4A16_MFMA_CHUNK", 2);
     int waves = (kg + per_wave - 1) / per_wave;
-    if (waves > 16) waves = 16;
+    if (waves > 8) waves = 8;
     if (waves < 1) waves = 1;
     const int gpw = (kg + waves - 1) / waves;
     waves = (kg + gpw - 1) / gpw;
-    // tiles of 16 rows per workgroup (1 or 2) and groups per load batch (1 or 2)
-    const int t = forced_t == 1 ? 1 : 2;
-    const int ch = chunk == 1 ? 1 : 2;
     const uint8_t* wq = prepared;
     const uint32_t* sz = reinterpret_cast<const uint32_t*>(prepared + sz_offset(n, k));
     const int yb = y_bf16 ? 1 : 0;
     const int N = (int)n, K = (int)k, M = (int)m;
-    if (t == 1 && ch == 1) return waves <= 8 ? launch_t<1, 1, 1, 512>(wq, sz, x, y, yb, N, K, M, gpw, waves, s)
-                                             : launch_t<1, 1, 1, 1024>(wq, sz, x, y, yb, N, K, M, gpw, waves, s);
-    if (t == 1) return waves <= 8 ? launch_t<1, 2, 1, 512>(wq, sz, x, y, yb, N, K, M, gpw, waves, s)
-                                  : launch_t<1, 2, 1, 1024>(wq, sz, x, y, yb, N, K, M, gpw, waves, s);
-    if (ch == 1) return waves <= 8 ? launch_t<2, 1, 1, 512>(wq, sz, x, y, yb, N, K, M, gpw, waves, s)
-                                   : launch_t<2, 1, 1, 1024>(wq, sz, x, y, yb, N, K, M, gpw, waves, s);
-    return waves <= 8 ? launch_t<2, 2, 1, 512>(wq, sz, x, y, yb, N, K, M, gpw, waves, s)
-                      : launch_t<2, 2, 1, 1024>(wq, sz, x, y, yb, N, K, M, gpw, waves, s);
+    // tiles of 16 rows per workgroup (1 or 2)
+    if (forced_t == 1) return launch_t<1>(wq, sz, x, y, yb, N, K, M, gpw, waves, s);
+    return launch_t<2>(wq, sz, x, y, yb, N, K, M, gpw, waves, s);
 }
 
 }  // namespace w4
