@@ -5,4 +5,10 @@ from .w4_oracle import (  # noqa: F401
     quantize_group_scalar, quantize_scalar, dot_scalar, dot_factored_exact,
     quantize_ref, unpack_codes, dequant_ref, gemv_ref, gemv_factored_ref,
     tolerance_ref, gemm_ref_rows, bits_per_weight, quantize_symmetric_ref, SYM_ZERO,
+    quantize_ref_f32, quantize_symmetric_ref_f32,
+)
+from .w4_formats import (  # noqa: F401
+    Format, CANONICAL, bf16_bits, bf16_value, scale_value, pack_zero_nibbles,
+    unpack_zero_nibbles, zero_bytes, quantize_format_ref, zeros_u8, dequant_format_ref,
+    gemv_format_ref, tolerance_format_ref, format_bits_per_weight, format_bytes,
 )

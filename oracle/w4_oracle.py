@@ -204,6 +204,13 @@ def quantize_ref(w: np.ndarray, group: int = GROUP):
     Returns (packed uint8 [N, K/2], scales float16 [N, K/group], zeros uint8 [N, K/group]).
     Weight quantization › How it works / Code, step by step on whole arrays.
     """
+    packed, s, z = quantize_ref_f32(w, group)
+    return packed, s.astype(np.float16), z
+
+
+def quantize_ref_f32(w: np.ndarray, group: int = GROUP):
+    """``quantize_ref`` with the binary32 scale returned unrounded (the stored formats
+    round it to fp16 or bf16)."""
     w = np.ascontiguousarray(w, dtype=np.float32)
     if w.ndim != 2:
         raise ValueError("W must be 2-D [N, K]")
@@ -223,10 +230,9 @@ def quantize_ref(w: np.ndarray, group: int = GROUP):
         z = _to_code_np(zc)
         t = g / s[:, :, None]
         codes = _to_code_np(_round_away_np(t).astype(np.float32) + zc[:, :, None])
-        s16 = s.astype(np.float16)
     codes = codes.reshape(n, k)
     packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
-    return packed, s16, z
+    return packed, s, z
 
 
 # ---------------------------------------------------------------------------
@@ -248,6 +254,12 @@ def quantize_symmetric_ref(w: np.ndarray, group: int = GROUP):
     all zeros 8).  A quotient that is NaN (a step that underflows to 0 on 0/0) clamps to
     -8, and +-inf clamp to the ends, as the C fmin/fmax clamp does.
     """
+    packed, s, z = quantize_symmetric_ref_f32(w, group)
+    return packed, s.astype(np.float16), z
+
+
+def quantize_symmetric_ref_f32(w: np.ndarray, group: int = GROUP):
+    """``quantize_symmetric_ref`` with the binary32 step returned unrounded."""
     w = np.ascontiguousarray(w, dtype=np.float32)
     if w.ndim != 2:
         raise ValueError("W must be 2-D [N, K]")
@@ -262,11 +274,10 @@ def quantize_symmetric_ref(w: np.ndarray, group: int = GROUP):
         s = np.where(amax > 0, amax / np.float32(SYM_TOP), np.float32(1.0)).astype(np.float32)
         t = g / s[:, :, None]
         q = np.fmin(np.fmax(np.rint(t), np.float32(-SYM_TOP - 1)), np.float32(SYM_TOP))
-        s16 = s.astype(np.float16)
     codes = (q.astype(np.int16) + SYM_ZERO).astype(np.uint8).reshape(n, k)
     packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
     zeros = np.full((n, k // group), SYM_ZERO, dtype=np.uint8)
-    return packed, s16, zeros
+    return packed, s, zeros
 
 
 def unpack_codes(packed: np.ndarray) -> np.ndarray:
