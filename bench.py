@@ -206,6 +206,50 @@ def page_layer(dev: str, reps: int = 5, copies: int = 64):
             "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
 
 
+FORMAT_VARIANTS = [  # (group, bf16 scale, zero bits): the storage variants timed at M = 1
+    (128, False, 8), (128, True, 8), (128, False, 4), (64, False, 8), (32, False, 8), (32, True, 4),
+]
+
+
+def format_variants(dev: str, reps: int = 5, copies: int = 2, calls: int = 16):
+    """w4_gemv_fmt at M = 1 on the 70B gate|up shape (57344 x 8192, bf16 x) per storage format.
+
+    ``copies`` prepared copies (2 x ~240 MB, past the 256 MB MALL) alternate over ``calls``
+    products in one graph.  GB/s counts the format's own bytes (codes, 2-byte scales, 4- or
+    8-bit zeros per group, x, y); the prepared layout carries every group's scale and zero
+    in one 4-byte word.
+    """
+    import torch
+
+    import dequant_gemv_w4_amd as w4
+    import synth
+    from dequant_gemv_w4_amd.decode import DecodeStep, GemvCall
+
+    n, k = synth.LLAMA70B_FUSED_SHAPES["gate_up"]
+    x = synth.normal_activations(1, k, 40200, dev)
+    out = {}
+    for group, sbf, zb in FORMAT_VARIANTS:
+        f = w4.W4Format.make(group, sbf, zb, False)
+        preps = []
+        for c in range(copies):
+            W = synth.normal_weights(n, k, 40300 + c, dev)
+            p, s, z = w4.w4_quantize_fmt(W, f)
+            del W
+            preps.append(w4.w4_prepare_fmt(p, s, z, f))
+            del p, s, z
+        y = torch.empty(1, n, dtype=torch.float32, device=dev)
+        st = DecodeStep([GemvCall(preps[i % copies], n, k, x, y, f) for i in range(calls)])
+        st.capture()
+        ms = time_step(st, reps, 1)
+        gbs = st.algorithmic_bytes() / (ms * 1e-3) / 1e9
+        out[f"g{group}_{'bf16' if sbf else 'fp16'}_z{zb}"] = {
+            "bits_per_weight": 4 + (16 + zb) / group, "us_per_call": round(ms * 1000 / calls, 2),
+            "GB/s": round(gbs, 1), "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
+        del st, preps
+        torch.cuda.empty_cache()
+    return out
+
+
 def llama7b_layers(dev: str, layers: int = 6, reps: int = 5, fused: bool = False):
     """7B-shaped layers with 1 % outlier channels (x20 in W columns and x), bf16 x, M=1.
 
@@ -445,6 +489,8 @@ def main() -> int:
         log(f"7B layers: {result['llama7b_layer_m1']}")
         result["llama7b_layer_fused_m1"] = llama7b_layers(dev, fused=True)
         log(f"7B layers, fused: {result['llama7b_layer_fused_m1']}")
+        result["format_variants_m1"] = format_variants(dev)
+        log(f"format variants: {result['format_variants_m1']}")
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle sample")

@@ -21,6 +21,8 @@ __all__ = [
     "w4_status_string", "w4_last_hip_error", "w4_format_version",
     "W4ChainGemv", "w4_chain_plan_bytes", "w4_chain_workspace_bytes", "w4_chain_plan",
     "w4_chain_run",
+    "W4Format", "w4_zeros_bytes", "w4_quantize_fmt", "w4_prepared_bytes_fmt", "w4_prepare_fmt",
+    "w4_unprepare_fmt", "w4_gemv_fmt",
     "W4_OK", "W4_F32", "W4_BF16", "GROUP",
 ]
 
@@ -37,6 +39,17 @@ STATUS_SCALE_OVERFLOW = 2
 STATUS_SCALE_ZERO = 4
 
 _lib = None
+
+
+class W4Format(ctypes.Structure):
+    """w4_format: group (32, 64, 128), scale_bf16 (0/1), zero_bits (4/8), symmetric (0/1)."""
+
+    _fields_ = [("group", ctypes.c_int32), ("scale_bf16", ctypes.c_int32),
+                ("zero_bits", ctypes.c_int32), ("symmetric", ctypes.c_int32)]
+
+    @classmethod
+    def make(cls, group=128, scale_bf16=False, zero_bits=8, symmetric=False):
+        return cls(int(group), int(bool(scale_bf16)), int(zero_bits), int(bool(symmetric)))
 
 
 class W4Error(RuntimeError):
@@ -91,6 +104,19 @@ def lib() -> ctypes.CDLL:
     L.w4_chain_plan.restype = i32
     L.w4_chain_run.argtypes = [vp, vp, vp, sz, vp]
     L.w4_chain_run.restype = i32
+    fp = ctypes.POINTER(W4Format)
+    L.w4_zeros_bytes.argtypes = [i64, i64, fp]
+    L.w4_zeros_bytes.restype = sz
+    L.w4_quantize_fmt.argtypes = [vp, i32, i64, i64, fp, vp, vp, vp, vp, vp]
+    L.w4_quantize_fmt.restype = i32
+    L.w4_prepared_bytes_fmt.argtypes = [i64, i64, fp]
+    L.w4_prepared_bytes_fmt.restype = sz
+    L.w4_prepare_fmt.argtypes = [vp, vp, vp, i64, i64, fp, vp, sz, vp]
+    L.w4_prepare_fmt.restype = i32
+    L.w4_unprepare_fmt.argtypes = [vp, i64, i64, fp, vp, vp, vp, vp]
+    L.w4_unprepare_fmt.restype = i32
+    L.w4_gemv_fmt.argtypes = [vp, i64, i64, fp, vp, i32, i64, vp, i32, vp]
+    L.w4_gemv_fmt.restype = i32
     del u32
     _lib = L
     return L
@@ -253,6 +279,114 @@ def w4_gemv(prepared, N: int, K: int, x, y=None, out_dtype=None):
     yt = W4_F32 if y.dtype == torch.float32 else W4_BF16
     _check(lib().w4_gemv(_ptr(prepared), N, K, _ptr(x), xt, M, _ptr(y), yt, _stream(x)),
            "w4_gemv")
+    return y
+
+
+def _fmt(fmt) -> W4Format:
+    if isinstance(fmt, W4Format):
+        return fmt
+    if isinstance(fmt, dict):
+        return W4Format.make(**fmt)
+    return W4Format.make(*fmt)
+
+
+def w4_zeros_bytes(N: int, K: int, fmt) -> int:
+    f = _fmt(fmt)
+    return int(lib().w4_zeros_bytes(int(N), int(K), ctypes.byref(f)))
+
+
+def w4_prepared_bytes_fmt(N: int, K: int, fmt) -> int:
+    f = _fmt(fmt)
+    return int(lib().w4_prepared_bytes_fmt(int(N), int(K), ctypes.byref(f)))
+
+
+def w4_quantize_fmt(W, fmt, status=None):
+    """Quantize W [N, K] (float32 or bfloat16) in format ``fmt`` (a W4Format, a dict of its
+    fields or a tuple).  Returns (packed uint8 [N, K/2], scales [N, K/group] float16 or
+    bfloat16, zeros uint8 [N, K/group] or [w4_zeros_bytes] for 4-bit zeros)."""
+    import torch
+    f = _fmt(fmt)
+    _require(W, (torch.float32, torch.bfloat16), None, "W")
+    if W.dim() != 2:
+        raise ValueError("W must be 2-D")
+    N, K = W.shape
+    if f.group not in (32, 64, 128) or K % f.group:
+        raise ValueError("K must be a multiple of the group size (32, 64 or 128)")
+    kg = K // f.group
+    dev = W.device
+    packed = torch.empty(N, K // 2, dtype=torch.uint8, device=dev)
+    scales = torch.empty(N, kg, dtype=torch.bfloat16 if f.scale_bf16 else torch.float16, device=dev)
+    nz = w4_zeros_bytes(N, K, f)
+    zeros = torch.empty((N, kg) if f.zero_bits == 8 else (max(nz, 1),), dtype=torch.uint8, device=dev)
+    st_ptr = ctypes.c_void_p(None)
+    if status is not None:
+        _require(status, (torch.int32,), None, "status")
+        st_ptr = _ptr(status)
+    wt = W4_BF16 if W.dtype == torch.bfloat16 else W4_F32
+    _check(lib().w4_quantize_fmt(_ptr(W), wt, N, K, ctypes.byref(f), _ptr(packed), _ptr(scales),
+                                 _ptr(zeros), st_ptr, _stream(W)), "w4_quantize_fmt")
+    return packed, scales, zeros
+
+
+def w4_prepare_fmt(packed, scales, zeros, fmt, prepared=None):
+    """Kernel layout of a format's arrays; returns a uint8 tensor of w4_prepared_bytes_fmt."""
+    import torch
+    f = _fmt(fmt)
+    _require(packed, torch.uint8, None, "packed")
+    N, Kh = packed.shape
+    K = 2 * Kh
+    _require(scales, torch.bfloat16 if f.scale_bf16 else torch.float16, (N, K // f.group), "scales")
+    _require(zeros, torch.uint8, None, "zeros")
+    if zeros.numel() < w4_zeros_bytes(N, K, f):
+        raise ValueError("zeros too small for the format")
+    nbytes = w4_prepared_bytes_fmt(N, K, f)
+    if prepared is None:
+        prepared = torch.empty(nbytes, dtype=torch.uint8, device=packed.device)
+    _require(prepared, torch.uint8, None, "prepared")
+    _check(lib().w4_prepare_fmt(_ptr(packed), _ptr(scales), _ptr(zeros), N, K, ctypes.byref(f),
+                                _ptr(prepared), prepared.numel(), _stream(packed)),
+           "w4_prepare_fmt")
+    return prepared
+
+
+def w4_unprepare_fmt(prepared, N: int, K: int, fmt):
+    """Inverse of w4_prepare_fmt: returns (packed, scales, zeros)."""
+    import torch
+    f = _fmt(fmt)
+    _require(prepared, torch.uint8, None, "prepared")
+    if prepared.numel() < w4_prepared_bytes_fmt(N, K, f):
+        raise ValueError("prepared buffer too small")
+    dev = prepared.device
+    kg = K // f.group
+    packed = torch.empty(N, K // 2, dtype=torch.uint8, device=dev)
+    scales = torch.empty(N, kg, dtype=torch.bfloat16 if f.scale_bf16 else torch.float16, device=dev)
+    nz = w4_zeros_bytes(N, K, f)
+    zeros = torch.empty((N, kg) if f.zero_bits == 8 else (max(nz, 1),), dtype=torch.uint8, device=dev)
+    _check(lib().w4_unprepare_fmt(_ptr(prepared), N, K, ctypes.byref(f), _ptr(packed),
+                                  _ptr(scales), _ptr(zeros), _stream(prepared)), "w4_unprepare_fmt")
+    return packed, scales, zeros
+
+
+def w4_gemv_fmt(prepared, N: int, K: int, fmt, x, y=None, out_dtype=None):
+    """w4_gemv on the prepared layout of format ``fmt``."""
+    import torch
+    f = _fmt(fmt)
+    _require(prepared, torch.uint8, None, "prepared")
+    _require(x, (torch.bfloat16, torch.float32), None, "x")
+    if x.dim() == 1:
+        x = x.unsqueeze(0)
+    M = x.shape[0]
+    if x.shape[1] != K:
+        raise ValueError("x must be [M, K]")
+    if out_dtype is None:
+        out_dtype = y.dtype if y is not None else torch.float32
+    if y is None:
+        y = torch.empty(M, N, dtype=out_dtype, device=x.device)
+    _require(y, (torch.float32, torch.bfloat16), (M, N), "y")
+    xt = W4_F32 if x.dtype == torch.float32 else W4_BF16
+    yt = W4_F32 if y.dtype == torch.float32 else W4_BF16
+    _check(lib().w4_gemv_fmt(_ptr(prepared), N, K, ctypes.byref(f), _ptr(x), xt, M, _ptr(y), yt,
+                             _stream(x)), "w4_gemv_fmt")
     return y
 
 

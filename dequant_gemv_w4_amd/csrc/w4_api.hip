@@ -44,6 +44,19 @@ w4_status check_nk(int64_t n, int64_t k) {
     return W4_OK;
 }
 
+w4_status to_fmt(const w4_format* in, w4::Fmt* out) {
+    if (!in) return W4_ERR_NULL;
+    if ((in->group != 32 && in->group != 64 && in->group != 128) ||
+        (in->scale_bf16 != 0 && in->scale_bf16 != 1) ||
+        (in->zero_bits != 4 && in->zero_bits != 8) || (in->symmetric != 0 && in->symmetric != 1))
+        return W4_ERR_UNSUPPORTED;
+    out->group = in->group;
+    out->scale_bf16 = in->scale_bf16 == 1;
+    out->zero4 = in->zero_bits == 4;
+    out->symmetric = in->symmetric == 1;
+    return W4_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -80,7 +93,9 @@ static w4_status quantize_common(const void* W, w4_dtype wt, int64_t N, int64_t 
         return W4_ERR_ALIGN;
     st = check_arch();
     if (st != W4_OK) return st;
-    hipError_t e = w4::launch_quantize(W, wt == W4_BF16, symmetric, N * (K / W4_GROUP), packed,
+    w4::Fmt f;
+    f.symmetric = symmetric;
+    hipError_t e = w4::launch_quantize(W, wt == W4_BF16, f, N * (K / W4_GROUP), packed,
                                        scales_f16, zeros, d_status, stream);
     return e == hipSuccess ? W4_OK : hip_fail(e);
 }
@@ -113,7 +128,7 @@ w4_status w4_prepare(const uint8_t* packed, const uint16_t* scales_f16, const ui
     if (prepared_bytes < w4_prepared_bytes(N, K)) return W4_ERR_BUFFER;
     st = check_arch();
     if (st != W4_OK) return st;
-    hipError_t e = w4::launch_prepare(packed, scales_f16, zeros, N, K,
+    hipError_t e = w4::launch_prepare(packed, scales_f16, zeros, N, K, w4::Fmt{},
                                       static_cast<uint8_t*>(prepared), stream);
     return e == hipSuccess ? W4_OK : hip_fail(e);
 }
@@ -127,7 +142,7 @@ w4_status w4_unprepare(const void* prepared, int64_t N, int64_t K, uint8_t* pack
         return W4_ERR_ALIGN;
     st = check_arch();
     if (st != W4_OK) return st;
-    hipError_t e = w4::launch_unprepare(static_cast<const uint8_t*>(prepared), N, K, packed,
+    hipError_t e = w4::launch_unprepare(static_cast<const uint8_t*>(prepared), N, K, w4::Fmt{}, packed,
                                         scales_f16, zeros, stream);
     return e == hipSuccess ? W4_OK : hip_fail(e);
 }
@@ -145,6 +160,100 @@ w4_status w4_gemv(const void* prepared, int64_t N, int64_t K, const void* x, w4_
     if (st != W4_OK) return st;
     hipError_t e = w4::launch_gemv(static_cast<const uint8_t*>(prepared), N, K, x, xt == W4_F32,
                                    M, y, yt == W4_BF16, stream);
+    return e == hipSuccess ? W4_OK : hip_fail(e);
+}
+
+size_t w4_zeros_bytes(int64_t N, int64_t K, const w4_format* fmt) {
+    w4::Fmt f;
+    if (to_fmt(fmt, &f) != W4_OK || check_nk(N, K) != W4_OK) return 0;
+    const int64_t groups = N * (K / f.group);
+    return (size_t)(f.zero4 ? (groups + 1) / 2 : groups);
+}
+
+w4_status w4_quantize_fmt(const void* W, w4_dtype wt, int64_t N, int64_t K,
+                          const w4_format* fmt, uint8_t* packed, uint16_t* scales,
+                          uint8_t* zeros, uint32_t* d_status, hipStream_t stream) {
+    if (!W || !packed || !scales || !zeros || !fmt) return W4_ERR_NULL;
+    w4::Fmt f;
+    w4_status st = to_fmt(fmt, &f);
+    if (st != W4_OK) return st;
+    if (wt != W4_F32 && wt != W4_BF16) return W4_ERR_DTYPE;
+    st = check_nk(N, K);
+    if (st != W4_OK) return st;
+    if (!aligned(W, 16) || !aligned(packed, 16) || !aligned(scales, 2) ||
+        (d_status && !aligned(d_status, 4)))
+        return W4_ERR_ALIGN;
+    st = check_arch();
+    if (st != W4_OK) return st;
+    hipError_t e = w4::launch_quantize(W, wt == W4_BF16, f, N * (K / f.group), packed, scales,
+                                       zeros, d_status, stream);
+    return e == hipSuccess ? W4_OK : hip_fail(e);
+}
+
+size_t w4_prepared_bytes_fmt(int64_t N, int64_t K, const w4_format* fmt) {
+    w4::Fmt f;
+    if (to_fmt(fmt, &f) != W4_OK || check_nk(N, K) != W4_OK) return 0;
+    return (size_t)w4::prepared_total_g(N, K, f.group);
+}
+
+w4_status w4_prepare_fmt(const uint8_t* packed, const uint16_t* scales, const uint8_t* zeros,
+                         int64_t N, int64_t K, const w4_format* fmt, void* prepared,
+                         size_t prepared_bytes, hipStream_t stream) {
+    if (!packed || !scales || !zeros || !prepared || !fmt) return W4_ERR_NULL;
+    w4::Fmt f;
+    w4_status st = to_fmt(fmt, &f);
+    if (st != W4_OK) return st;
+    st = check_nk(N, K);
+    if (st != W4_OK) return st;
+    if (!aligned(packed, 16) || !aligned(scales, 2) || !aligned(prepared, 256))
+        return W4_ERR_ALIGN;
+    if (prepared_bytes < w4_prepared_bytes_fmt(N, K, fmt)) return W4_ERR_BUFFER;
+    st = check_arch();
+    if (st != W4_OK) return st;
+    hipError_t e = w4::launch_prepare(packed, scales, zeros, N, K, f,
+                                      static_cast<uint8_t*>(prepared), stream);
+    return e == hipSuccess ? W4_OK : hip_fail(e);
+}
+
+w4_status w4_unprepare_fmt(const void* prepared, int64_t N, int64_t K, const w4_format* fmt,
+                           uint8_t* packed, uint16_t* scales, uint8_t* zeros,
+                           hipStream_t stream) {
+    if (!packed || !scales || !zeros || !prepared || !fmt) return W4_ERR_NULL;
+    w4::Fmt f;
+    w4_status st = to_fmt(fmt, &f);
+    if (st != W4_OK) return st;
+    st = check_nk(N, K);
+    if (st != W4_OK) return st;
+    if (!aligned(packed, 16) || !aligned(scales, 2) || !aligned(prepared, 256))
+        return W4_ERR_ALIGN;
+    st = check_arch();
+    if (st != W4_OK) return st;
+    hipError_t e = w4::launch_unprepare(static_cast<const uint8_t*>(prepared), N, K, f, packed,
+                                        scales, zeros, stream);
+    return e == hipSuccess ? W4_OK : hip_fail(e);
+}
+
+w4_status w4_gemv_fmt(const void* prepared, int64_t N, int64_t K, const w4_format* fmt,
+                      const void* x, w4_dtype xt, int64_t M, void* y, w4_dtype yt,
+                      hipStream_t stream) {
+    if (!fmt) return W4_ERR_NULL;
+    w4::Fmt f;
+    w4_status st = to_fmt(fmt, &f);
+    if (st != W4_OK) return st;
+    if (f.group == W4_GROUP && !f.scale_bf16)
+        return w4_gemv(prepared, N, K, x, xt, M, y, yt, stream);
+    if (!prepared || !x || !y) return W4_ERR_NULL;
+    if ((xt != W4_F32 && xt != W4_BF16) || (yt != W4_F32 && yt != W4_BF16)) return W4_ERR_DTYPE;
+    st = check_nk(N, K);
+    if (st != W4_OK) return st;
+    if (K > W4_GEMV_MAX_K || M < 1 || M > W4_GEMV_MAX_M) return W4_ERR_SHAPE;
+    if (!aligned(prepared, 256) || !aligned(x, 16) || !aligned(y, yt == W4_F32 ? 4 : 2))
+        return W4_ERR_ALIGN;
+    st = check_arch();
+    if (st != W4_OK) return st;
+    hipError_t e = w4::launch_gemv_dot2(static_cast<const uint8_t*>(prepared), N, K, f.group,
+                                        f.scale_bf16, x, xt == W4_F32, M, y, yt == W4_BF16,
+                                        stream);
     return e == hipSuccess ? W4_OK : hip_fail(e);
 }
 

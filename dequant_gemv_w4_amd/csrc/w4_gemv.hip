@@ -107,18 +107,20 @@ __device__ __forceinline__ float reduce4(float a0, float a1, float a2, float a3)
     return k;
 }
 
-template <int MT, bool XF32, int SPT, int MAXT, int CH, bool RAGGED>
+// SBF16: the scale bits are bfloat16 (else binary16); gshift: log2(group / 32), the slices
+// of one group (a group of 32, 64 or 128 inputs has its own scale/zero word)
+template <int MT, bool XF32, int SPT, int MAXT, int CH, bool RAGGED, bool SBF16>
 __global__ __launch_bounds__(MAXT) void gemv_kernel(const u32x4_t* __restrict__ wq,
                                                     const u32x4_t* __restrict__ sz4,
                                                     const void* __restrict__ xv,
                                                     void* __restrict__ yv, int y_bf16, int N,
-                                                    int K, int M, int rows_per_wg) {
+                                                    int K, int M, int rows_per_wg, int gshift) {
     constexpr int XE = XF32 ? 2 * MT : MT;  // bf16 operand rows
     constexpr int R = kRowsPerStep;
     extern __shared__ float red[];          // [waves][rows_per_wg][XE]
 
     const int S = K >> 5;
-    const int Kg = K >> 7;
+    const int Kg = K >> (5 + gshift);
     const int T = blockDim.x;
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
@@ -137,7 +139,7 @@ __global__ __launch_bounds__(MAXT) void gemv_kernel(const u32x4_t* __restrict__ 
         act[j] = RAGGED ? sl[j] < S : true;
         const int slc = RAGGED ? min(sl[j], S - 1) : sl[j];
         woff[j] = (uint32_t)slc * 16u;
-        soff[j] = (uint32_t)(slc >> 2) * 16u;
+        soff[j] = (uint32_t)(slc >> gshift) * 16u;
     }
 
     // ---- x slices first: their loads complete before the weight stream that follows
@@ -228,7 +230,8 @@ __global__ __launch_bounds__(MAXT) void gemv_kernel(const u32x4_t* __restrict__ 
 #pragma unroll
                 for (int rr = 0; rr < R; ++rr) {
                     const uint32_t szw = sb[c][j][rr];
-                    const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)(szw & 0xFFFFu));
+                    const float s = SBF16 ? __uint_as_float(szw << 16)
+                                          : (float)__builtin_bit_cast(_Float16, (uint16_t)(szw & 0xFFFFu));
                     const float zb = (float)((szw >> 16) & 0xFFu);  // zero + 128
                     uint32_t pr[16];
 #pragma unroll
@@ -304,6 +307,8 @@ struct GemvArgs {
     const void* x;
     void* y;
     int y_bf16, n, k, m, rows;
+    int gshift;       // log2(group / 32)
+    bool scale_bf16;
 };
 
 int env_int(const char* name, int dflt) {
@@ -358,24 +363,24 @@ int rows_for(Kern kernel, int block, int n, int xe, int chunk_rows, std::atomic<
     return rows;
 }
 
-template <int MT, bool XF32, int SPT, int MAXT, int CH, bool RAGGED>
+template <int MT, bool XF32, int SPT, int MAXT, int CH, bool RAGGED, bool SBF16>
 hipError_t launch_var(GemvArgs a, dim3 block, hipStream_t s) {
     constexpr int XE = XF32 ? 2 * MT : MT;
     static std::atomic<int> cache[17];
-    auto kern = gemv_kernel<MT, XF32, SPT, MAXT, CH, RAGGED>;
+    auto kern = gemv_kernel<MT, XF32, SPT, MAXT, CH, RAGGED, SBF16>;
     a.rows = rows_for(kern, (int)block.x, a.n, XE, CH * kRowsPerStep, cache);
     const dim3 grid((unsigned)((a.n + a.rows - 1) / a.rows));
     const size_t shmem = (size_t)(block.x / 64) * a.rows * XE * sizeof(float);
     hipLaunchKernelGGL(kern, grid, block, shmem, s, a.wq, a.sz4, a.x, a.y, a.y_bf16, a.n, a.k, a.m,
-                       a.rows);
+                       a.rows, a.gshift);
     return hipGetLastError();
 }
 
-template <int MT, bool XF32, int SPT, int MAXT, int CH>
+template <int MT, bool XF32, int SPT, int MAXT, int CH, bool SBF16>
 hipError_t launch_one(const GemvArgs& a, dim3 block, hipStream_t s) {
     const bool ragged = (int)block.x * SPT * 32 != a.k;
-    return ragged ? launch_var<MT, XF32, SPT, MAXT, CH, true>(a, block, s)
-                  : launch_var<MT, XF32, SPT, MAXT, CH, false>(a, block, s);
+    return ragged ? launch_var<MT, XF32, SPT, MAXT, CH, true, SBF16>(a, block, s)
+                  : launch_var<MT, XF32, SPT, MAXT, CH, false, SBF16>(a, block, s);
 }
 
 // Instantiated variants (MT = rows of x per launch, SPT = 16-byte slices per lane,
@@ -390,26 +395,36 @@ int max_mt(bool x_f32, int spt) {
     return spt == 1 ? 2 : 1;
 }
 
-hipError_t dispatch(bool x_f32, int spt, int mt, const GemvArgs& a, dim3 block, hipStream_t s) {
-    static const int chunk = env_int("W4A16_GEMV_CHUNK", 2);
+// SB: bfloat16 scale bits (the format variants take the default load chunk only)
+template <bool SB>
+hipError_t dispatch_t(bool x_f32, int spt, int mt, const GemvArgs& a, dim3 block, hipStream_t s) {
+    static const int chunk = SB ? 2 : env_int("W4A16_GEMV_CHUNK", 2);
     if (!x_f32 && mt == 1 && spt == 1) {
-        if (block.x > 512) {
-            if (chunk == 1) return launch_one<1, false, 1, 1024, 1>(a, block, s);
-            return chunk == 4 ? launch_one<1, false, 1, 1024, 4>(a, block, s)
-                              : launch_one<1, false, 1, 1024, 2>(a, block, s);
+        if constexpr (!SB) {
+            if (block.x > 512) {
+                if (chunk == 1) return launch_one<1, false, 1, 1024, 1, SB>(a, block, s);
+                if (chunk == 4) return launch_one<1, false, 1, 1024, 4, SB>(a, block, s);
+            } else {
+                if (chunk == 1) return launch_one<1, false, 1, 512, 1, SB>(a, block, s);
+                if (chunk == 4) return launch_one<1, false, 1, 512, 4, SB>(a, block, s);
+            }
         }
-        if (chunk == 1) return launch_one<1, false, 1, 512, 1>(a, block, s);
-        return chunk == 4 ? launch_one<1, false, 1, 512, 4>(a, block, s)
-                          : launch_one<1, false, 1, 512, 2>(a, block, s);
+        return block.x > 512 ? launch_one<1, false, 1, 1024, 2, SB>(a, block, s)
+                             : launch_one<1, false, 1, 512, 2, SB>(a, block, s);
     }
 #define W4_CASE(MTV, XF, SP, NB) \
-    if (mt == MTV && x_f32 == XF && spt == SP) return launch_one<MTV, XF, SP, 512, NB>(a, block, s);
+    if (mt == MTV && x_f32 == XF && spt == SP) return launch_one<MTV, XF, SP, 512, NB, SB>(a, block, s);
     W4_CASE(2, false, 1, 2) W4_CASE(3, false, 1, 2) W4_CASE(4, false, 1, 2)
     W4_CASE(1, false, 2, 2) W4_CASE(2, false, 2, 1)
     W4_CASE(1, true, 1, 2) W4_CASE(2, true, 1, 2)
     W4_CASE(1, true, 2, 1)
 #undef W4_CASE
     return hipErrorInvalidValue;
+}
+
+hipError_t dispatch(bool x_f32, int spt, int mt, const GemvArgs& a, dim3 block, hipStream_t s) {
+    return a.scale_bf16 ? dispatch_t<true>(x_f32, spt, mt, a, block, s)
+                        : dispatch_t<false>(x_f32, spt, mt, a, block, s);
 }
 
 }  // namespace
@@ -429,6 +444,12 @@ hipError_t launch_gemv(const uint8_t* prepared, int64_t n, int64_t k, const void
                            (m == 3 && one_pass && n <= 16384 && gemv_ring_takes(n, k));
     if (!x_f32 && !dot2_wins && use_mfma)
         return launch_gemv_mfma(prepared, n, k, static_cast<const uint16_t*>(x), m, y, y_bf16, s);
+    return launch_gemv_dot2(prepared, n, k, kGroup, false, x, x_f32, m, y, y_bf16, s);
+}
+
+hipError_t launch_gemv_dot2(const uint8_t* prepared, int64_t n, int64_t k, int group,
+                            bool scale_bf16, const void* x, bool x_f32, int64_t m, void* y,
+                            bool y_bf16, hipStream_t s) {
     const int S = (int)(k / 32);
     GemvArgs a;
     a.wq = reinterpret_cast<const u32x4_t*>(prepared);
@@ -437,6 +458,8 @@ hipError_t launch_gemv(const uint8_t* prepared, int64_t n, int64_t k, const void
     a.n = (int)n;
     a.k = (int)k;
     a.rows = 0;
+    a.gshift = group == 32 ? 0 : group == 64 ? 1 : 2;
+    a.scale_bf16 = scale_bf16;
     const bool wide = !x_f32 && m == 1;      // one slice per lane, up to 1024 threads
     const int spt = wide ? 1 : (S <= 512 ? 1 : 2);
     const int waves = (S + 64 * spt - 1) / (64 * spt);

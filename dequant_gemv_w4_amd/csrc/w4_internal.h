@@ -40,6 +40,14 @@ inline __host__ __device__ int64_t sz_words(int64_t n, int64_t k) {
 inline __host__ __device__ int64_t prepared_total(int64_t n, int64_t k) {
     return sz_offset(n, k) + sz_words(n, k) * 4;
 }
+// the same layout for a group of 32, 64 or 128 inputs: one scale/zero word per row and
+// group, four rows of one group per 16 bytes
+inline __host__ __device__ int64_t sz_words_g(int64_t n, int64_t k, int64_t group) {
+    return (n + 3) / 4 * 4 * (k / group);
+}
+inline __host__ __device__ int64_t prepared_total_g(int64_t n, int64_t k, int64_t group) {
+    return sz_offset(n, k) + sz_words_g(n, k, group) * 4;
+}
 // index of the scale/zero word of row n, group g
 inline __host__ __device__ int64_t sz_index(int64_t n, int64_t g, int64_t kg) {
     return ((n >> 2) * kg + g) * 4 + (n & 3);
@@ -98,15 +106,30 @@ int chain_grid(int max_k);
 hipError_t launch_chain(const ChainHeader& h, const uint8_t* plan_dev, uint32_t* ws, hipStream_t s);
 
 // Launch wrappers (defined in the .hip files); return hipSuccess or the launch error.
-hipError_t launch_quantize(const void* W, bool bf16, bool symmetric, int64_t n_groups,
+// Storage variant of the weight format: group of 32, 64 or 128 inputs, scale stored as
+// binary16 or bfloat16 bits, zeros one per byte or two per byte (flat over [N, K/group],
+// even index in the low nibble), asymmetric or symmetric codes.
+struct Fmt {
+    int group = 128;
+    bool scale_bf16 = false;
+    bool zero4 = false;
+    bool symmetric = false;
+};
+
+hipError_t launch_quantize(const void* W, bool bf16, const Fmt& f, int64_t n_groups,
                            uint8_t* packed, uint16_t* scales, uint8_t* zeros, uint32_t* status,
                            hipStream_t s);
 hipError_t launch_prepare(const uint8_t* packed, const uint16_t* scales, const uint8_t* zeros,
-                          int64_t n, int64_t k, uint8_t* prepared, hipStream_t s);
-hipError_t launch_unprepare(const uint8_t* prepared, int64_t n, int64_t k, uint8_t* packed,
-                            uint16_t* scales, uint8_t* zeros, hipStream_t s);
+                          int64_t n, int64_t k, const Fmt& f, uint8_t* prepared, hipStream_t s);
+hipError_t launch_unprepare(const uint8_t* prepared, int64_t n, int64_t k, const Fmt& f,
+                            uint8_t* packed, uint16_t* scales, uint8_t* zeros, hipStream_t s);
 hipError_t launch_gemv(const uint8_t* prepared, int64_t n, int64_t k, const void* x, bool x_f32,
                        int64_t m, void* y, bool y_bf16, hipStream_t s);
+// the one-row (dot2) kernel on any group size and scale type (w4_gemv routes here and to
+// the matrix-core kernels for the canonical format)
+hipError_t launch_gemv_dot2(const uint8_t* prepared, int64_t n, int64_t k, int group,
+                            bool scale_bf16, const void* x, bool x_f32, int64_t m, void* y,
+                            bool y_bf16, hipStream_t s);
 hipError_t launch_gemv_mfma(const uint8_t* prepared, int64_t n, int64_t k, const uint16_t* x,
                             int64_t m, void* y, bool y_bf16, hipStream_t s);
 // Whether launch_gemv_mfma runs the shape on the ring kernel (x held in registers, weights

@@ -11,11 +11,20 @@
 // clamp(round(w / step), -8, 7) with halves to even (rintf), stored as code + 8 with
 // zero 8, so the products' (stored - zero) * scale16 holds unchanged.
 //
-// Work split: 32 lanes own one group (4 consecutive weights each, one 16-byte
-// load), a wave owns two groups, a 256-thread block eight.  The group's
-// minimum and maximum are a 32-lane butterfly; every lane then derives the
-// same scale and zero and writes its two packed bytes, so a wave stores 128
-// contiguous bytes.
+// Storage variants (page "Quantization" › "Code": int4 groups of 128 and of 32;
+// page "Weight quantization" › "Implementation notes": scales kept in fp16 or bf16;
+// "Code" and "Complexity and constants": a 4-bit zero per group): groups of 32, 64 or
+// 128 inputs; the binary32 step stored as binary16 or bfloat16 (both round to nearest
+// even); zeros one per byte or two per byte, packed over the flat [N, K/group] array with
+// the even index in the low nibble.  The codes and the step do not depend on the storage.
+//
+// Work split: G/4 lanes own one group (4 consecutive weights each, one 16-byte
+// load of binary32 weights), a 256-thread block 1024/G groups.  The group's
+// minimum and maximum are a butterfly over those lanes; every lane then derives
+// the same scale and zero and writes its two packed bytes, so the lanes of a
+// group store its G/2 contiguous bytes.  With 4-bit zeros the first lane of an
+// even group also takes the odd group's zero (the next G/4 lanes of the same
+// wave) and writes the shared byte.
 #include "w4_internal.h"
 
 namespace w4 {
@@ -45,19 +54,27 @@ __device__ __forceinline__ void load4(const void* __restrict__ W, int64_t idx, f
     }
 }
 
-template <bool BF16, bool SYM>
+__device__ __forceinline__ uint16_t bf16_bits_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// LPG: lanes per group (group = 4 LPG inputs)
+template <bool BF16, bool SYM, int LPG>
 __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ W, int64_t n_groups,
                                                        uint16_t* __restrict__ packed16,
                                                        uint16_t* __restrict__ scales,
                                                        uint8_t* __restrict__ zeros,
-                                                       uint32_t* __restrict__ status) {
+                                                       uint32_t* __restrict__ status,
+                                                       int scale_bf16, int zero4) {
 #pragma clang fp contract(off)
-    const int lane = threadIdx.x & 31;
-    const int64_t gi = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
+    constexpr int G = 4 * LPG;
+    const int lane = threadIdx.x & (LPG - 1);
+    const int64_t gi = (int64_t)blockIdx.x * (256 / LPG) + (threadIdx.x / LPG);
     const bool valid = gi < n_groups;
 
     float v[4] = {0.f, 0.f, 0.f, 0.f};
-    if (valid) load4<BF16>(W, gi * kGroup + lane * 4, v);
+    if (valid) load4<BF16>(W, gi * G + lane * 4, v);
 
     bool bad = false;
     float lo = v[0], hi = v[0];
@@ -68,9 +85,9 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
         hi = fmaxf(hi, v[i]);
     }
 #pragma unroll
-    for (int d = 16; d >= 1; d >>= 1) {
-        lo = fminf(lo, __shfl_xor(lo, d, 32));
-        hi = fmaxf(hi, __shfl_xor(hi, d, 32));
+    for (int d = LPG / 2; d >= 1; d >>= 1) {
+        lo = fminf(lo, __shfl_xor(lo, d, LPG));
+        hi = fmaxf(hi, __shfl_xor(hi, d, LPG));
     }
     float s, zc;
     uint32_t c[4];
@@ -92,17 +109,28 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
 #pragma unroll
         for (int i = 0; i < 4; ++i) c[i] = to_code(roundf(v[i] / s) + zc);
     }
+    const uint32_t zbyte = to_code(zc);
+    // the odd neighbour's zero, LPG lanes up in the same wave (64 / LPG groups per wave, an
+    // even number, so an even group's partner never crosses the wave)
+    const uint32_t zodd = __shfl((int)zbyte, (int)(threadIdx.x & 63) + LPG, 64) & 0xFu;
 
     if (!valid) return;
-    packed16[gi * (kGroup / 4) + lane] = (uint16_t)(c[0] | (c[1] << 4) | (c[2] << 8) | (c[3] << 12));
+    packed16[gi * LPG + lane] = (uint16_t)(c[0] | (c[1] << 4) | (c[2] << 8) | (c[3] << 12));
     if (bad && status) atomicOr(status, 1u);  // W4_STATUS_NONFINITE
     if (lane == 0) {
-        const uint16_t s16 = __builtin_bit_cast(uint16_t, (_Float16)s);  // round to nearest even
+        const uint16_t s16 = scale_bf16 ? bf16_bits_rne(s)
+                                        : __builtin_bit_cast(uint16_t, (_Float16)s);  // nearest even
+        const uint32_t inf_bits = scale_bf16 ? 0x7F80u : 0x7C00u;
         scales[gi] = s16;
-        zeros[gi] = (uint8_t)to_code(zc);
+        if (!zero4) {
+            zeros[gi] = (uint8_t)zbyte;
+        } else if ((gi & 1) == 0) {
+            const bool pair = gi + 1 < n_groups;
+            zeros[gi >> 1] = (uint8_t)(zbyte | (pair ? zodd << 4 : 0u));
+        }
         uint32_t flags = 0;
-        if ((s16 & 0x7FFFu) == 0x7C00u) flags |= 2u;          // W4_STATUS_SCALE_OVERFLOW
-        if ((s16 & 0x7FFFu) == 0 && nonempty) flags |= 4u;   // W4_STATUS_SCALE_ZERO
+        if ((s16 & 0x7FFFu) == inf_bits) flags |= 2u;           // W4_STATUS_SCALE_OVERFLOW
+        if ((s16 & 0x7FFFu) == 0 && nonempty) flags |= 4u;     // W4_STATUS_SCALE_ZERO
         if (flags && status) atomicOr(status, flags);
     }
 }
@@ -111,7 +139,7 @@ __global__ __launch_bounds__(256) void prepare_kernel(const uint4* __restrict__ 
                                                       const uint16_t* __restrict__ scales,
                                                       const uint8_t* __restrict__ zeros,
                                                       int64_t n_vec, int64_t n_rows, int64_t kg,
-                                                      uint4* __restrict__ out_words,
+                                                      int zero4, uint4* __restrict__ out_words,
                                                       uint32_t* __restrict__ out_sz) {
     const int64_t n_words = (n_rows + 3) / 4 * 4 * kg;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -132,7 +160,9 @@ __global__ __launch_bounds__(256) void prepare_kernel(const uint4* __restrict__ 
         uint32_t v = 0;
         if (row < n_rows) {
             const int64_t src = row * kg + g;
-            v = (uint32_t)scales[src] | ((((uint32_t)zeros[src] + 128u) & 0xFFu) << 16);
+            const uint32_t z = zero4 ? ((uint32_t)zeros[src >> 1] >> (4 * (src & 1))) & 0xFu
+                                     : (uint32_t)zeros[src];
+            v = (uint32_t)scales[src] | (((z + 128u) & 0xFFu) << 16);
         }
         out_sz[i] = v;
     }
@@ -141,7 +171,7 @@ __global__ __launch_bounds__(256) void prepare_kernel(const uint4* __restrict__ 
 __global__ __launch_bounds__(256) void unprepare_kernel(const uint4* __restrict__ words,
                                                         const uint32_t* __restrict__ sz,
                                                         int64_t n_vec, int64_t n_rows, int64_t kg,
-                                                        uint4* __restrict__ packed,
+                                                        int zero4, uint4* __restrict__ packed,
                                                         uint16_t* __restrict__ scales,
                                                         uint8_t* __restrict__ zeros) {
     const int64_t n_groups = n_rows * kg;
@@ -154,11 +184,24 @@ __global__ __launch_bounds__(256) void unprepare_kernel(const uint4* __restrict_
         w.w = to_canonical_word(w.w);
         packed[i] = w;
     }
+    auto zero_of = [&](int64_t i) {
+        const int64_t row = i / kg;
+        return (((sz[sz_index(row, i - row * kg, kg)] >> 16) - 128u) & 0xFFu);
+    };
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_groups; i += stride) {
         const int64_t row = i / kg;
         const uint32_t v = sz[sz_index(row, i - row * kg, kg)];
         scales[i] = (uint16_t)(v & 0xFFFFu);
-        zeros[i] = (uint8_t)(((v >> 16) - 128u) & 0xFFu);
+        if (!zero4) zeros[i] = (uint8_t)(((v >> 16) - 128u) & 0xFFu);
+    }
+    if (zero4) {
+        // one thread per byte: groups 2i and 2i+1
+        const int64_t n_bytes = (n_groups + 1) / 2;
+        for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_bytes; i += stride) {
+            uint32_t b = zero_of(2 * i) & 0xFu;
+            if (2 * i + 1 < n_groups) b |= (zero_of(2 * i + 1) & 0xFu) << 4;
+            zeros[i] = (uint8_t)b;
+        }
     }
 }
 
@@ -171,39 +214,49 @@ int64_t elementwise_blocks(int64_t work) {
 
 }  // namespace
 
-hipError_t launch_quantize(const void* W, bool bf16, bool symmetric, int64_t n_groups,
+hipError_t launch_quantize(const void* W, bool bf16, const Fmt& f, int64_t n_groups,
                            uint8_t* packed, uint16_t* scales, uint8_t* zeros, uint32_t* status,
                            hipStream_t s) {
-    const int64_t blocks = (n_groups + 7) / 8;
+    const int lpg = f.group / 4;
+    const int64_t blocks = (n_groups + (256 / lpg) - 1) / (256 / lpg);
     uint16_t* p16 = reinterpret_cast<uint16_t*>(packed);
-    auto kern = bf16 ? (symmetric ? quantize_kernel<true, true> : quantize_kernel<true, false>)
-                     : (symmetric ? quantize_kernel<false, true> : quantize_kernel<false, false>);
-    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, s, W, n_groups, p16, scales,
-                       zeros, status);
-    return hipGetLastError();
+#define W4_Q(LPG)                                                                              \
+    if (lpg == LPG) {                                                                          \
+        auto kern = bf16 ? (f.symmetric ? quantize_kernel<true, true, LPG>                     \
+                                        : quantize_kernel<true, false, LPG>)                   \
+                         : (f.symmetric ? quantize_kernel<false, true, LPG>                    \
+                                        : quantize_kernel<false, false, LPG>);                 \
+        hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, s, W, n_groups, p16,    \
+                           scales, zeros, status, f.scale_bf16 ? 1 : 0, f.zero4 ? 1 : 0);      \
+        return hipGetLastError();                                                              \
+    }
+    W4_Q(32) W4_Q(16) W4_Q(8)
+#undef W4_Q
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_prepare(const uint8_t* packed, const uint16_t* scales, const uint8_t* zeros,
-                          int64_t n, int64_t k, uint8_t* prepared, hipStream_t s) {
+                          int64_t n, int64_t k, const Fmt& f, uint8_t* prepared, hipStream_t s) {
     const int64_t n_vec = packed_bytes(n, k) / 16;
-    const int64_t n_words = sz_words(n, k);
+    const int64_t n_words = sz_words_g(n, k, f.group);
     const int64_t blocks = elementwise_blocks(n_vec > n_words ? n_vec : n_words);
     hipLaunchKernelGGL(prepare_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
-                       reinterpret_cast<const uint4*>(packed), scales, zeros, n_vec, n, k / kGroup,
-                       reinterpret_cast<uint4*>(prepared),
+                       reinterpret_cast<const uint4*>(packed), scales, zeros, n_vec, n, k / f.group,
+                       f.zero4 ? 1 : 0, reinterpret_cast<uint4*>(prepared),
                        reinterpret_cast<uint32_t*>(prepared + sz_offset(n, k)));
     return hipGetLastError();
 }
 
-hipError_t launch_unprepare(const uint8_t* prepared, int64_t n, int64_t k, uint8_t* packed,
-                            uint16_t* scales, uint8_t* zeros, hipStream_t s) {
+hipError_t launch_unprepare(const uint8_t* prepared, int64_t n, int64_t k, const Fmt& f,
+                            uint8_t* packed, uint16_t* scales, uint8_t* zeros, hipStream_t s) {
     const int64_t n_vec = packed_bytes(n, k) / 16;
-    const int64_t n_groups = n * (k / kGroup);
+    const int64_t n_groups = n * (k / f.group);
     const int64_t blocks = elementwise_blocks(n_vec > n_groups ? n_vec : n_groups);
     hipLaunchKernelGGL(unprepare_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
                        reinterpret_cast<const uint4*>(prepared),
-                       reinterpret_cast<const uint32_t*>(prepared + sz_offset(n, k)), n_vec,
-                       n, k / kGroup, reinterpret_cast<uint4*>(packed), scales, zeros);
+                       reinterpret_cast<const uint32_t*>(prepared + sz_offset(n, k)), n_vec, n,
+                       k / f.group, f.zero4 ? 1 : 0, reinterpret_cast<uint4*>(packed), scales,
+                       zeros);
     return hipGetLastError();
 }
 

@@ -18,16 +18,20 @@ from . import W4_BF16, W4_F32, W4Error, lib, w4_chain_plan, w4_chain_run, w4_cha
 
 @dataclass
 class GemvCall:
-    prepared: object   # uint8 tensor from w4_prepare
+    prepared: object   # uint8 tensor from w4_prepare (or w4_prepare_fmt)
     n: int
     k: int
     x: object          # [M, K] bf16 or f32 tensor
     y: object          # [M, N] f32 or bf16 tensor
+    fmt: object = None  # W4Format of the prepared layout; None: the canonical format
 
     def algorithmic_bytes(self) -> int:
-        """Bytes the method must move: codes, fp16 scales, byte zeros, activations, outputs."""
+        """Bytes the method must move: codes, scales and zeros as the format stores them
+        (canonical: fp16 scales and byte zeros per 128 inputs), activations, outputs."""
         m = self.x.shape[0]
-        return (self.n * self.k // 2 + (self.n * self.k // 128) * 3
+        group, zero_bits = (128, 8) if self.fmt is None else (self.fmt.group, self.fmt.zero_bits)
+        groups = self.n * self.k // group
+        return (self.n * self.k // 2 + groups * 2 + (groups * zero_bits + 7) // 8
                 + m * self.k * self.x.element_size() + m * self.n * self.y.element_size())
 
 
@@ -37,16 +41,19 @@ class DecodeStep:
         self.calls = calls
         self._graph = None
         L = lib()
-        self._fn = L.w4_gemv
         self._args = []
         for c in calls:
             if c.x.shape[1] != c.k or c.y.shape != (c.x.shape[0], c.n):
                 raise ValueError("inconsistent GEMV shapes")
             xt = W4_F32 if c.x.dtype == torch.float32 else W4_BF16
             yt = W4_F32 if c.y.dtype == torch.float32 else W4_BF16
-            self._args.append((ctypes.c_void_p(c.prepared.data_ptr()), c.n, c.k,
-                               ctypes.c_void_p(c.x.data_ptr()), xt, c.x.shape[0],
-                               ctypes.c_void_p(c.y.data_ptr()), yt))
+            head = (ctypes.c_void_p(c.prepared.data_ptr()), c.n, c.k)
+            tail = (ctypes.c_void_p(c.x.data_ptr()), xt, c.x.shape[0],
+                    ctypes.c_void_p(c.y.data_ptr()), yt)
+            if c.fmt is None:
+                self._args.append((L.w4_gemv, "w4_gemv", head + tail))
+            else:
+                self._args.append((L.w4_gemv_fmt, "w4_gemv_fmt", head + (ctypes.byref(c.fmt),) + tail))
 
     def algorithmic_bytes(self) -> int:
         return sum(c.algorithmic_bytes() for c in self.calls)
@@ -54,11 +61,10 @@ class DecodeStep:
     def run_eager(self) -> None:
         import torch
         s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-        fn = self._fn
-        for a in self._args:
+        for fn, name, a in self._args:
             st = fn(*a, s)
             if st != 0:
-                raise W4Error(st, "w4_gemv")
+                raise W4Error(st, name)
 
     def capture(self) -> None:
         """Record the whole step once into a graph (replayed by run())."""

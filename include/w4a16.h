@@ -137,6 +137,72 @@ w4_status w4_gemv(const void* prepared, int64_t N, int64_t K,
                   void* y, w4_dtype yt, hipStream_t stream);
 
 /*
+ * Storage variants of the format (page "Quantization" › "Code": int4 groups of 128
+ * and of 32; page "Weight quantization" › "Implementation notes": scales kept in fp16
+ * or bf16; "Code" and "Complexity and constants": a 4-bit zero per group).
+ *   group       32, 64 or 128 consecutive inputs of one row share a scale and a zero.
+ *   scale_bf16  0: scales are binary16 bit patterns; 1: bfloat16 bit patterns.  Either
+ *               is the binary32 step rounded to nearest even.
+ *   zero_bits   8: zeros [N, K/group] bytes; 4: two zeros per byte over the flat
+ *               [N, K/group] array (index i at byte i/2, even index in the low nibble),
+ *               ceil(N*K/group / 2) bytes.
+ *   symmetric   0: the asymmetric method of w4_quantize; 1: that of
+ *               w4_quantize_symmetric (zero 8).
+ * The codes and the binary32 step do not depend on the storage; {128, 0, 8, 0} is the
+ * canonical format of w4_quantize and {128, 0, 8, 1} that of w4_quantize_symmetric.
+ * The prepared layout of a format with group 128 and binary16 scales is the canonical
+ * one (zeros are widened to the kernel's byte), so w4_gemv and w4_gemm take it; other
+ * formats are read by w4_gemv_fmt only.  A format outside these values is refused with
+ * W4_ERR_UNSUPPORTED.
+ */
+typedef struct {
+    int32_t group;
+    int32_t scale_bf16;
+    int32_t zero_bits;
+    int32_t symmetric;
+} w4_format;
+
+/* bytes of the zeros array of a format (0 for an invalid format or shape) */
+size_t w4_zeros_bytes(int64_t N, int64_t K, const w4_format* fmt);
+
+/*
+ * w4_quantize_fmt -- w4_quantize / w4_quantize_symmetric in format *fmt.
+ *   scales  out [N, K/group] 16-bit patterns of the format's scale type; 2-B aligned.
+ *   zeros   out, w4_zeros_bytes(N, K, fmt) bytes.
+ * Requires K % 128 == 0 (as every product does).  Other arguments, errors and d_status
+ * bits as w4_quantize; with bfloat16 scales W4_STATUS_SCALE_OVERFLOW / _ZERO refer to
+ * bfloat16 infinity / zero.
+ */
+w4_status w4_quantize_fmt(const void* W, w4_dtype wt, int64_t N, int64_t K,
+                          const w4_format* fmt, uint8_t* packed, uint16_t* scales,
+                          uint8_t* zeros, uint32_t* d_status, hipStream_t stream);
+
+/*
+ * w4_prepare_fmt / w4_unprepare_fmt -- the kernel layout of a format: the code region
+ * of w4_prepare followed by one scale/zero word per row and group (four rows of one
+ * group per 16 bytes).  Size w4_prepared_bytes_fmt(N, K, fmt); 256-B aligned.
+ * w4_unprepare_fmt is the exact inverse.
+ */
+size_t w4_prepared_bytes_fmt(int64_t N, int64_t K, const w4_format* fmt);
+w4_status w4_prepare_fmt(const uint8_t* packed, const uint16_t* scales, const uint8_t* zeros,
+                         int64_t N, int64_t K, const w4_format* fmt, void* prepared,
+                         size_t prepared_bytes, hipStream_t stream);
+w4_status w4_unprepare_fmt(const void* prepared, int64_t N, int64_t K, const w4_format* fmt,
+                           uint8_t* packed, uint16_t* scales, uint8_t* zeros,
+                           hipStream_t stream);
+
+/*
+ * w4_gemv_fmt -- w4_gemv on the prepared layout of format *fmt (page "Weight
+ * quantization", "How it works": scale * (sum code*x - zero * sum x) per group).  The
+ * canonical-layout formats (group 128, binary16 scales) take w4_gemv's kernels; the
+ * others run on its one-row (VALU) kernel at every M, in steps of up to four rows of x.
+ * Arguments, limits and errors as w4_gemv.
+ */
+w4_status w4_gemv_fmt(const void* prepared, int64_t N, int64_t K, const w4_format* fmt,
+                      const void* x, w4_dtype xt, int64_t M,
+                      void* y, w4_dtype yt, hipStream_t stream);
+
+/*
  * w4_gemm -- prefill-sized product Y[M, N] = X[M, K] * w_hat^T for any M >= 1
  * (page "LLM Quantization Architecture in Depth" › "Why fewer bits make
  * decoding faster": prefill is compute bound and weight-only formats must turn

@@ -83,3 +83,45 @@ def test_python_layer_rejects_cpu_tensors():
         w4.w4_quantize(torch.zeros(4, 128))
     with pytest.raises(ValueError):
         w4.w4_quantize_symmetric(torch.zeros(4, 128))
+
+
+def test_format_sizes_closed_form():
+    F = w4.W4Format.make
+    # group 32: K/32 scale/zero words per row, rows padded to four
+    assert w4.w4_prepared_bytes_fmt(8192, 8192, F(32)) == 8192 * 4096 + 8192 * 256 * 4
+    assert w4.w4_prepared_bytes_fmt(5, 256, F(64, True, 4)) == 768 + 8 * 4 * 4
+    # group 128 with binary16 scales is the canonical layout, whatever the zeros
+    assert w4.w4_prepared_bytes_fmt(3, 384, F(128, False, 4, True)) == w4.w4_prepared_bytes(3, 384)
+    assert w4.w4_zeros_bytes(5, 256, F(32, True, 4)) == 20        # 40 groups, two per byte
+    assert w4.w4_zeros_bytes(3, 128, F(128, False, 4)) == 2       # 3 groups -> 2 bytes
+    assert w4.w4_zeros_bytes(3, 128, F(128)) == 3
+    for bad in (F(16), F(256), F(128, False, 6), w4.W4Format(128, 2, 8, 0), w4.W4Format(128, 0, 8, 3)):
+        assert w4.w4_zeros_bytes(4, 256, bad) == 0
+        assert w4.w4_prepared_bytes_fmt(4, 256, bad) == 0
+    assert w4.w4_prepared_bytes_fmt(4, 96, F(32)) == 0            # K must be a multiple of 128
+
+
+def test_format_entry_points_validate_before_device_work():
+    L = w4.lib()
+    s = NULL
+    ok = ctypes.byref(w4.W4Format.make(32, True, 4, False))
+    bad = ctypes.byref(w4.W4Format.make(48))
+    fnull = ctypes.POINTER(w4.W4Format)()
+    # the format itself: missing, then outside the supported values
+    assert L.w4_quantize_fmt(_fake(), 0, 4, 128, fnull, _fake(), _fake(), _fake(), NULL, s) == 1
+    assert L.w4_quantize_fmt(_fake(), 0, 4, 128, bad, _fake(), _fake(), _fake(), NULL, s) == 5
+    assert L.w4_prepare_fmt(_fake(), _fake(), _fake(), 4, 128, bad, _fake(), 1 << 20, s) == 5
+    assert L.w4_unprepare_fmt(_fake(), 4, 128, bad, _fake(), _fake(), _fake(), s) == 5
+    assert L.w4_gemv_fmt(_fake(), 4, 128, bad, _fake(), 1, 1, _fake(), 0, s) == 5
+    # then the same checks as the canonical entry points
+    assert L.w4_quantize_fmt(NULL, 0, 4, 128, ok, _fake(), _fake(), _fake(), NULL, s) == 1
+    assert L.w4_quantize_fmt(_fake(), 7, 4, 128, ok, _fake(), _fake(), _fake(), NULL, s) == 4
+    assert L.w4_quantize_fmt(_fake(), 0, 4, 96, ok, _fake(), _fake(), _fake(), NULL, s) == 2
+    assert L.w4_quantize_fmt(_fake(0x100004), 0, 4, 128, ok, _fake(), _fake(), _fake(), NULL, s) == 3
+    assert L.w4_prepare_fmt(_fake(), _fake(), _fake(), 4, 128, ok, _fake(), 10, s) == 9
+    assert L.w4_gemv_fmt(_fake(), 4, 128, ok, _fake(), 1, 17, _fake(), 0, s) == 2
+    assert L.w4_gemv_fmt(_fake(), 4, 128, ok, _fake(), 5, 1, _fake(), 0, s) == 4
+    assert L.w4_gemv_fmt(_fake(0x100010), 4, 128, ok, _fake(), 1, 1, _fake(), 0, s) == 3
+    # a canonical-layout format goes through w4_gemv's own checks
+    canon = ctypes.byref(w4.W4Format.make(128, False, 4, True))
+    assert L.w4_gemv_fmt(_fake(), 4, 128, canon, _fake(), 1, 0, _fake(), 0, s) == 2
