@@ -36,7 +36,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 # counter reads for a 256 MiB device copy (FETCH_SIZE x2, WRITE_SIZE x1); average of the four
 # launches of a layer (qkv, o, gate_up, down).  Source: the profile summary
 # profiles/w4_gemv_llama70b_fused_step_hbm_traffic.md
-GEMV_STEP_TRAFFIC_BYTES_PER_LAUNCH = 114034481
+GEMV_STEP_TRAFFIC_BYTES_PER_LAUNCH = 114039772
 BF16_DENSE_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 METRIC = "W4A16 g128 GEMV achieved HBM GB/s (% of peak), 70B layer shapes, batch 1"
 

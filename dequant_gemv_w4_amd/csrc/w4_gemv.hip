@@ -19,6 +19,8 @@
 //     there), so step c computes while the later steps are still arriving and
 //     the compiler's in-order wait counts stay exact (no load crosses a loop
 //     iteration);
+//   * groups of up to eight waves end the launch with a round of workgroups that take
+//     half the rows of the others, which shortens the tail of the weight stream;
 //   * the scale/zero words of the four rows of a step are one 16-byte load;
 //   * unpack: v_and_or_b32((word >> 4j), 0x000F000F, 0x43004300) turns the two
 //     codes of an input pair into the bf16 values 128+q, and v_dot2_f32_bf16
@@ -114,7 +116,8 @@ __global__ __launch_bounds__(MAXT) void gemv_kernel(const u32x4_t* __restrict__ 
                                                     const u32x4_t* __restrict__ sz4,
                                                     const void* __restrict__ xv,
                                                     void* __restrict__ yv, int y_bf16, int N,
-                                                    int K, int M, int rows_per_wg, int gshift) {
+                                                    int K, int M, int rows_per_wg, int gshift,
+                                                    int tail_first, int tail_rows) {
     constexpr int XE = XF32 ? 2 * MT : MT;  // bf16 operand rows
     constexpr int R = kRowsPerStep;
     extern __shared__ float red[];          // [waves][rows_per_wg][XE]
@@ -125,7 +128,13 @@ __global__ __launch_bounds__(MAXT) void gemv_kernel(const u32x4_t* __restrict__ 
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int n_waves = T >> 6;
-    const int r0 = blockIdx.x * rows_per_wg;
+    // workgroups from tail_first on (the last ones dispatched) take tail_rows rows each, so
+    // the launch ends on short workgroups; rows_per_wg is the LDS row stride of both kinds
+    const int row_stride = rows_per_wg;
+    const bool in_tail = (int)blockIdx.x >= tail_first;
+    const int r0 = in_tail ? tail_first * rows_per_wg + ((int)blockIdx.x - tail_first) * tail_rows
+                           : (int)blockIdx.x * rows_per_wg;
+    if (in_tail) rows_per_wg = tail_rows;
     const int r_end = min(N, r0 + rows_per_wg);
 
     // slice j of this lane is threadIdx.x + j*T (16 bytes of every row).  With a ragged
@@ -263,7 +272,7 @@ __global__ __launch_bounds__(MAXT) void gemv_kernel(const u32x4_t* __restrict__ 
 #pragma unroll
             for (int e = 0; e < XE; ++e) {
                 const float k = reduce4(acc[0][e], acc[1][e], acc[2][e], acc[3][e]);
-                if ((lane & 15) == 0) red[(wave * rows_per_wg + rbase + (lane >> 4)) * XE + e] = k;
+                if ((lane & 15) == 0) red[(wave * row_stride + rbase + (lane >> 4)) * XE + e] = k;
             }
         }
     };
@@ -287,7 +296,7 @@ __global__ __launch_bounds__(MAXT) void gemv_kernel(const u32x4_t* __restrict__ 
         if (m >= M) continue;
         float v = 0.0f;
         for (int w = 0; w < n_waves; ++w) {
-            const float* p = red + (w * rows_per_wg + rloc) * XE;
+            const float* p = red + (w * row_stride + rloc) * XE;
             if constexpr (XF32)
                 v += p[2 * m] + p[2 * m + 1];
             else
@@ -369,10 +378,32 @@ hipError_t launch_var(GemvArgs a, dim3 block, hipStream_t s) {
     static std::atomic<int> cache[17];
     auto kern = gemv_kernel<MT, XF32, SPT, MAXT, CH, RAGGED, SBF16>;
     a.rows = rows_for(kern, (int)block.x, a.n, XE, CH * kRowsPerStep, cache);
-    const dim3 grid((unsigned)((a.n + a.rows - 1) / a.rows));
+    unsigned wgs = (unsigned)((a.n + a.rows - 1) / a.rows);
+    // A short last round: the last round of resident workgroups takes 1/tail of the rows.
+    // Workgroups start in index order as earlier ones finish, so the final ones otherwise
+    // start late with a full share and stream alone at the end.  Measured on MI355X
+    // (57344x8192 at M = 1): 38.3-38.4 us against 39.5-40.0 us; the one-round 14-wave
+    // groups of K ~ 28K run slower with it, so they keep equal shares.
+    int tail_first = (int)wgs, tail_rows = a.rows;
+    static const int tail_env = env_int("W4A16_GEMV_TAIL", -1);
+    const int tail = tail_env >= 0 ? tail_env : (block.x <= 512 ? 2 : 0);
+    static const int tail_rounds = env_int("W4A16_GEMV_TAILROUNDS", 1);
+    const int half = tail > 0 ? a.rows / tail : 0;
+    if (tail > 1 && half * tail == a.rows && half >= CH * kRowsPerStep && half % (CH * kRowsPerStep) == 0) {
+        const long round = (long)cache[block.x / 64].load(std::memory_order_relaxed) * compute_units();
+        const long tail_rows_total = round * tail_rounds * half;
+        const long main_wgs = ((long)a.n - tail_rows_total) / a.rows;
+        if (main_wgs > 0) {
+            tail_first = (int)main_wgs;
+            tail_rows = half;
+            const long rest = (long)a.n - main_wgs * a.rows;
+            wgs = (unsigned)(main_wgs + (rest + half - 1) / half);
+        }
+    }
+    const dim3 grid(wgs);
     const size_t shmem = (size_t)(block.x / 64) * a.rows * XE * sizeof(float);
     hipLaunchKernelGGL(kern, grid, block, shmem, s, a.wq, a.sz4, a.x, a.y, a.y_bf16, a.n, a.k, a.m,
-                       a.rows, a.gshift);
+                       a.rows, a.gshift, tail_first, tail_rows);
     return hipGetLastError();
 }
 
