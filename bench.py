@@ -179,6 +179,61 @@ def per_shape(prepared, layers: int, dev: str, reps: int = 3, fused: bool = Fals
     return out
 
 
+def read_ceiling(prepared, layers: int, dev: str, step_ms: float, reps: int = 10):
+    """What a kernel that only reads achieves (w4_stream_read, a plain streaming read).
+
+    ``stream``: one 4 GiB buffer read start to end.  ``step_pattern``: every prepared matrix
+    of the step read once, in the step's order, as one launch each from one graph: the
+    same bytes (layout padding included) in the same launch pattern as the GEMV step, so
+    ``gemv_step_vs_pattern`` (pattern time / GEMV step time) says how close the products
+    come to a pure read.
+    """
+    import torch
+
+    import dequant_gemv_w4_amd as w4
+    import synth
+
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    big = torch.zeros(4 << 30, dtype=torch.uint8, device=dev)
+    for _ in range(2):
+        w4.w4_stream_read(big, sink)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        w4.w4_stream_read(big, sink)
+    end.record()
+    end.synchronize()
+    stream_gbs = big.numel() * reps / (start.elapsed_time(end) * 1e-3) / 1e9
+    del big
+    torch.cuda.empty_cache()
+
+    bufs = [prepared[(layer, name)] for layer in range(layers) for name in synth.FUSED_ORDER]
+    for b in bufs:
+        w4.w4_stream_read(b, sink)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for b in bufs:
+            w4.w4_stream_read(b, sink)
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(reps):
+        g.replay()
+    end.record()
+    end.synchronize()
+    ms = start.elapsed_time(end) / reps
+    nbytes = sum(b.numel() for b in bufs)
+    return {"stream_GB/s": round(stream_gbs, 1),
+            "stream_pct_of_hbm_peak": round(100 * stream_gbs / HBM_PEAK_GBS, 2),
+            "step_pattern_ms": round(ms, 4), "step_pattern_bytes": int(nbytes),
+            "step_pattern_GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "gemv_step_vs_pattern": round(ms / step_ms, 4)}
+
+
 def page_layer(dev: str, reps: int = 5, copies: int = 64):
     """The page's single layer: W 4096x4096 and binary32 x from its xorshift draws, M=1.
 
@@ -464,6 +519,8 @@ def main() -> int:
             log(f"M={m}: {msm:.3f} ms/step")
         result["batch_sweep_fused"] = batches
         result["per_shape_fused_m1"] = per_shape(prepared, args.layers, dev, fused=True)
+        result["read_ceiling"] = read_ceiling(prepared, args.layers, dev, ms)
+        log(f"read ceiling: {result['read_ceiling']}")
         del step, prepared
         torch.cuda.empty_cache()
         log("building the unfused stack")

@@ -18,7 +18,7 @@ __all__ = [
     "W4Error", "lib", "declared_symbols",
     "w4_quantize", "w4_quantize_symmetric", "w4_prepared_bytes", "w4_prepare", "w4_unprepare",
     "w4_gemv", "w4_gemm_workspace_bytes", "w4_gemm",
-    "w4_status_string", "w4_last_hip_error", "w4_format_version",
+    "w4_status_string", "w4_last_hip_error", "w4_format_version", "w4_stream_read",
     "W4ChainGemv", "w4_chain_plan_bytes", "w4_chain_workspace_bytes", "w4_chain_plan",
     "w4_chain_run",
     "W4Format", "w4_zeros_bytes", "w4_quantize_fmt", "w4_prepared_bytes_fmt", "w4_prepare_fmt",
@@ -96,6 +96,8 @@ def lib() -> ctypes.CDLL:
     L.w4_last_hip_error.restype = ctypes.c_char_p
     L.w4_format_version.argtypes = []
     L.w4_format_version.restype = i32
+    L.w4_stream_read.argtypes = [vp, sz, vp, vp]
+    L.w4_stream_read.restype = i32
     L.w4_chain_plan_bytes.argtypes = [i64]
     L.w4_chain_plan_bytes.restype = sz
     L.w4_chain_workspace_bytes.argtypes = [i64]
@@ -176,6 +178,17 @@ def w4_last_hip_error() -> str:
 
 def w4_format_version() -> int:
     return int(lib().w4_format_version())
+
+
+def w4_stream_read(buf, sink) -> None:
+    """Measurement probe: read every byte of the device tensor ``buf`` once and discard it
+    (``sink``: an int32 device tensor the kernel may overwrite)."""
+    import torch
+    _require(sink, torch.int32, None, "sink")
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    _check(lib().w4_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                _stream(buf)), "w4_stream_read")
 
 
 def w4_prepared_bytes(N: int, K: int) -> int:

@@ -381,4 +381,14 @@ w4_status w4_chain_run(const void* plan_dev, const void* plan_host, void* worksp
     return e == hipSuccess ? W4_OK : hip_fail(e);
 }
 
+w4_status w4_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream) {
+    if (!buf || !sink) return W4_ERR_NULL;
+    if (bytes == 0 || bytes % 16 != 0) return W4_ERR_SHAPE;
+    if (!aligned(buf, 16) || !aligned(sink, 4)) return W4_ERR_ALIGN;
+    w4_status st = check_arch();
+    if (st != W4_OK) return st;
+    hipError_t e = w4::launch_stream_read(buf, (int64_t)bytes, sink, stream);
+    return e == hipSuccess ? W4_OK : hip_fail(e);
+}
+
 }  // extern "C"

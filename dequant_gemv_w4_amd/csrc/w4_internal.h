@@ -137,6 +137,7 @@ hipError_t launch_gemv_mfma(const uint8_t* prepared, int64_t n, int64_t k, const
 // workgroup when one workgroup runs per compute unit.
 bool gemv_ring_takes(int64_t n, int64_t k);
 size_t gemm_workspace(int64_t m, int64_t k);
+hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t s);
 hipError_t launch_gemm(const uint8_t* prepared, int64_t n, int64_t k, const void* X, int64_t m,
                        void* Y, bool y_bf16, void* workspace, hipStream_t s);
 

@@ -263,6 +263,19 @@ w4_status w4_chain_plan(const w4_chain_gemv* gemvs, int64_t count, void* plan_ho
 w4_status w4_chain_run(const void* plan_dev, const void* plan_host, void* workspace,
                        size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * w4_stream_read -- measurement probe, not part of the method: reads `bytes` bytes of
+ * device memory at `buf` once with plain streaming loads (8192 workgroups, each a
+ * contiguous share, non-temporal 16-byte loads) and discards them, so a product's rate
+ * can be compared with a kernel that only reads the same bytes in the same launch
+ * pattern (page "Weight quantization", "Complexity and constants": decode time is bytes
+ * read / bandwidth).
+ *   buf   device memory, 16-B aligned; bytes a non-zero multiple of 16.
+ *   sink  a device word the kernel may overwrite (it almost never does); 4-B aligned.
+ * Errors: W4_ERR_NULL, W4_ERR_SHAPE, W4_ERR_ALIGN, W4_ERR_ARCH, W4_ERR_HIP.
+ */
+w4_status w4_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 /* Text of a status code (static storage). */
 const char* w4_status_string(w4_status s);
 /* Message of the last W4_ERR_HIP on the calling thread ("" if none). */

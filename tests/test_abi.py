@@ -125,3 +125,14 @@ def test_format_entry_points_validate_before_device_work():
     # a canonical-layout format goes through w4_gemv's own checks
     canon = ctypes.byref(w4.W4Format.make(128, False, 4, True))
     assert L.w4_gemv_fmt(_fake(), 4, 128, canon, _fake(), 1, 0, _fake(), 0, s) == 2
+
+
+def test_stream_read_validates_before_device_work():
+    L = w4.lib()
+    s = NULL
+    assert L.w4_stream_read(NULL, 1024, _fake(), s) == 1
+    assert L.w4_stream_read(_fake(), 1024, NULL, s) == 1
+    assert L.w4_stream_read(_fake(), 0, _fake(), s) == 2
+    assert L.w4_stream_read(_fake(), 1000, _fake(), s) == 2
+    assert L.w4_stream_read(_fake(0x100008), 1024, _fake(), s) == 3
+    assert L.w4_stream_read(_fake(), 1024, _fake(0x100002), s) == 3

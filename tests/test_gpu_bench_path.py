@@ -53,3 +53,16 @@ def test_bench_step_sampled_rows_against_oracle():
             worst = max(worst, r)
         print(f"M={m}: worst err/bound {worst:.3e}")
         del step
+
+
+def test_stream_read_probe_reads_without_writing():
+    # the bandwidth probe leaves its sink alone unless the folded words equal its fixed
+    # word; a zero buffer folds to 0, and a ragged size (not a multiple of the share)
+    # must read in bounds
+    import dequant_gemv_w4_amd as w4
+    sink = torch.full((1,), 7, dtype=torch.int32, device=DEV)
+    for nbytes in (16, 4096 * 16 + 48, 3 << 20):
+        buf = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+        w4.w4_stream_read(buf, sink)
+        torch.cuda.synchronize()
+        assert int(sink.item()) == 7

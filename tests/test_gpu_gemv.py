@@ -91,6 +91,31 @@ def test_llama70b_layer_batches_sampled_rows(matrix):
         print(f"{matrix} M={m}: worst err/bound {r:.3e}")
 
 
+def test_short_last_round_rows():
+    # 57344 x 8192 at M = 1, 2 (bf16 x) and M = 1 (binary32 x): the one-row kernel's last
+    # round of workgroups takes half the rows of the others.  Dense windows around where the
+    # short workgroups begin (row 45056 at 16 + 8 rows per workgroup on 256 CUs) and at the
+    # end, plus random rows, against the oracle.
+    n, k = 57344, 8192
+    W = synth.normal_weights(n, k, 2024, DEV)
+    prep, _ = _quant_prepare(W)
+    rng = np.random.default_rng(31)
+    rows = np.unique(np.concatenate([np.arange(44800, 45312), np.arange(n - 256, n),
+                                     rng.choice(n, 64, replace=False)]))
+    W32 = to_np32(W[torch.from_numpy(rows).to(DEV)])
+    del W
+    p, s, z = oracle.quantize_ref(W32)
+    x16 = synth.normal_activations(2, k, 2025, DEV)
+    x32 = torch.from_numpy(to_np32(x16[:1])).to(DEV) * 0.5 + 0.1234567
+    for x in (x16[:1].contiguous(), x16, x32):
+        m = x.shape[0]
+        y = to_np32(_run(prep, n, k, x))
+        xr = to_np32(x)
+        r = assert_within(y[:, rows], oracle.gemv_ref(p, s, z, xr), oracle.tolerance_ref(p, s, z, xr),
+                          f"57344x8192 M={m} {x.dtype}")
+        print(f"M={m} {x.dtype}: worst err/bound {r:.3e}")
+
+
 @pytest.mark.parametrize("n,k,m", [(1, 128, 1), (5, 256, 16), (1000, 384, 2), (77, 11008, 1),
                                    (64, 32768, 1), (64, 32768, 5), (4099, 2048, 8),
                                    (77, 11008, 4), (130, 16512, 2), (33, 16512, 3),
