@@ -12,3 +12,7 @@ from .w4_formats import (  # noqa: F401
     unpack_zero_nibbles, zero_bytes, quantize_format_ref, zeros_u8, dequant_format_ref,
     gemv_format_ref, tolerance_format_ref, format_bits_per_weight, format_bytes,
 )
+from .fp8_oracle import (  # noqa: F401
+    FP8_MAX, E4M3_VALUES, e4m3_decode, e4m3_encode, quantize_rows_fp8_ref, dequant_fp8_ref,
+    gemm_fp8_ref, tolerance_fp8_ref,
+)
