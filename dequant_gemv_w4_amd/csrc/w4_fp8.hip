@@ -1,0 +1,258 @@
+// W8A8 in FP8 E4M3 for prefill: per-row quantization and the product on the matrix cores.
+//
+// Prefill is bound by the matrix units, so a weight-only format barely speeds it up; the
+// arithmetic itself has to be narrower, with activations quantized too: W8A8 in FP8 or
+// INT8 (page "LLM Quantization Architecture in Depth" › "Why fewer bits make decoding
+// faster" and "Number formats, scales and granularity": E4M3 for weights and activations,
+// largest value 448; dynamic per-token activation scales).
+//
+// Quantization (fp8_quantize_rows_kernel, one workgroup per row): the row's largest
+// magnitude over 448 is the scale (1 for an all-zero row), both in binary64 as in the
+// page's program ("Quantization" › "Code": FP8 E4M3 per-channel, rounding to 3 mantissa
+// bits with subnormals, largest value 448); each value divided by the scale in binary64 is
+// capped at 448 and rounded, halves to even, on the grid of 3 mantissa bits of its binary
+// exponent (exponents below -6 use the grid of -6).  Codes are OCP E4M3 bytes (sign,
+// exponent with bias 7, mantissa), the byte the gfx950 matrix cores take as format 0; a
+// value that rounds to zero keeps its sign.  The scale is stored as binary32.
+//
+// Product (fp8_gemm_kernel): Y[m, n] = sx[m] * sw[n] * sum_k qx[m, k] * qw[n, k] with
+// v_mfma_scale_f32_32x32x64_f8f6f4 (block scales left at 2^0), binary32 accumulation;
+// every product of two E4M3 values is exact in binary32.  256 threads per 128 x 128
+// output tile, wave (wm, wn) owns 64 x 64 as 2 x 2 MFMA tiles; a K step is 128 inputs,
+// staged through registers into a double-buffered LDS tile (16-byte chunk c of row r at
+// slot c ^ (r & 7), so the operand reads of 32 rows spread over the banks).  A lane
+// supplies row (lane % 32) and the 32 inputs 32 * (lane / 32) .. +31 of a 64-input MFMA
+// step, the same inputs for both operands, so each output is a dot product over matching
+// inputs whatever order the unit sums them in.
+#include "w4_internal.h"
+
+namespace w4 {
+namespace {
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef int v8i_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kQT = 256;          // threads of a quantizer workgroup (one row)
+constexpr double kFp8Max = 448.0;
+
+// E4M3 byte of a binary64 quotient t (the rounding described at the top of the file)
+__device__ __forceinline__ uint32_t e4m3_byte(double t) {
+    if (t == 0.0) return 0u;
+    const uint32_t sign = t < 0.0 ? 0x80u : 0u;
+    const double mag = fmin(fabs(t), kFp8Max);
+    int e = 0;
+    (void)frexp(mag, &e);                          // mag = f * 2^e, f in [0.5, 1)
+    const int ex = max(e - 1, -6);
+    const double grid = ldexp(1.0, ex - 3);
+    const double r = fmin(rint(mag / grid) * grid, kFp8Max);
+    if (r == 0.0) return sign;
+    if (r < 0x1p-6) return sign | (uint32_t)(r * 512.0);   // subnormal: r = m * 2^-9
+    int E = 0;
+    const double f = frexp(r, &E);                 // r = (2f) * 2^(E-1)
+    return sign | ((uint32_t)(E + 6) << 3) | (uint32_t)((2.0 * f - 1.0) * 8.0);
+}
+
+template <bool IN_BF16>
+__device__ __forceinline__ void load8(const void* a, int64_t i, float (&v)[8]) {
+    if constexpr (IN_BF16) {
+        const u32x4_t w = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a) + i);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            v[2 * q] = __uint_as_float(w[q] << 16);
+            v[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+        }
+    } else {
+        const u32x4_t w0 = *reinterpret_cast<const u32x4_t*>(static_cast<const float*>(a) + i);
+        const u32x4_t w1 = *reinterpret_cast<const u32x4_t*>(static_cast<const float*>(a) + i + 4);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            v[q] = __uint_as_float(w0[q]);
+            v[4 + q] = __uint_as_float(w1[q]);
+        }
+    }
+}
+
+template <bool IN_BF16>
+__global__ __launch_bounds__(kQT) void fp8_quantize_rows_kernel(const void* __restrict__ a,
+                                                                int64_t K,
+                                                                uint8_t* __restrict__ codes,
+                                                                float* __restrict__ scales,
+                                                                uint32_t* __restrict__ status) {
+    __shared__ float wmax[kQT / 64];
+    const int64_t row = blockIdx.x;
+    const void* src = IN_BF16 ? (const void*)(static_cast<const uint16_t*>(a) + row * K)
+                              : (const void*)(static_cast<const float*>(a) + row * K);
+    float amax = 0.0f;
+    bool finite = true;
+    for (int64_t i = (int64_t)threadIdx.x * 8; i < K; i += kQT * 8) {
+        float v[8];
+        load8<IN_BF16>(src, i, v);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            finite &= isfinite(v[q]);
+            amax = fmaxf(amax, fabsf(v[q]));
+        }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = amax;
+    if (!finite && status) atomicOr(status, 1u);
+    __syncthreads();
+    amax = wmax[0];
+#pragma unroll
+    for (int w = 1; w < kQT / 64; ++w) amax = fmaxf(amax, wmax[w]);
+    const double s = amax == 0.0f ? 1.0 : (double)amax / kFp8Max;
+    if (threadIdx.x == 0) scales[row] = (float)s;
+    uint8_t* dst = codes + row * K;
+    for (int64_t i = (int64_t)threadIdx.x * 8; i < K; i += kQT * 8) {
+        float v[8];
+        load8<IN_BF16>(src, i, v);
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            lo |= e4m3_byte((double)v[q] / s) << (8 * q);
+            hi |= e4m3_byte((double)v[4 + q] / s) << (8 * q);
+        }
+        *reinterpret_cast<uint2*>(dst + i) = make_uint2(lo, hi);
+    }
+}
+
+constexpr int kFM = 128, kFN = 128, kFK = 128;  // output tile; K step (bytes = inputs)
+constexpr int kFT = 256;
+constexpr int kTileBytes = kFM * kFK;            // 16 KiB per operand and buffer
+
+__global__ __launch_bounds__(kFT) void fp8_gemm_kernel(const uint8_t* __restrict__ X,
+                                                       const float* __restrict__ sx,
+                                                       const uint8_t* __restrict__ W,
+                                                       const float* __restrict__ sw,
+                                                       void* __restrict__ Y, int y_bf16, int M,
+                                                       int N, int K, int tiles_n) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kTileBytes];  // [buffer][X, W]
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wm = wave >> 1;
+    const int wn = wave & 1;
+    const int m0 = (int)(blockIdx.x / tiles_n) * kFM;
+    const int n0 = (int)(blockIdx.x % tiles_n) * kFN;
+
+    // staging: chunk i = tid + 256 u of a tile is row i / 8, 16-byte chunk i % 8
+    const uint8_t* gx[4];
+    const uint8_t* gw[4];
+    uint32_t slot[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int i = tid + kFT * u;
+        const int r = i >> 3;
+        const int c = i & 7;
+        gx[u] = X + (int64_t)min(m0 + r, M - 1) * K + 16 * c;   // rows past M repeat M-1
+        gw[u] = W + (int64_t)min(n0 + r, N - 1) * K + 16 * c;
+        slot[u] = (uint32_t)(r * kFK + ((c ^ (r & 7)) << 4));
+    }
+    u32x4_t rx[4], rw[4];
+    auto load = [&](int kt) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            rx[u] = *reinterpret_cast<const u32x4_t*>(gx[u] + (int64_t)kt * kFK);
+            rw[u] = *reinterpret_cast<const u32x4_t*>(gw[u] + (int64_t)kt * kFK);
+        }
+    };
+    auto store = [&](int b) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            *reinterpret_cast<u32x4_t*>(&lds[b][0][slot[u]]) = rx[u];
+            *reinterpret_cast<u32x4_t*>(&lds[b][1][slot[u]]) = rw[u];
+        }
+    };
+    // the 32 inputs 64 kh + 32 (lane / 32) .. +31 of row r of operand tile t
+    auto operand = [&](int b, int t, int r, int kh) {
+        const int c0 = 4 * kh + 2 * (lane >> 5);
+        const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(&lds[b][t][r * kFK + ((c0 ^ (r & 7)) << 4)]);
+        const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(&lds[b][t][r * kFK + (((c0 + 1) ^ (r & 7)) << 4)]);
+        const v8i_t v = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                         (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        return v;
+    };
+
+    f32x16_t acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = (f32x16_t){};
+
+    const int Kt = K / kFK;
+    load(0);
+    store(0);
+    __syncthreads();
+    for (int kt = 0; kt < Kt; ++kt) {
+        const int b = kt & 1;
+        if (kt + 1 < Kt) load(kt + 1);   // in flight while this step computes
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+            v8i_t xa[2], wb[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) xa[i] = operand(b, 0, 64 * wm + 32 * i + (lane & 31), kh);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) wb[j] = operand(b, 1, 64 * wn + 32 * j + (lane & 31), kh);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    // formats 0 / 0: E4M3 for both operands; block scales 127 = 2^0
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        xa[i], wb[j], acc[i][j], 0, 0, 0, 127, 0, 127);
+        }
+        if (kt + 1 < Kt) store(b ^ 1);
+        __syncthreads();
+    }
+
+    // element v of a 32 x 32 result: column lane % 32, row 8 (v / 4) + 4 (lane / 32) + v % 4
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int c = n0 + 64 * wn + 32 * j + (lane & 31);
+            if (c >= N) continue;
+            const float scw = sw[c];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int r = m0 + 64 * wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                if (r >= M) continue;
+                const float y = acc[i][j][v] * sx[r] * scw;
+                const int64_t o = (int64_t)r * N + c;
+                if (y_bf16) {
+                    const uint32_t u = __float_as_uint(y);
+                    static_cast<uint16_t*>(Y)[o] = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+                } else {
+                    static_cast<float*>(Y)[o] = y;
+                }
+            }
+        }
+}
+
+}  // namespace
+
+hipError_t launch_fp8_quantize_rows(const void* a, bool bf16, int64_t rows, int64_t k,
+                                    uint8_t* codes, float* scales, uint32_t* status,
+                                    hipStream_t s) {
+    if (bf16)
+        hipLaunchKernelGGL(fp8_quantize_rows_kernel<true>, dim3((unsigned)rows), dim3(kQT), 0, s, a,
+                           k, codes, scales, status);
+    else
+        hipLaunchKernelGGL(fp8_quantize_rows_kernel<false>, dim3((unsigned)rows), dim3(kQT), 0, s,
+                           a, k, codes, scales, status);
+    return hipGetLastError();
+}
+
+hipError_t launch_fp8_gemm(const uint8_t* xq, const float* sx, int64_t m, const uint8_t* wq,
+                           const float* sw, int64_t n, int64_t k, void* y, bool y_bf16,
+                           hipStream_t s) {
+    const int tiles_n = (int)((n + kFN - 1) / kFN);
+    const int64_t tiles = ((m + kFM - 1) / kFM) * tiles_n;
+    hipLaunchKernelGGL(fp8_gemm_kernel, dim3((unsigned)tiles), dim3(kFT), 0, s, xq, sx, wq, sw, y,
+                       y_bf16 ? 1 : 0, (int)m, (int)n, (int)k, tiles_n);
+    return hipGetLastError();
+}
+
+}  // namespace w4

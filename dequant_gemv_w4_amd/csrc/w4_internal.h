@@ -138,6 +138,12 @@ hipError_t launch_gemv_mfma(const uint8_t* prepared, int64_t n, int64_t k, const
 bool gemv_ring_takes(int64_t n, int64_t k);
 size_t gemm_workspace(int64_t m, int64_t k);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t s);
+hipError_t launch_fp8_quantize_rows(const void* a, bool bf16, int64_t rows, int64_t k,
+                                    uint8_t* codes, float* scales, uint32_t* status,
+                                    hipStream_t s);
+hipError_t launch_fp8_gemm(const uint8_t* xq, const float* sx, int64_t m, const uint8_t* wq,
+                           const float* sw, int64_t n, int64_t k, void* y, bool y_bf16,
+                           hipStream_t s);
 hipError_t launch_gemm(const uint8_t* prepared, int64_t n, int64_t k, const void* X, int64_t m,
                        void* Y, bool y_bf16, void* workspace, hipStream_t s);
 

@@ -51,6 +51,7 @@ extern "C" {
 #define W4_FORMAT_VERSION 2
 #define W4_GEMV_MAX_M 16
 #define W4_GEMV_MAX_K 32768
+#define W4_FP8_MAX_K 65536
 
 typedef enum {
     W4_OK = 0,
@@ -262,6 +263,42 @@ w4_status w4_chain_plan(const w4_chain_gemv* gemvs, int64_t count, void* plan_ho
                         size_t plan_bytes);
 w4_status w4_chain_run(const void* plan_dev, const void* plan_host, void* workspace,
                        size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * W8A8 in FP8 E4M3 for prefill (page "LLM Quantization Architecture in Depth" › "Why fewer
+ * bits make decoding faster": prefill is compute bound, so its arithmetic must be narrower,
+ * with activations quantized too; › "Number formats, scales and granularity": E4M3, largest
+ * value 448, dynamic per-token activation scales; page "Quantization" › "Code": FP8 E4M3
+ * per-channel scaling, rounding to 3 mantissa bits with subnormals).
+ *
+ * w4_fp8_quantize_rows -- per-row E4M3 quantization of A [rows, K] (weights: one row per
+ * output channel; activations: one row per token, at run time).
+ *   scale[r] = max_k |A[r, k]| / 448 in binary64 (1 for an all-zero row), stored rounded to
+ *   binary32; code = E4M3 byte of A[r, k] / scale[r] (binary64 quotient, magnitude capped at
+ *   448, rounded halves-to-even on the grid of 3 mantissa bits of its binary exponent,
+ *   exponents below -6 on the grid of -6).  Bytes are OCP E4M3: sign bit 7, exponent bits
+ *   6..3 with bias 7, mantissa bits 2..0; 0x7E = 448; a value that rounds to zero keeps its
+ *   sign (0x80); 0x7F/0xFF (NaN) are never written.
+ *   A       [rows, K] row-major, binary32 (at = W4_F32) or bfloat16 (W4_BF16); 16-B aligned.
+ *   codes   [rows, K] bytes, 16-B aligned.   scales  [rows] binary32, 4-B aligned.
+ *   d_status  optional device word: bit 0 is OR-ed in if a row holds a non-finite value
+ *             (its codes are then undefined).
+ * Requires K a multiple of 128, 128 <= K <= W4_FP8_MAX_K.
+ *
+ * w4_fp8_gemm -- Y[m, n] = sx[m] * sw[n] * sum_k value(xq[m, k]) * value(wq[n, k]) on the
+ * FP8 matrix cores with binary32 accumulation (each product of two E4M3 values is exact).
+ *   xq, sx   [M, K] codes and [M] scales of the activations (w4_fp8_quantize_rows).
+ *   wq, sw   [N, K] codes and [N] scales of the weights.
+ *   Y        [M, N] row-major, binary32 (yt = W4_F32) or bfloat16 (W4_BF16); must not
+ *            overlap the inputs.  Codes 16-B aligned, scales 4-B, Y 4-B (2-B for bf16).
+ * Requires K a multiple of 128, 128 <= K <= W4_FP8_MAX_K.  Deterministic (no atomics).
+ */
+w4_status w4_fp8_quantize_rows(const void* A, w4_dtype at, int64_t rows, int64_t K,
+                               uint8_t* codes, float* scales, uint32_t* d_status,
+                               hipStream_t stream);
+w4_status w4_fp8_gemm(const uint8_t* xq, const float* sx, int64_t M, const uint8_t* wq,
+                      const float* sw, int64_t N, int64_t K, void* Y, w4_dtype yt,
+                      hipStream_t stream);
 
 /*
  * w4_stream_read -- measurement probe, not part of the method: reads `bytes` bytes of
