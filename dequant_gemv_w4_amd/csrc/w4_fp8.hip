@@ -18,10 +18,11 @@
 // Product (fp8_gemm_kernel): Y[m, n] = sx[m] * sw[n] * sum_k qx[m, k] * qw[n, k] with
 // v_mfma_scale_f32_32x32x64_f8f6f4 (block scales left at 2^0), binary32 accumulation;
 // every product of two E4M3 values is exact in binary32.  512 threads per 128 x 256
-// output tile (a 256-thread 128 x 128 tile is the alternative), wave (wm, wn) owns 64 x 64
-// as 2 x 2 MFMA tiles; a K step is 128 inputs, loaded two steps ahead into one of two
-// register sets and stored into a double-buffered LDS tile (16-byte chunk c of row r at
-// slot c ^ (r & 7), so the operand reads of 32 rows spread over the banks).  A lane
+// output tile, wave (wm, wn) owns 64 x 64 as 2 x 2 MFMA tiles; a K step is 128 inputs.
+// fp8_gemm_ring_kernel (the default) loads each step straight into a three-stage LDS ring
+// two steps ahead; fp8_gemm_kernel (tiles of other shapes) stages the loads through two
+// register sets into a double-buffered LDS tile.  In LDS, 16-byte chunk c of row r sits
+// at slot c ^ (r & 7), so the operand reads of 32 rows spread over the banks.  A lane
 // supplies row (lane % 32) and the 32 inputs 32 * (lane / 32) .. +31 of a 64-input MFMA
 // step, the same inputs for both operands, so each output is a dot product over matching
 // inputs whatever order the unit sums them in.
@@ -261,6 +262,137 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fp8_gemm_kernel(
         }
 }
 
+// 16 bytes per lane from global memory straight into LDS: lane l of the wave writes bytes
+// [16 l, 16 l + 16) after the wave-uniform LDS address.  Inline assembly, so the compiler
+// does not order the LDS reads of other stages behind these loads; the kernel waits for
+// them itself (vmcnt) before the barrier that publishes a stage.
+__device__ __forceinline__ void fp8_load_lds16(const void* g, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(g), "s"(lds_addr)
+                 : "memory", "m0");
+}
+
+// The same product with a three-stage LDS ring filled by direct loads two steps ahead:
+// 512 threads, 128 x 256 output tile, wave (wm, wn) owns 64 x 64 (2 x 2 MFMA tiles).  A
+// stage is the X tile (128 rows x 128 inputs, 16 KiB) and the W tile (256 x 128, 32 KiB),
+// chunk c of row r at slot c ^ (r & 7): each wave issues 2 X and 4 W loads of 8 rows x
+// 128 bytes per stage, lane l loading chunk (l % 8) ^ (row & 7) of row l / 8 so that it
+// lands in its swizzled slot.
+constexpr int kRingStages = 3;
+constexpr int kRingX = 128 * kFK;
+constexpr int kRingW = 256 * kFK;
+constexpr int kRingStage = kRingX + kRingW;
+
+__global__ __launch_bounds__(512) void fp8_gemm_ring_kernel(
+    const uint8_t* __restrict__ X, const float* __restrict__ sx, const uint8_t* __restrict__ W,
+    const float* __restrict__ sw, void* __restrict__ Y, int y_bf16, int M, int N, int K,
+    int tiles_n) {
+    __shared__ __attribute__((aligned(16))) uint8_t ring[kRingStages * kRingStage];
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wm = wave >> 2;
+    const int wn = wave & 3;
+    const int m0 = (int)(blockIdx.x / tiles_n) * 128;
+    const int n0 = (int)(blockIdx.x % tiles_n) * 256;
+
+    // per-lane sources of this wave's loads (step 0; a step adds 128 bytes)
+    const uint8_t* xsrc[2];
+    const uint8_t* wsrc[4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int r = 8 * (2 * wave + i) + (lane >> 3);
+        xsrc[i] = X + (int64_t)min(m0 + r, M - 1) * K + 16 * ((lane & 7) ^ (r & 7));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 8 * (4 * wave + i) + (lane >> 3);
+        wsrc[i] = W + (int64_t)min(n0 + r, N - 1) * K + 16 * ((lane & 7) ^ (r & 7));
+    }
+    const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring);
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    auto issue = [&](int st, int kt) {
+        const uint32_t base = ring_lds + st * kRingStage;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            fp8_load_lds16(xsrc[i] + (int64_t)kt * kFK, base + (2 * wave_u + i) * 1024);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            fp8_load_lds16(wsrc[i] + (int64_t)kt * kFK, base + kRingX + (4 * wave_u + i) * 1024);
+    };
+    auto operand = [&](const uint8_t* t, int r, int kh) {
+        const int c0 = 4 * kh + 2 * (lane >> 5);
+        const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(&t[r * kFK + ((c0 ^ (r & 7)) << 4)]);
+        const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(&t[r * kFK + (((c0 + 1) ^ (r & 7)) << 4)]);
+        const v8i_t v = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                         (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        return v;
+    };
+
+    f32x16_t acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = (f32x16_t){};
+
+    const int Kt = K / kFK;
+    issue(0, 0);
+    if (Kt > 1) issue(1, 1);
+    for (int kt = 0; kt < Kt; ++kt) {
+        // this wave's loads of step kt have landed (the six of step kt+1 may still be in
+        // flight); the barrier makes every wave's loads visible and frees the stage that
+        // step kt+2 reuses
+        if (kt + 1 < Kt)
+            __builtin_amdgcn_s_waitcnt(0xF76);  // vmcnt(6)
+        else
+            __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
+        __syncthreads();
+        if (kt + 2 < Kt) issue((kt + 2) % kRingStages, kt + 2);
+        const uint8_t* xs = ring + (kt % kRingStages) * kRingStage;
+        const uint8_t* ws = xs + kRingX;
+        v8i_t xa[2][2], wb[2][2];
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) xa[kh][i] = operand(xs, 64 * wm + 32 * i + (lane & 31), kh);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) wb[kh][j] = operand(ws, 64 * wn + 32 * j + (lane & 31), kh);
+        }
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        xa[kh][i], wb[kh][j], acc[i][j], 0, 0, 0, 127, 0, 127);
+    }
+
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int c = n0 + 64 * wn + 32 * j + (lane & 31);
+            if (c >= N) continue;
+            const float scw = sw[c];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int r = m0 + 64 * wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                if (r >= M) continue;
+                const float y = acc[i][j][v] * sx[r] * scw;
+                const int64_t o = (int64_t)r * N + c;
+                if (y_bf16) {
+                    const uint32_t u = __float_as_uint(y);
+                    static_cast<uint16_t*>(Y)[o] = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+                } else {
+                    static_cast<float*>(Y)[o] = y;
+                }
+            }
+        }
+}
+
 template <int TM, int TN, int WGM, int WGN>
 hipError_t launch_fp8_gemm_t(const uint8_t* xq, const float* sx, int64_t m, const uint8_t* wq,
                              const float* sw, int64_t n, int64_t k, void* y, bool y_bf16,
@@ -291,14 +423,22 @@ hipError_t launch_fp8_quantize_rows(const void* a, bool bf16, int64_t rows, int6
 hipError_t launch_fp8_gemm(const uint8_t* xq, const float* sx, int64_t m, const uint8_t* wq,
                            const float* sw, int64_t n, int64_t k, void* y, bool y_bf16,
                            hipStream_t s) {
+    // measured on MI355X at 4096 x 28672 x 8192: the three-stage ring 1.09-1.10 ms; register
+    // staging two steps ahead 1.14-1.16 ms with 128 x 256 tiles (W4A16_FP8_TILE=256), 1.16 ms
+    // with 256 x 128, 1.58 ms with 128 x 128 tiles (W4A16_FP8_TILE=128)
     static const int tile = [] {
         const char* e = getenv("W4A16_FP8_TILE");
-        return e ? atoi(e) : 256;
+        return e ? atoi(e) : 1;
     }();
     if (tile == 128)
         return launch_fp8_gemm_t<2, 2, 2, 2>(xq, sx, m, wq, sw, n, k, y, y_bf16, s);
-    // measured on MI355X at 4096 x 28672 x 8192: 128 x 256 tiles 1.14 ms, 256 x 128 tiles
-    // 1.16 ms, 128 x 128 tiles 1.58 ms
+    if (tile != 256) {
+        const int tiles_n = (int)((n + 255) / 256);
+        const int64_t tiles = ((m + 127) / 128) * tiles_n;
+        hipLaunchKernelGGL(fp8_gemm_ring_kernel, dim3((unsigned)tiles), dim3(512), 0, s, xq, sx,
+                           wq, sw, y, y_bf16 ? 1 : 0, (int)m, (int)n, (int)k, tiles_n);
+        return hipGetLastError();
+    }
     return launch_fp8_gemm_t<2, 2, 2, 4>(xq, sx, m, wq, sw, n, k, y, y_bf16, s);
 }
 
