@@ -16,3 +16,6 @@ from .fp8_oracle import (  # noqa: F401
     FP8_MAX, E4M3_VALUES, e4m3_decode, e4m3_encode, quantize_rows_fp8_ref, dequant_fp8_ref,
     gemm_fp8_ref, tolerance_fp8_ref,
 )
+from .int8_oracle import (  # noqa: F401
+    INT8_MAX, quantize_rows_int8_ref, dequant_int8_ref, gemm_int8_ref, tolerance_int8_ref,
+)
