@@ -38,7 +38,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 # profiles/w4_gemv_llama70b_fused_step_hbm_traffic.md
 GEMV_STEP_TRAFFIC_BYTES_PER_LAUNCH = 114039772
 BF16_DENSE_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
-FP8_DENSE_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
+W8_DENSE_TOPS = 5000.0         # MI355X dense fp8 MFMA TFLOP/s, and int8 TOP/s
 METRIC = "W4A16 g128 GEMV achieved HBM GB/s (% of peak), 70B layer shapes, batch 1"
 
 
@@ -372,11 +372,12 @@ def prefill_gemm(prepared, dev: str, reps: int = 20, warmup: int = 10):
             "mfma_util_vs_2.5PF_dense_bf16": round(tflops / BF16_DENSE_TFLOPS, 4)}
 
 
-def prefill_fp8(dev: str, w4a16_ms: float | None, reps: int = 20, warmup: int = 10):
-    """W8A8 in FP8 E4M3 on the prefill shape: the same X and W draws as the W4A16 GEMM.
+def prefill_w8a8(dev: str, w4a16_ms: float | None, fmt: str = "fp8", reps: int = 20,
+                 warmup: int = 10):
+    """W8A8 (FP8 E4M3 or INT8) on the prefill shape: the same X and W draws as the W4A16 GEMM.
 
     W is quantized per output channel beforehand (untimed, as a checkpoint would be); the
-    timed product is the per-token quantization of X plus the FP8 GEMM, with the GEMM
+    timed product is the per-token quantization of X plus the 8-bit GEMM, with the GEMM
     alone reported beside it.
     """
     import torch
@@ -384,12 +385,14 @@ def prefill_fp8(dev: str, w4a16_ms: float | None, reps: int = 20, warmup: int = 
     import dequant_gemv_w4_amd as w4
     import synth
 
+    quant = w4.w4_fp8_quantize_rows if fmt == "fp8" else w4.w4_int8_quantize_rows
+    gemm = w4.w4_fp8_gemm if fmt == "fp8" else w4.w4_int8_gemm
     m, n, k = 4096, 28672, 8192
     X = synth.normal_activations(m, k, 40200, dev)
     W = synth.normal_weights(n, k, synth.seed_for(4, "gate", 0), dev)
-    wq, sw = w4.w4_fp8_quantize_rows(W)
+    wq, sw = quant(W)
     del W
-    xq, sx = w4.w4_fp8_quantize_rows(X)
+    xq, sx = quant(X)
     Y = torch.empty(m, n, dtype=torch.float32, device=dev)
 
     def timed(fn):
@@ -406,17 +409,18 @@ def prefill_fp8(dev: str, w4a16_ms: float | None, reps: int = 20, warmup: int = 
         return start.elapsed_time(end) / reps
 
     def full():
-        w4.w4_fp8_quantize_rows(X, codes=xq, scales=sx)
-        w4.w4_fp8_gemm(xq, sx, wq, sw, Y=Y)
+        quant(X, codes=xq, scales=sx)
+        gemm(xq, sx, wq, sw, Y=Y)
 
     ms_full = timed(full)
-    ms_gemm = timed(lambda: w4.w4_fp8_gemm(xq, sx, wq, sw, Y=Y))
+    ms_gemm = timed(lambda: gemm(xq, sx, wq, sw, Y=Y))
     flops = 2.0 * m * n * k
+    unit = "TFLOP/s" if fmt == "fp8" else "TOP/s"
     out = {"M": m, "N": n, "K": k, "ms": round(ms_full, 3),
-           "TFLOP/s": round(flops / (ms_full * 1e-3) / 1e12, 1),
+           unit: round(flops / (ms_full * 1e-3) / 1e12, 1),
            "gemm_ms": round(ms_gemm, 3),
-           "gemm_TFLOP/s": round(flops / (ms_gemm * 1e-3) / 1e12, 1),
-           "mfma_util_vs_5PF_dense_fp8": round(flops / (ms_gemm * 1e-3) / 1e12 / FP8_DENSE_TFLOPS, 4)}
+           "gemm_" + unit: round(flops / (ms_gemm * 1e-3) / 1e12, 1),
+           f"mfma_util_vs_5P_dense_{fmt}": round(flops / (ms_gemm * 1e-3) / 1e12 / W8_DENSE_TOPS, 4)}
     if w4a16_ms:
         out["speedup_vs_w4a16_gemm"] = round(w4a16_ms / ms_full, 3)
     return out
@@ -588,8 +592,10 @@ def main() -> int:
         log("per-shape done")
         result["prefill_gemm"] = prefill_gemm(unfused, dev)
         log(f"prefill GEMM: {result['prefill_gemm']}")
-        result["prefill_w8a8_fp8"] = prefill_fp8(dev, result["prefill_gemm"]["ms"])
+        result["prefill_w8a8_fp8"] = prefill_w8a8(dev, result["prefill_gemm"]["ms"], "fp8")
         log(f"prefill W8A8 FP8: {result['prefill_w8a8_fp8']}")
+        result["prefill_w8a8_int8"] = prefill_w8a8(dev, result["prefill_gemm"]["ms"], "int8")
+        log(f"prefill W8A8 INT8: {result['prefill_w8a8_int8']}")
         del unfused
         torch.cuda.empty_cache()
         result["quantizer"] = quantizer_rate(dev)

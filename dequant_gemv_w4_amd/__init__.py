@@ -19,7 +19,7 @@ __all__ = [
     "w4_quantize", "w4_quantize_symmetric", "w4_prepared_bytes", "w4_prepare", "w4_unprepare",
     "w4_gemv", "w4_gemm_workspace_bytes", "w4_gemm",
     "w4_status_string", "w4_last_hip_error", "w4_format_version", "w4_stream_read",
-    "w4_fp8_quantize_rows", "w4_fp8_gemm",
+    "w4_fp8_quantize_rows", "w4_fp8_gemm", "w4_int8_quantize_rows", "w4_int8_gemm",
     "W4ChainGemv", "w4_chain_plan_bytes", "w4_chain_workspace_bytes", "w4_chain_plan",
     "w4_chain_run",
     "W4Format", "w4_zeros_bytes", "w4_quantize_fmt", "w4_prepared_bytes_fmt", "w4_prepare_fmt",
@@ -103,6 +103,10 @@ def lib() -> ctypes.CDLL:
     L.w4_fp8_quantize_rows.restype = i32
     L.w4_fp8_gemm.argtypes = [vp, vp, i64, vp, vp, i64, i64, vp, i32, vp]
     L.w4_fp8_gemm.restype = i32
+    L.w4_int8_quantize_rows.argtypes = [vp, i32, i64, i64, vp, vp, vp, vp]
+    L.w4_int8_quantize_rows.restype = i32
+    L.w4_int8_gemm.argtypes = [vp, vp, i64, vp, vp, i64, i64, vp, i32, vp]
+    L.w4_int8_gemm.restype = i32
     L.w4_chain_plan_bytes.argtypes = [i64]
     L.w4_chain_plan_bytes.restype = sz
     L.w4_chain_workspace_bytes.argtypes = [i64]
@@ -532,4 +536,48 @@ def w4_fp8_gemm(xq, sx, wq, sw, Y=None, out_dtype=None):
     _check(lib().w4_fp8_gemm(_ptr(xq), _ptr(sx), m, _ptr(wq), _ptr(sw), n, k, _ptr(Y),
                              W4_F32 if Y.dtype == torch.float32 else W4_BF16, _stream(xq)),
            "w4_fp8_gemm")
+    return Y
+
+
+def w4_int8_quantize_rows(A, codes=None, scales=None, status=None):
+    """Per-row symmetric INT8 codes [rows, K] int8 and binary32 steps [rows] of a 2-D
+    binary32 or bfloat16 device tensor."""
+    import torch
+    _require(A, (torch.float32, torch.bfloat16), None, "A")
+    if A.dim() != 2 or not A.is_contiguous():
+        raise ValueError("A must be a contiguous [rows, K] tensor")
+    rows, k = A.shape
+    if codes is None:
+        codes = torch.empty(rows, k, dtype=torch.int8, device=A.device)
+    if scales is None:
+        scales = torch.empty(rows, dtype=torch.float32, device=A.device)
+    _require(codes, torch.int8, (rows, k), "codes")
+    _require(scales, torch.float32, (rows,), "scales")
+    st = ctypes.c_void_p(None)
+    if status is not None:
+        _require(status, torch.int32, None, "status")
+        st = _ptr(status)
+    _check(lib().w4_int8_quantize_rows(_ptr(A), W4_F32 if A.dtype == torch.float32 else W4_BF16,
+                                       rows, k, _ptr(codes), _ptr(scales), st, _stream(A)),
+           "w4_int8_quantize_rows")
+    return codes, scales
+
+
+def w4_int8_gemm(xq, sx, wq, sw, Y=None, out_dtype=None):
+    """Y [M, N] = sx[m] sw[n] sum_k xq[m, k] wq[n, k] (int8 codes, exact int32 sums)."""
+    import torch
+    _require(xq, torch.int8, None, "xq")
+    _require(wq, torch.int8, None, "wq")
+    m, k = xq.shape
+    n, k2 = wq.shape
+    if k2 != k:
+        raise ValueError("xq and wq must have the same K")
+    _require(sx, torch.float32, (m,), "sx")
+    _require(sw, torch.float32, (n,), "sw")
+    if Y is None:
+        Y = torch.empty(m, n, dtype=out_dtype or torch.float32, device=xq.device)
+    _require(Y, (torch.float32, torch.bfloat16), (m, n), "Y")
+    _check(lib().w4_int8_gemm(_ptr(xq), _ptr(sx), m, _ptr(wq), _ptr(sw), n, k, _ptr(Y),
+                              W4_F32 if Y.dtype == torch.float32 else W4_BF16, _stream(xq)),
+           "w4_int8_gemm")
     return Y

@@ -417,6 +417,45 @@ w4_status w4_fp8_gemm(const uint8_t* xq, const float* sx, int64_t M, const uint8
     return e == hipSuccess ? W4_OK : hip_fail(e);
 }
 
+w4_status w4_int8_quantize_rows(const void* A, w4_dtype at, int64_t rows, int64_t K,
+                                int8_t* codes, float* scales, uint32_t* d_status,
+                                hipStream_t stream) {
+    if (!A || !codes || !scales) return W4_ERR_NULL;
+    if (at != W4_F32 && at != W4_BF16) return W4_ERR_DTYPE;
+    if (rows < 1 || rows > (int64_t)INT32_MAX || K < W4_GROUP || K % W4_GROUP != 0 ||
+        K > W4_FP8_MAX_K)
+        return W4_ERR_SHAPE;
+    if (!aligned(A, 16) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(d_status, 4))
+        return W4_ERR_ALIGN;
+    w4_status st = check_arch();
+    if (st != W4_OK) return st;
+    hipError_t e = w4::launch_fp8_quantize_rows(A, at == W4_BF16, rows, K,
+                                                reinterpret_cast<uint8_t*>(codes), scales,
+                                                d_status, stream, true);
+    return e == hipSuccess ? W4_OK : hip_fail(e);
+}
+
+w4_status w4_int8_gemm(const int8_t* xq, const float* sx, int64_t M, const int8_t* wq,
+                       const float* sw, int64_t N, int64_t K, void* Y, w4_dtype yt,
+                       hipStream_t stream) {
+    if (!xq || !sx || !wq || !sw || !Y) return W4_ERR_NULL;
+    if (yt != W4_F32 && yt != W4_BF16) return W4_ERR_DTYPE;
+    if (M < 1 || N < 1 || M > (int64_t)INT32_MAX || N > (int64_t)INT32_MAX || K < W4_GROUP ||
+        K % W4_GROUP != 0 || K > W4_FP8_MAX_K)
+        return W4_ERR_SHAPE;
+    const int64_t tiles = ((M + 127) / 128) * ((N + 255) / 256);
+    if (tiles > (int64_t)INT32_MAX) return W4_ERR_SHAPE;
+    if (!aligned(xq, 16) || !aligned(wq, 16) || !aligned(sx, 4) || !aligned(sw, 4) ||
+        !aligned(Y, yt == W4_F32 ? 4 : 2))
+        return W4_ERR_ALIGN;
+    w4_status st = check_arch();
+    if (st != W4_OK) return st;
+    hipError_t e = w4::launch_int8_gemm(reinterpret_cast<const uint8_t*>(xq), sx, M,
+                                        reinterpret_cast<const uint8_t*>(wq), sw, N, K, Y,
+                                        yt == W4_BF16, stream);
+    return e == hipSuccess ? W4_OK : hip_fail(e);
+}
+
 w4_status w4_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream) {
     if (!buf || !sink) return W4_ERR_NULL;
     if (bytes == 0 || bytes % 16 != 0) return W4_ERR_SHAPE;

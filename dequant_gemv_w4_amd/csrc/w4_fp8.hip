@@ -77,7 +77,15 @@ __device__ __forceinline__ void load8(const void* a, int64_t i, float (&v)[8]) {
     }
 }
 
-template <bool IN_BF16>
+// INT8 (symmetric, page "Quantization" › "How it really works" and "Code"): the step is the
+// row's largest magnitude over 127 (1 for an all-zero row), in binary64; code = the
+// binary64 quotient rounded to the nearest integer, halves to even, clamped to [-128, 127].
+__device__ __forceinline__ uint32_t int8_byte(double t) {
+    const double q = fmin(fmax(rint(t), -128.0), 127.0);
+    return (uint32_t)(uint8_t)(int8_t)(int)q;
+}
+
+template <bool IN_BF16, bool INT8>
 __global__ __launch_bounds__(kQT) void fp8_quantize_rows_kernel(const void* __restrict__ a,
                                                                 int64_t K,
                                                                 uint8_t* __restrict__ codes,
@@ -106,7 +114,7 @@ __global__ __launch_bounds__(kQT) void fp8_quantize_rows_kernel(const void* __re
     amax = wmax[0];
 #pragma unroll
     for (int w = 1; w < kQT / 64; ++w) amax = fmaxf(amax, wmax[w]);
-    const double s = amax == 0.0f ? 1.0 : (double)amax / kFp8Max;
+    const double s = amax == 0.0f ? 1.0 : (double)amax / (INT8 ? 127.0 : kFp8Max);
     if (threadIdx.x == 0) scales[row] = (float)s;
     uint8_t* dst = codes + row * K;
     for (int64_t i = (int64_t)threadIdx.x * 8; i < K; i += kQT * 8) {
@@ -115,8 +123,13 @@ __global__ __launch_bounds__(kQT) void fp8_quantize_rows_kernel(const void* __re
         uint32_t lo = 0, hi = 0;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            lo |= e4m3_byte((double)v[q] / s) << (8 * q);
-            hi |= e4m3_byte((double)v[4 + q] / s) << (8 * q);
+            if constexpr (INT8) {
+                lo |= int8_byte((double)v[q] / s) << (8 * q);
+                hi |= int8_byte((double)v[4 + q] / s) << (8 * q);
+            } else {
+                lo |= e4m3_byte((double)v[q] / s) << (8 * q);
+                hi |= e4m3_byte((double)v[4 + q] / s) << (8 * q);
+            }
         }
         *reinterpret_cast<uint2*>(dst + i) = make_uint2(lo, hi);
     }
@@ -284,6 +297,12 @@ constexpr int kRingX = 128 * kFK;
 constexpr int kRingW = 256 * kFK;
 constexpr int kRingStage = kRingX + kRingW;
 
+// INT8: v_mfma_i32_32x32x32_i8 (exact int32 sums); a lane supplies row (lane % 32) and the
+// 16 inputs 32 s + 16 (lane / 32) .. +15 of MFMA step s, one 16-byte chunk.
+typedef int v4i_t __attribute__((ext_vector_type(4)));
+typedef int i32x16_t __attribute__((ext_vector_type(16)));
+
+template <bool INT8>
 __global__ __launch_bounds__(512) void fp8_gemm_ring_kernel(
     const uint8_t* __restrict__ X, const float* __restrict__ sx, const uint8_t* __restrict__ W,
     const float* __restrict__ sw, void* __restrict__ Y, int y_bf16, int M, int N, int K,
@@ -332,10 +351,17 @@ __global__ __launch_bounds__(512) void fp8_gemm_ring_kernel(
     };
 
     f32x16_t acc[2][2];
+    i32x16_t iacc[2][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = (f32x16_t){};
+        for (int j = 0; j < 2; ++j) {
+            acc[i][j] = (f32x16_t){};
+            iacc[i][j] = (i32x16_t){};
+        }
+    auto chunk = [&](const uint8_t* t, int r, int c) {
+        return __builtin_bit_cast(v4i_t, *reinterpret_cast<const u32x4_t*>(&t[r * kFK + ((c ^ (r & 7)) << 4)]));
+    };
 
     const int Kt = K / kFK;
     issue(0, 0);
@@ -352,6 +378,24 @@ __global__ __launch_bounds__(512) void fp8_gemm_ring_kernel(
         if (kt + 2 < Kt) issue((kt + 2) % kRingStages, kt + 2);
         const uint8_t* xs = ring + (kt % kRingStages) * kRingStage;
         const uint8_t* ws = xs + kRingX;
+        if constexpr (INT8) {
+            v4i_t xa[4][2], wb[4][2];
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+#pragma unroll
+                for (int i = 0; i < 2; ++i) xa[st][i] = chunk(xs, 64 * wm + 32 * i + (lane & 31), 2 * st + (lane >> 5));
+#pragma unroll
+                for (int j = 0; j < 2; ++j) wb[st][j] = chunk(ws, 64 * wn + 32 * j + (lane & 31), 2 * st + (lane >> 5));
+            }
+#pragma unroll
+            for (int st = 0; st < 4; ++st)
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        iacc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xa[st][i], wb[st][j], iacc[i][j], 0, 0, 0);
+            continue;
+        }
         v8i_t xa[2][2], wb[2][2];
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh) {
@@ -381,7 +425,7 @@ __global__ __launch_bounds__(512) void fp8_gemm_ring_kernel(
             for (int v = 0; v < 16; ++v) {
                 const int r = m0 + 64 * wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
                 if (r >= M) continue;
-                const float y = acc[i][j][v] * sx[r] * scw;
+                const float y = (INT8 ? (float)iacc[i][j][v] : acc[i][j][v]) * sx[r] * scw;
                 const int64_t o = (int64_t)r * N + c;
                 if (y_bf16) {
                     const uint32_t u = __float_as_uint(y);
@@ -410,13 +454,28 @@ hipError_t launch_fp8_gemm_t(const uint8_t* xq, const float* sx, int64_t m, cons
 
 hipError_t launch_fp8_quantize_rows(const void* a, bool bf16, int64_t rows, int64_t k,
                                     uint8_t* codes, float* scales, uint32_t* status,
-                                    hipStream_t s) {
-    if (bf16)
-        hipLaunchKernelGGL(fp8_quantize_rows_kernel<true>, dim3((unsigned)rows), dim3(kQT), 0, s, a,
-                           k, codes, scales, status);
-    else
-        hipLaunchKernelGGL(fp8_quantize_rows_kernel<false>, dim3((unsigned)rows), dim3(kQT), 0, s,
-                           a, k, codes, scales, status);
+                                    hipStream_t s, bool int8) {
+    const dim3 grid((unsigned)rows), block(kQT);
+    if (int8) {
+        if (bf16)
+            hipLaunchKernelGGL((fp8_quantize_rows_kernel<true, true>), grid, block, 0, s, a, k, codes, scales, status);
+        else
+            hipLaunchKernelGGL((fp8_quantize_rows_kernel<false, true>), grid, block, 0, s, a, k, codes, scales, status);
+    } else if (bf16) {
+        hipLaunchKernelGGL((fp8_quantize_rows_kernel<true, false>), grid, block, 0, s, a, k, codes, scales, status);
+    } else {
+        hipLaunchKernelGGL((fp8_quantize_rows_kernel<false, false>), grid, block, 0, s, a, k, codes, scales, status);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_int8_gemm(const uint8_t* xq, const float* sx, int64_t m, const uint8_t* wq,
+                            const float* sw, int64_t n, int64_t k, void* y, bool y_bf16,
+                            hipStream_t s) {
+    const int tiles_n = (int)((n + 255) / 256);
+    const int64_t tiles = ((m + 127) / 128) * tiles_n;
+    hipLaunchKernelGGL(fp8_gemm_ring_kernel<true>, dim3((unsigned)tiles), dim3(512), 0, s, xq, sx,
+                       wq, sw, y, y_bf16 ? 1 : 0, (int)m, (int)n, (int)k, tiles_n);
     return hipGetLastError();
 }
 
@@ -435,7 +494,7 @@ hipError_t launch_fp8_gemm(const uint8_t* xq, const float* sx, int64_t m, const 
     if (tile != 256) {
         const int tiles_n = (int)((n + 255) / 256);
         const int64_t tiles = ((m + 127) / 128) * tiles_n;
-        hipLaunchKernelGGL(fp8_gemm_ring_kernel, dim3((unsigned)tiles), dim3(512), 0, s, xq, sx,
+        hipLaunchKernelGGL(fp8_gemm_ring_kernel<false>, dim3((unsigned)tiles), dim3(512), 0, s, xq, sx,
                            wq, sw, y, y_bf16 ? 1 : 0, (int)m, (int)n, (int)k, tiles_n);
         return hipGetLastError();
     }

@@ -301,6 +301,28 @@ w4_status w4_fp8_gemm(const uint8_t* xq, const float* sx, int64_t M, const uint8
                       hipStream_t stream);
 
 /*
+ * W8A8 in INT8 (page "Quantization" › "How it really works" and "Code": symmetric 8-bit
+ * codes with one absmax scale per block; the architecture page names INT8 beside FP8 for
+ * W8A8 prefill).
+ *
+ * w4_int8_quantize_rows -- per-row symmetric INT8: step[r] = max_k |A[r, k]| / 127 in
+ *   binary64 (1 for an all-zero row), stored rounded to binary32; code = A[r, k] / step[r]
+ *   in binary64, rounded to the nearest integer with halves to even, clamped to
+ *   [-128, 127].  Arguments, alignment, limits and status as w4_fp8_quantize_rows, with
+ *   codes [rows, K] int8.
+ * w4_int8_gemm -- Y[m, n] = sx[m] * sw[n] * sum_k xq[m, k] * wq[n, k] on the INT8 matrix
+ *   cores; the sums are exact int32 (|sum| <= K * 128 * 128 < 2^31 for K <= W4_FP8_MAX_K),
+ *   then converted to binary32 and scaled.  Arguments, alignment and limits as
+ *   w4_fp8_gemm.  Deterministic.
+ */
+w4_status w4_int8_quantize_rows(const void* A, w4_dtype at, int64_t rows, int64_t K,
+                                int8_t* codes, float* scales, uint32_t* d_status,
+                                hipStream_t stream);
+w4_status w4_int8_gemm(const int8_t* xq, const float* sx, int64_t M, const int8_t* wq,
+                       const float* sw, int64_t N, int64_t K, void* Y, w4_dtype yt,
+                       hipStream_t stream);
+
+/*
  * w4_stream_read -- measurement probe, not part of the method: reads `bytes` bytes of
  * device memory at `buf` once with plain streaming loads (8192 workgroups, each a
  * contiguous share, non-temporal 16-byte loads) and discards them, so a product's rate

@@ -156,3 +156,17 @@ def test_fp8_entry_points_validate_before_device_work():
     assert L.w4_fp8_gemm(f(), f(), 4, f(), f(), 4, 64, f(), 0, s) == 2
     assert L.w4_fp8_gemm(f(0x100004), f(), 4, f(), f(), 4, 128, f(), 0, s) == 3
     assert L.w4_fp8_gemm(f(), f(), 4, f(), f(), 4, 128, f(0x100002), 0, s) == 3
+
+
+def test_int8_entry_points_validate_before_device_work():
+    L = w4.lib()
+    s = NULL
+    f = _fake
+    assert L.w4_int8_quantize_rows(NULL, 0, 4, 128, f(), f(), NULL, s) == 1
+    assert L.w4_int8_quantize_rows(f(), 3, 4, 128, f(), f(), NULL, s) == 4
+    assert L.w4_int8_quantize_rows(f(), 0, 4, 200, f(), f(), NULL, s) == 2
+    assert L.w4_int8_quantize_rows(f(), 0, 4, 128, f(0x100008), f(), NULL, s) == 3
+    assert L.w4_int8_gemm(f(), f(), 4, NULL, f(), 4, 128, f(), 0, s) == 1
+    assert L.w4_int8_gemm(f(), f(), 4, f(), f(), 4, 128, f(), 7, s) == 4
+    assert L.w4_int8_gemm(f(), f(), 4, f(), f(), 0, 128, f(), 0, s) == 2
+    assert L.w4_int8_gemm(f(), f(), 4, f(), f(), 4, 128, f(0x100002), 0, s) == 3
