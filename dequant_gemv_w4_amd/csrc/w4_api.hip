@@ -393,7 +393,7 @@ w4_status w4_fp8_quantize_rows(const void* A, w4_dtype at, int64_t rows, int64_t
         return W4_ERR_ALIGN;
     w4_status st = check_arch();
     if (st != W4_OK) return st;
-    hipError_t e = w4::launch_fp8_quantize_rows(A, at == W4_BF16, rows, K, codes, scales,
+    hipError_t e = w4::launch_w8_quantize_rows(A, at == W4_BF16, rows, K, codes, scales,
                                                 d_status, stream);
     return e == hipSuccess ? W4_OK : hip_fail(e);
 }
@@ -429,7 +429,7 @@ w4_status w4_int8_quantize_rows(const void* A, w4_dtype at, int64_t rows, int64_
         return W4_ERR_ALIGN;
     w4_status st = check_arch();
     if (st != W4_OK) return st;
-    hipError_t e = w4::launch_fp8_quantize_rows(A, at == W4_BF16, rows, K,
+    hipError_t e = w4::launch_w8_quantize_rows(A, at == W4_BF16, rows, K,
                                                 reinterpret_cast<uint8_t*>(codes), scales,
                                                 d_status, stream, true);
     return e == hipSuccess ? W4_OK : hip_fail(e);

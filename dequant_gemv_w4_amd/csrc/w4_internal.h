@@ -139,7 +139,7 @@ bool gemv_ring_takes(int64_t n, int64_t k);
 size_t gemm_workspace(int64_t m, int64_t k);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t s);
 // 8-bit rows: E4M3 codes, or symmetric INT8 codes when int8 is set
-hipError_t launch_fp8_quantize_rows(const void* a, bool bf16, int64_t rows, int64_t k,
+hipError_t launch_w8_quantize_rows(const void* a, bool bf16, int64_t rows, int64_t k,
                                     uint8_t* codes, float* scales, uint32_t* status,
                                     hipStream_t s, bool int8 = false);
 hipError_t launch_int8_gemm(const uint8_t* xq, const float* sx, int64_t m, const uint8_t* wq,

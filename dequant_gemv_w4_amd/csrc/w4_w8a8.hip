@@ -1,4 +1,5 @@
-// W8A8 in FP8 E4M3 for prefill: per-row quantization and the product on the matrix cores.
+// W8A8 for prefill, in FP8 E4M3 or INT8: per-row quantization and the product on the
+// matrix cores.
 //
 // Prefill is bound by the matrix units, so a weight-only format barely speeds it up; the
 // arithmetic itself has to be narrower, with activations quantized too: W8A8 in FP8 or
@@ -6,23 +7,26 @@
 // faster" and "Number formats, scales and granularity": E4M3 for weights and activations,
 // largest value 448; dynamic per-token activation scales).
 //
-// Quantization (fp8_quantize_rows_kernel, one workgroup per row): the row's largest
-// magnitude over 448 is the scale (1 for an all-zero row), both in binary64 as in the
-// page's program ("Quantization" › "Code": FP8 E4M3 per-channel, rounding to 3 mantissa
-// bits with subnormals, largest value 448); each value divided by the scale in binary64 is
-// capped at 448 and rounded, halves to even, on the grid of 3 mantissa bits of its binary
-// exponent (exponents below -6 use the grid of -6).  Codes are OCP E4M3 bytes (sign,
-// exponent with bias 7, mantissa), the byte the gfx950 matrix cores take as format 0; a
-// value that rounds to zero keeps its sign.  The scale is stored as binary32.
+// Quantization (w8_quantize_rows_kernel, one workgroup per row), in binary64 as in the
+// page's program ("Quantization" › "Code": per-tensor / per-channel absmax scales):
+//   * E4M3: the scale is the row's largest magnitude over 448 (1 for an all-zero row);
+//     each value divided by it is capped at 448 and rounded, halves to even, on the grid of
+//     3 mantissa bits of its binary exponent (exponents below -6 use the grid of -6).
+//     Codes are OCP E4M3 bytes (sign, exponent with bias 7, mantissa), the byte the gfx950
+//     matrix cores take as format 0; a value that rounds to zero keeps its sign;
+//   * INT8: the step is the largest magnitude over 127; codes are the quotients rounded to
+//     the nearest integer, halves to even, clamped to [-128, 127].
+// The scale is stored as binary32.
 //
-// Product (fp8_gemm_kernel): Y[m, n] = sx[m] * sw[n] * sum_k qx[m, k] * qw[n, k] with
-// v_mfma_scale_f32_32x32x64_f8f6f4 (block scales left at 2^0), binary32 accumulation;
-// every product of two E4M3 values is exact in binary32.  512 threads per 128 x 256
-// output tile, wave (wm, wn) owns 64 x 64 as 2 x 2 MFMA tiles; a K step is 128 inputs.
-// fp8_gemm_ring_kernel (the default) loads each step straight into a three-stage LDS ring
-// two steps ahead; fp8_gemm_kernel (tiles of other shapes) stages the loads through two
-// register sets into a double-buffered LDS tile.  In LDS, 16-byte chunk c of row r sits
-// at slot c ^ (r & 7), so the operand reads of 32 rows spread over the banks.  A lane
+// Product: Y[m, n] = sx[m] * sw[n] * sum_k qx[m, k] * qw[n, k].  FP8 runs on
+// v_mfma_scale_f32_32x32x64_f8f6f4 (block scales left at 2^0) with binary32 accumulation
+// (every product of two E4M3 values is exact in binary32); INT8 on v_mfma_i32_32x32x32_i8
+// with exact int32 sums.  w8_gemm_ring_kernel (the default for both): 512 threads per
+// 128 x 256 output tile, wave (wm, wn) owns 64 x 64 as 2 x 2 MFMA tiles, a K step is 128
+// inputs loaded straight into a three-stage LDS ring two steps ahead.
+// fp8_gemm_staged_kernel (FP8, other tile shapes) stages the loads through two register
+// sets into a double-buffered LDS tile.  In LDS, 16-byte chunk c of row r sits at slot
+// c ^ (r & 7), so the operand reads of 32 rows spread over the banks.  For FP8 a lane
 // supplies row (lane % 32) and the 32 inputs 32 * (lane / 32) .. +31 of a 64-input MFMA
 // step, the same inputs for both operands, so each output is a dot product over matching
 // inputs whatever order the unit sums them in.
@@ -86,7 +90,7 @@ __device__ __forceinline__ uint32_t int8_byte(double t) {
 }
 
 template <bool IN_BF16, bool INT8>
-__global__ __launch_bounds__(kQT) void fp8_quantize_rows_kernel(const void* __restrict__ a,
+__global__ __launch_bounds__(kQT) void w8_quantize_rows_kernel(const void* __restrict__ a,
                                                                 int64_t K,
                                                                 uint8_t* __restrict__ codes,
                                                                 float* __restrict__ scales,
@@ -140,7 +144,7 @@ constexpr int kFK = 128;  // K step (bytes = inputs)
 // Output tile (WGM * TM * 32) x (WGN * TN * 32): WGM x WGN waves, each owning TM x TN MFMA
 // tiles of 32 x 32.
 template <int TM, int TN, int WGM, int WGN>
-__global__ __launch_bounds__(64 * WGM * WGN) void fp8_gemm_kernel(
+__global__ __launch_bounds__(64 * WGM * WGN) void fp8_gemm_staged_kernel(
     const uint8_t* __restrict__ X, const float* __restrict__ sx, const uint8_t* __restrict__ W,
     const float* __restrict__ sw, void* __restrict__ Y, int y_bf16, int M, int N, int K,
     int tiles_n) {
@@ -279,7 +283,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fp8_gemm_kernel(
 // [16 l, 16 l + 16) after the wave-uniform LDS address.  Inline assembly, so the compiler
 // does not order the LDS reads of other stages behind these loads; the kernel waits for
 // them itself (vmcnt) before the barrier that publishes a stage.
-__device__ __forceinline__ void fp8_load_lds16(const void* g, uint32_t lds_addr) {
+__device__ __forceinline__ void w8_load_lds16(const void* g, uint32_t lds_addr) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                  :
                  : "v"(g), "s"(lds_addr)
@@ -303,7 +307,7 @@ typedef int v4i_t __attribute__((ext_vector_type(4)));
 typedef int i32x16_t __attribute__((ext_vector_type(16)));
 
 template <bool INT8>
-__global__ __launch_bounds__(512) void fp8_gemm_ring_kernel(
+__global__ __launch_bounds__(512) void w8_gemm_ring_kernel(
     const uint8_t* __restrict__ X, const float* __restrict__ sx, const uint8_t* __restrict__ W,
     const float* __restrict__ sw, void* __restrict__ Y, int y_bf16, int M, int N, int K,
     int tiles_n) {
@@ -336,10 +340,10 @@ __global__ __launch_bounds__(512) void fp8_gemm_ring_kernel(
         const uint32_t base = ring_lds + st * kRingStage;
 #pragma unroll
         for (int i = 0; i < 2; ++i)
-            fp8_load_lds16(xsrc[i] + (int64_t)kt * kFK, base + (2 * wave_u + i) * 1024);
+            w8_load_lds16(xsrc[i] + (int64_t)kt * kFK, base + (2 * wave_u + i) * 1024);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            fp8_load_lds16(wsrc[i] + (int64_t)kt * kFK, base + kRingX + (4 * wave_u + i) * 1024);
+            w8_load_lds16(wsrc[i] + (int64_t)kt * kFK, base + kRingX + (4 * wave_u + i) * 1024);
     };
     auto operand = [&](const uint8_t* t, int r, int kh) {
         const int c0 = 4 * kh + 2 * (lane >> 5);
@@ -444,7 +448,7 @@ hipError_t launch_fp8_gemm_t(const uint8_t* xq, const float* sx, int64_t m, cons
     constexpr int BM = WGM * TM * 32, BN = WGN * TN * 32;
     const int tiles_n = (int)((n + BN - 1) / BN);
     const int64_t tiles = ((m + BM - 1) / BM) * tiles_n;
-    hipLaunchKernelGGL((fp8_gemm_kernel<TM, TN, WGM, WGN>), dim3((unsigned)tiles),
+    hipLaunchKernelGGL((fp8_gemm_staged_kernel<TM, TN, WGM, WGN>), dim3((unsigned)tiles),
                        dim3(64 * WGM * WGN), 0, s, xq, sx, wq, sw, y, y_bf16 ? 1 : 0, (int)m,
                        (int)n, (int)k, tiles_n);
     return hipGetLastError();
@@ -452,19 +456,19 @@ hipError_t launch_fp8_gemm_t(const uint8_t* xq, const float* sx, int64_t m, cons
 
 }  // namespace
 
-hipError_t launch_fp8_quantize_rows(const void* a, bool bf16, int64_t rows, int64_t k,
+hipError_t launch_w8_quantize_rows(const void* a, bool bf16, int64_t rows, int64_t k,
                                     uint8_t* codes, float* scales, uint32_t* status,
                                     hipStream_t s, bool int8) {
     const dim3 grid((unsigned)rows), block(kQT);
     if (int8) {
         if (bf16)
-            hipLaunchKernelGGL((fp8_quantize_rows_kernel<true, true>), grid, block, 0, s, a, k, codes, scales, status);
+            hipLaunchKernelGGL((w8_quantize_rows_kernel<true, true>), grid, block, 0, s, a, k, codes, scales, status);
         else
-            hipLaunchKernelGGL((fp8_quantize_rows_kernel<false, true>), grid, block, 0, s, a, k, codes, scales, status);
+            hipLaunchKernelGGL((w8_quantize_rows_kernel<false, true>), grid, block, 0, s, a, k, codes, scales, status);
     } else if (bf16) {
-        hipLaunchKernelGGL((fp8_quantize_rows_kernel<true, false>), grid, block, 0, s, a, k, codes, scales, status);
+        hipLaunchKernelGGL((w8_quantize_rows_kernel<true, false>), grid, block, 0, s, a, k, codes, scales, status);
     } else {
-        hipLaunchKernelGGL((fp8_quantize_rows_kernel<false, false>), grid, block, 0, s, a, k, codes, scales, status);
+        hipLaunchKernelGGL((w8_quantize_rows_kernel<false, false>), grid, block, 0, s, a, k, codes, scales, status);
     }
     return hipGetLastError();
 }
@@ -474,7 +478,7 @@ hipError_t launch_int8_gemm(const uint8_t* xq, const float* sx, int64_t m, const
                             hipStream_t s) {
     const int tiles_n = (int)((n + 255) / 256);
     const int64_t tiles = ((m + 127) / 128) * tiles_n;
-    hipLaunchKernelGGL(fp8_gemm_ring_kernel<true>, dim3((unsigned)tiles), dim3(512), 0, s, xq, sx,
+    hipLaunchKernelGGL(w8_gemm_ring_kernel<true>, dim3((unsigned)tiles), dim3(512), 0, s, xq, sx,
                        wq, sw, y, y_bf16 ? 1 : 0, (int)m, (int)n, (int)k, tiles_n);
     return hipGetLastError();
 }
@@ -494,7 +498,7 @@ hipError_t launch_fp8_gemm(const uint8_t* xq, const float* sx, int64_t m, const 
     if (tile != 256) {
         const int tiles_n = (int)((n + 255) / 256);
         const int64_t tiles = ((m + 127) / 128) * tiles_n;
-        hipLaunchKernelGGL(fp8_gemm_ring_kernel<false>, dim3((unsigned)tiles), dim3(512), 0, s, xq, sx,
+        hipLaunchKernelGGL(w8_gemm_ring_kernel<false>, dim3((unsigned)tiles), dim3(512), 0, s, xq, sx,
                            wq, sw, y, y_bf16 ? 1 : 0, (int)m, (int)n, (int)k, tiles_n);
         return hipGetLastError();
     }
