@@ -55,6 +55,42 @@ def test_bench_step_sampled_rows_against_oracle():
         del step
 
 
+def test_full_80_layer_step_sampled_rows_against_oracle():
+    # the headline workload at its full size: 80 fused layers (about 36 GB resident), M = 1,
+    # replayed from the captured graph exactly as the benchmark times it; 16 seeded rows of
+    # every matrix of every layer against the oracle, and two replays bit-identical
+    layers = 80
+    prepared = bench.build_stack(layers, DEV, fused=True)
+    step = bench.make_step(prepared, layers, 1, DEV, fused=True)
+    step.capture()
+    step.run()
+    torch.cuda.synchronize()
+    first = [c.y.clone() for c in step.calls]
+    step.run()
+    torch.cuda.synchronize()
+    assert all(torch.equal(c.y, f) for c, f in zip(step.calls, first)), "replays differ"
+    del first
+    order = synth.FUSED_ORDER
+    shapes = synth.LLAMA70B_FUSED_SHAPES
+    rng = np.random.default_rng(80)
+    worst = 0.0
+    for i, call in enumerate(step.calls):
+        layer, j = divmod(i, len(order))
+        name = order[j]
+        n, k = shapes[name]
+        rows = np.unique(np.concatenate([[0, n - 1], rng.choice(n, 14, replace=False)]))
+        seed = synth.seed_for(4, synth.FUSED_PARTS[name][0], layer) + 10000
+        W = synth.normal_weights(n, k, seed, DEV)
+        w32 = to_np32(W[torch.from_numpy(rows).to(DEV)])
+        del W
+        p, s, z = oracle.quantize_ref(w32)
+        x32 = to_np32(call.x)
+        r = assert_within(to_np32(call.y)[:, rows], oracle.gemv_ref(p, s, z, x32),
+                          oracle.tolerance_ref(p, s, z, x32), f"80-layer step layer {layer} {name}")
+        worst = max(worst, r)
+    print(f"80 layers: worst err/bound {worst:.3e}")
+
+
 def test_stream_read_probe_reads_without_writing():
     # the bandwidth probe leaves its sink alone unless the folded words equal its fixed
     # word; a zero buffer folds to 0, and a ragged size (not a multiple of the share)
