@@ -26,7 +26,8 @@
 // inputs loaded straight into a three-stage LDS ring two steps ahead.
 // fp8_gemm_staged_kernel (FP8, other tile shapes) stages the loads through two register
 // sets into a double-buffered LDS tile.  In LDS, 16-byte chunk c of row r sits at slot
-// c ^ (r & 7), so the operand reads of 32 rows spread over the banks.  For FP8 a lane
+// c ^ ((r / 2) & 7) (w8_slot), so the operand reads of 16 consecutive rows, which share a
+// cycle, touch 16 different 16-byte bank groups.  For FP8 a lane
 // supplies row (lane % 32) and the 32 inputs 32 * (lane / 32) .. +31 of a 64-input MFMA
 // step, the same inputs for both operands, so each output is a dot product over matching
 // inputs whatever order the unit sums them in.
@@ -141,6 +142,13 @@ __global__ __launch_bounds__(kQT) void w8_quantize_rows_kernel(const void* __res
 
 constexpr int kFK = 128;  // K step (bytes = inputs)
 
+// LDS slot of 16-byte chunk c (0..7) of tile row r (rows of 128 bytes).  A 16-lane quarter
+// of a 16-byte read takes one LDS cycle when its 16 rows hit 16 different 16-byte groups of
+// the 256-byte bank row: row r covers groups 8 (r & 1) .. +7, and c ^ ((r >> 1) & 7) spreads
+// the 8 row pairs over them (c ^ (r & 7) repeats every 8 rows: two lanes per bank group).
+// The map is its own inverse: the loader fetches chunk w8_slot(r, s) into slot s.
+__device__ __forceinline__ int w8_slot(int r, int c) { return c ^ ((r >> 1) & 7); }
+
 // Output tile (WGM * TM * 32) x (WGN * TN * 32): WGM x WGN waves, each owning TM x TN MFMA
 // tiles of 32 x 32.
 template <int TM, int TN, int WGM, int WGN>
@@ -172,13 +180,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fp8_gemm_staged_kernel(
     for (int u = 0; u < UX; ++u) {
         const int i = tid + T * u, r = i >> 3, c = i & 7;
         gx[u] = X + (int64_t)min(m0 + r, M - 1) * K + 16 * c;   // rows past M repeat M-1
-        sxo[u] = (uint32_t)(r * kFK + ((c ^ (r & 7)) << 4));
+        sxo[u] = (uint32_t)(r * kFK + (w8_slot(r, c) << 4));
     }
 #pragma unroll
     for (int u = 0; u < UW; ++u) {
         const int i = tid + T * u, r = i >> 3, c = i & 7;
         gw[u] = W + (int64_t)min(n0 + r, N - 1) * K + 16 * c;
-        swo[u] = (uint32_t)(r * kFK + ((c ^ (r & 7)) << 4));
+        swo[u] = (uint32_t)(r * kFK + (w8_slot(r, c) << 4));
     }
     // two register sets, so a step's loads are issued two steps before they are stored:
     // set 0 holds the even steps, set 1 the odd ones.  Loads past the last step repeat it
@@ -201,8 +209,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void fp8_gemm_staged_kernel(
     // the 32 inputs 64 kh + 32 (lane / 32) .. +31 of row r of an operand tile
     auto operand = [&](const uint8_t* t, int r, int kh) {
         const int c0 = 4 * kh + 2 * (lane >> 5);
-        const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(&t[r * kFK + ((c0 ^ (r & 7)) << 4)]);
-        const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(&t[r * kFK + (((c0 + 1) ^ (r & 7)) << 4)]);
+        const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(&t[r * kFK + (w8_slot(r, c0) << 4)]);
+        const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(&t[r * kFK + (w8_slot(r, c0 + 1) << 4)]);
         const v8i_t v = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                          (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
         return v;
@@ -293,8 +301,8 @@ __device__ __forceinline__ void w8_load_lds16(const void* g, uint32_t lds_addr) 
 // The same product with a three-stage LDS ring filled by direct loads two steps ahead:
 // 512 threads, 128 x 256 output tile, wave (wm, wn) owns 64 x 64 (2 x 2 MFMA tiles).  A
 // stage is the X tile (128 rows x 128 inputs, 16 KiB) and the W tile (256 x 128, 32 KiB),
-// chunk c of row r at slot c ^ (r & 7): each wave issues 2 X and 4 W loads of 8 rows x
-// 128 bytes per stage, lane l loading chunk (l % 8) ^ (row & 7) of row l / 8 so that it
+// chunk c of row r at slot w8_slot(r, c): each wave issues 2 X and 4 W loads of 8 rows x
+// 128 bytes per stage, lane l loading chunk w8_slot(row, l % 8) of row l / 8 so that it
 // lands in its swizzled slot.
 constexpr int kRingStages = 3;
 constexpr int kRingX = 128 * kFK;
@@ -326,12 +334,12 @@ __global__ __launch_bounds__(512) void w8_gemm_ring_kernel(
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int r = 8 * (2 * wave + i) + (lane >> 3);
-        xsrc[i] = X + (int64_t)min(m0 + r, M - 1) * K + 16 * ((lane & 7) ^ (r & 7));
+        xsrc[i] = X + (int64_t)min(m0 + r, M - 1) * K + 16 * w8_slot(r, lane & 7);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = 8 * (4 * wave + i) + (lane >> 3);
-        wsrc[i] = W + (int64_t)min(n0 + r, N - 1) * K + 16 * ((lane & 7) ^ (r & 7));
+        wsrc[i] = W + (int64_t)min(n0 + r, N - 1) * K + 16 * w8_slot(r, lane & 7);
     }
     const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring);
@@ -347,8 +355,8 @@ __global__ __launch_bounds__(512) void w8_gemm_ring_kernel(
     };
     auto operand = [&](const uint8_t* t, int r, int kh) {
         const int c0 = 4 * kh + 2 * (lane >> 5);
-        const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(&t[r * kFK + ((c0 ^ (r & 7)) << 4)]);
-        const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(&t[r * kFK + (((c0 + 1) ^ (r & 7)) << 4)]);
+        const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(&t[r * kFK + (w8_slot(r, c0) << 4)]);
+        const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(&t[r * kFK + (w8_slot(r, c0 + 1) << 4)]);
         const v8i_t v = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                          (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
         return v;
@@ -364,7 +372,7 @@ __global__ __launch_bounds__(512) void w8_gemm_ring_kernel(
             iacc[i][j] = (i32x16_t){};
         }
     auto chunk = [&](const uint8_t* t, int r, int c) {
-        return __builtin_bit_cast(v4i_t, *reinterpret_cast<const u32x4_t*>(&t[r * kFK + ((c ^ (r & 7)) << 4)]));
+        return __builtin_bit_cast(v4i_t, *reinterpret_cast<const u32x4_t*>(&t[r * kFK + (w8_slot(r, c) << 4)]));
     };
 
     const int Kt = K / kFK;
