@@ -65,7 +65,8 @@ def test_quantize_rows_nonfinite_sets_status():
     assert int(st.item()) & 1
 
 
-@pytest.mark.parametrize("m,n,k", [(200, 300, 384), (1, 1, 128), (129, 257, 1024), (64, 4096, 8192)])
+@pytest.mark.parametrize("m,n,k", [(200, 300, 384), (1, 1, 128), (129, 257, 1024), (64, 4096, 8192),
+                                   (3, 5, 65536)])
 def test_gemm_full_small(m, n, k):
     X = synth.normal_activations(m, k, 4300 + m, DEV)
     W = synth.normal_weights(n, k, 4301 + n, DEV)

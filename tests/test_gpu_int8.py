@@ -61,7 +61,8 @@ def test_quantize_rows_bf16_activations(rows, k):
     _check_codes(codes, steps, rc, rs, f"bf16 {rows}x{k}")
 
 
-@pytest.mark.parametrize("m,n,k", [(200, 300, 384), (1, 1, 128), (129, 257, 1024), (64, 4096, 8192)])
+@pytest.mark.parametrize("m,n,k", [(200, 300, 384), (1, 1, 128), (129, 257, 1024), (64, 4096, 8192),
+                                   (3, 5, 65536)])
 def test_gemm_full_small(m, n, k):
     X = synth.normal_activations(m, k, 5300 + m, DEV)
     W = synth.normal_weights(n, k, 5301 + n, DEV)
