@@ -314,19 +314,31 @@ constexpr int kRingStage = kRingX + kRingW;
 typedef int v4i_t __attribute__((ext_vector_type(4)));
 typedef int i32x16_t __attribute__((ext_vector_type(16)));
 
+constexpr int kW8Xcds = 8;   // accelerator complex dies of MI355X, each with its own L2
+
 template <bool INT8>
 __global__ __launch_bounds__(512) void w8_gemm_ring_kernel(
     const uint8_t* __restrict__ X, const float* __restrict__ sx, const uint8_t* __restrict__ W,
     const float* __restrict__ sw, void* __restrict__ Y, int y_bf16, int M, int N, int K,
-    int tiles_n) {
+    int tiles_m, int tiles_n, int group_m, int per_xcd) {
     __shared__ __attribute__((aligned(16))) uint8_t ring[kRingStages * kRingStage];
+    // Tile order: workgroup b runs on XCD b % 8 and each XCD takes a contiguous range of a
+    // grouped order (group_m tiles of M per band, N within the band), so the workgroups
+    // resident on one XCD cover a compact block of tiles and share X rows and W columns in
+    // that XCD's L2.  Slots past the last tile exit.
+    const int t = (int)(blockIdx.x % kW8Xcds) * per_xcd + (int)(blockIdx.x / kW8Xcds);
+    if (t >= tiles_m * tiles_n) return;
+    const int band = t / (group_m * tiles_n);
+    const int first_m = band * group_m;
+    const int gm = min(tiles_m - first_m, group_m);
+    const int rb = t - band * group_m * tiles_n;
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
     const int wm = wave >> 2;
     const int wn = wave & 3;
-    const int m0 = (int)(blockIdx.x / tiles_n) * 128;
-    const int n0 = (int)(blockIdx.x % tiles_n) * 256;
+    const int m0 = (first_m + rb % gm) * 128;
+    const int n0 = (rb / gm) * 256;
 
     // per-lane sources of this wave's loads (step 0; a step adds 128 bytes)
     const uint8_t* xsrc[2];
@@ -462,6 +474,24 @@ hipError_t launch_fp8_gemm_t(const uint8_t* xq, const float* sx, int64_t m, cons
     return hipGetLastError();
 }
 
+template <bool INT8>
+hipError_t launch_ring(const uint8_t* xq, const float* sx, int64_t m, const uint8_t* wq,
+                       const float* sw, int64_t n, int64_t k, void* y, bool y_bf16,
+                       hipStream_t s) {
+    static const int group_env = [] {
+        const char* e = getenv("W4A16_W8_GROUP_M");
+        return e ? atoi(e) : 8;
+    }();
+    const int tiles_n = (int)((n + 255) / 256);
+    const int tiles_m = (int)((m + 127) / 128);
+    const int group_m = group_env < 1 ? 1 : (group_env > tiles_m ? tiles_m : group_env);
+    const int per_xcd = (tiles_m * tiles_n + kW8Xcds - 1) / kW8Xcds;
+    hipLaunchKernelGGL(w8_gemm_ring_kernel<INT8>, dim3((unsigned)(per_xcd * kW8Xcds)), dim3(512),
+                       0, s, xq, sx, wq, sw, y, y_bf16 ? 1 : 0, (int)m, (int)n, (int)k, tiles_m,
+                       tiles_n, group_m, per_xcd);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_w8_quantize_rows(const void* a, bool bf16, int64_t rows, int64_t k,
@@ -484,11 +514,7 @@ hipError_t launch_w8_quantize_rows(const void* a, bool bf16, int64_t rows, int64
 hipError_t launch_int8_gemm(const uint8_t* xq, const float* sx, int64_t m, const uint8_t* wq,
                             const float* sw, int64_t n, int64_t k, void* y, bool y_bf16,
                             hipStream_t s) {
-    const int tiles_n = (int)((n + 255) / 256);
-    const int64_t tiles = ((m + 127) / 128) * tiles_n;
-    hipLaunchKernelGGL(w8_gemm_ring_kernel<true>, dim3((unsigned)tiles), dim3(512), 0, s, xq, sx,
-                       wq, sw, y, y_bf16 ? 1 : 0, (int)m, (int)n, (int)k, tiles_n);
-    return hipGetLastError();
+    return launch_ring<true>(xq, sx, m, wq, sw, n, k, y, y_bf16, s);
 }
 
 hipError_t launch_fp8_gemm(const uint8_t* xq, const float* sx, int64_t m, const uint8_t* wq,
@@ -503,13 +529,7 @@ hipError_t launch_fp8_gemm(const uint8_t* xq, const float* sx, int64_t m, const 
     }();
     if (tile == 128)
         return launch_fp8_gemm_t<2, 2, 2, 2>(xq, sx, m, wq, sw, n, k, y, y_bf16, s);
-    if (tile != 256) {
-        const int tiles_n = (int)((n + 255) / 256);
-        const int64_t tiles = ((m + 127) / 128) * tiles_n;
-        hipLaunchKernelGGL(w8_gemm_ring_kernel<false>, dim3((unsigned)tiles), dim3(512), 0, s, xq, sx,
-                           wq, sw, y, y_bf16 ? 1 : 0, (int)m, (int)n, (int)k, tiles_n);
-        return hipGetLastError();
-    }
+    if (tile != 256) return launch_ring<false>(xq, sx, m, wq, sw, n, k, y, y_bf16, s);
     return launch_fp8_gemm_t<2, 2, 2, 4>(xq, sx, m, wq, sw, n, k, y, y_bf16, s);
 }
 
