@@ -170,3 +170,16 @@ def test_int8_entry_points_validate_before_device_work():
     assert L.w4_int8_gemm(f(), f(), 4, f(), f(), 4, 128, f(), 7, s) == 4
     assert L.w4_int8_gemm(f(), f(), 4, f(), f(), 0, 128, f(), 0, s) == 2
     assert L.w4_int8_gemm(f(), f(), 4, f(), f(), 4, 128, f(0x100002), 0, s) == 3
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import json
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    out = json.loads(r.stdout.strip().splitlines()[-1])
+    assert "error" in out and out["n_gpus"] == 2
