@@ -269,6 +269,8 @@ w4_status w4_gemm(const void* prepared, int64_t N, int64_t K, const void* X, int
     w4_status st = check_nk(N, K);
     if (st != W4_OK) return st;
     if (M < 1 || (M + 127) / 128 > 65535) return W4_ERR_SHAPE;
+    // the tile count (128 x 256 output tiles, padded to a multiple of 8) is a grid size
+    if (((M + 127) / 128) * ((N + 255) / 256) > (int64_t)INT32_MAX - 8) return W4_ERR_SHAPE;
     if (!workspace || workspace_bytes < w4_gemm_workspace_bytes(M, N, K)) return W4_ERR_WORKSPACE;
     if (!aligned(prepared, 256) || !aligned(X, 16) || !aligned(Y, yt == W4_F32 ? 4 : 2) ||
         !aligned(workspace, 16))

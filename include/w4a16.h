@@ -217,6 +217,8 @@ w4_status w4_gemv_fmt(const void* prepared, int64_t N, int64_t K, const w4_forma
  *   workspace device scratch of w4_gemm_workspace_bytes(M, N, K) bytes (per-group
  *             sums of X; K/128 * ceil(M/128)*128 floats), 16-B aligned; contents
  *             need no initialisation.  Calls sharing a workspace must be ordered.
+ * Limits: N, K as w4_prepare; 1 <= M <= 65535*128; at most 2^31 - 9 output tiles of
+ * 128 x 256 (else W4_ERR_SHAPE).
  */
 size_t w4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 w4_status w4_gemm(const void* prepared, int64_t N, int64_t K,

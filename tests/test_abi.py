@@ -64,6 +64,11 @@ def test_validation_errors_before_device_work():
     assert L.w4_gemv(_fake(), 4, 128, _fake(), 1, 17, _fake(), 0, s) == 2
     assert L.w4_gemv(_fake(), 4, 65536, _fake(), 1, 1, _fake(), 0, s) == 2
     assert L.w4_gemm(_fake(), 4, 192, _fake(), 4, _fake(), 0, NULL, 0, s) == 2
+    # more output tiles than a grid holds
+    big = 1 << 62
+    assert L.w4_gemm(_fake(), 2**31 - 1, 128, _fake(), 65535 * 128, _fake(), 0, _fake(), big, s) == 2
+    assert L.w4_fp8_gemm(_fake(), _fake(), 2**31 - 1, _fake(), _fake(), 2**31 - 1, 128, _fake(), 0, s) == 2
+    assert L.w4_int8_gemm(_fake(), _fake(), 2**31 - 1, _fake(), _fake(), 2**31 - 1, 128, _fake(), 0, s) == 2
     # alignment
     assert L.w4_quantize(_fake(0x100004), 0, 4, 128, _fake(), _fake(), _fake(), NULL, s) == 3
     assert L.w4_gemv(_fake(0x100010), 4, 128, _fake(), 1, 1, _fake(), 0, s) == 3
