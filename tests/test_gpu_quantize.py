@@ -210,3 +210,52 @@ def test_symmetric_weights_through_gemv_and_gemm():
     assert_within(Y, oracle.gemv_ref(rp, rs, rz, x32), oracle.tolerance_ref(rp, rs, rz, x32),
                   "symmetric GEMM")
 
+
+
+def _near_half_rows(rng, rows: int, symmetric: bool):
+    """Groups whose binary32 quotients w / s lie on or within a few ulps of k + 1/2, for
+    scales that are not powers of two.  The first one or two entries fix the group's range;
+    the others are (k + 1/2) * s rounded to binary32 and moved by up to 4 ulps."""
+    out = []
+    for _ in range(rows):
+        if symmetric:
+            amax = np.float32(rng.uniform(0.01, 2.0))
+            s = np.float32(amax / np.float32(7))
+            lo, hi = -amax, amax
+            ks = rng.integers(-8, 7, 127)
+        else:
+            lo = np.float32(-rng.uniform(0.01, 2.0))
+            hi = np.float32(rng.uniform(0.01, 2.0))
+            s = np.float32(np.float32(hi - lo) / np.float32(15))
+            ks = rng.integers(-15, 15, 126)
+        base = ((ks + 0.5) * np.float64(s)).astype(np.float32)
+        moved = (base.view(np.int32) + rng.integers(-4, 5, base.size).astype(np.int32)).view(np.float32)
+        moved = np.clip(moved, lo, hi).astype(np.float32)
+        head = [hi] if symmetric else [lo, hi]
+        out.append(np.concatenate([np.array(head, dtype=np.float32), moved]))
+    return np.stack(out)
+
+
+def _half_distance(w, symmetric: bool):
+    """|w / s - nearest half| in binary32 for every weight after the range-fixing entries."""
+    w = w.astype(np.float32)
+    if symmetric:
+        s = (np.abs(w).max(axis=1) / np.float32(7)).astype(np.float32)
+    else:
+        s = ((np.maximum(w.max(axis=1), 0) - np.minimum(w.min(axis=1), 0)) / np.float32(15)).astype(np.float32)
+    q = (w / s[:, None]).astype(np.float32)
+    return np.abs(q - (np.floor(q) + np.float32(0.5)))
+
+
+@pytest.mark.parametrize("symmetric", [False, True])
+def test_quotients_on_and_near_halves_bit_exact(symmetric):
+    rng = np.random.default_rng(31 if symmetric else 30)
+    w = _near_half_rows(rng, 512, symmetric)
+    d = _half_distance(w, symmetric)
+    # the draw holds exact ties and quotients a few ulps off them on both sides
+    assert np.count_nonzero(d == 0) > 1000
+    assert np.count_nonzero((d > 0) & (d < 2.0 ** -17)) > 1000
+    gpu, st = (_gpu_quant_sym if symmetric else _gpu_quant)(torch.from_numpy(w).to(DEV))
+    assert st == 0
+    ref = oracle.quantize_symmetric_ref(w) if symmetric else oracle.quantize_ref(w)
+    assert_quant_equal(gpu, ref, "quotients on and near halves" + (" (symmetric)" if symmetric else ""))
