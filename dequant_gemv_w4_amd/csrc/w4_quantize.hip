@@ -18,14 +18,12 @@
 // even); zeros one per byte or two per byte, packed over the flat [N, K/group] array with
 // the even index in the low nibble.  The codes and the step do not depend on the storage.
 //
-// Work split: G/4 lanes own one group (4 consecutive weights each, one 16-byte
-// load of binary32 weights), a 256-thread block 1024/G groups per pass and four
-// passes over consecutive chunks, whose loads are all issued first.  The group's
-// minimum and maximum are a butterfly over those lanes; every lane then derives
-// the same scale and zero and writes its two packed bytes, so the lanes of a
-// group store its G/2 contiguous bytes.  With 4-bit zeros the first lane of an
-// even group also takes the odd group's zero (the next G/4 lanes of the same
-// wave) and writes the shared byte.
+// Work split: G/16 lanes own one group (16 weights each, four 16-byte loads of
+// binary32 weights), a 256-thread block 4096/G groups.  The group's minimum and
+// maximum are a butterfly over those lanes; every lane then derives the same scale
+// and zero and writes its eight packed bytes, so the lanes of a group store its G/2
+// bytes.  With 4-bit zeros the first lane of an even group also takes the odd
+// group's zero (the next G/16 lanes of the same wave) and writes the shared byte.
 #include <cstdlib>
 
 #include "w4_internal.h"
@@ -73,10 +71,11 @@ __device__ __forceinline__ uint16_t bf16_bits_rne(float f) {
     return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
-// LPG: lanes per group (group = 4 LPG inputs).  U: groups per thread; the block takes U
-// consecutive chunks of 256/LPG groups, and every thread issues the loads of all U before it
-// quantizes the first, so U times the bytes are in flight per wave.
-template <bool BF16, bool SYM, int LPG, int U>
+// LPG: lanes per group, each lane quantizes 16 weights of its group (group = 16 LPG
+// inputs).  Lane i of a group holds the 16-byte chunks i, i + LPG, i + 2 LPG, i + 3 LPG of
+// the group's binary32 weights, so each of the four loads of a wave covers LPG*16
+// contiguous bytes of each of its 64/LPG groups (eight full 128-byte lines at group 128).
+template <bool BF16, bool SYM, int LPG>
 __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ W, int64_t n_groups,
                                                        uint16_t* __restrict__ packed16,
                                                        uint16_t* __restrict__ scales,
@@ -84,91 +83,87 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
                                                        uint32_t* __restrict__ status,
                                                        int scale_bf16, int zero4) {
 #pragma clang fp contract(off)
-    constexpr int G = 4 * LPG;
+    constexpr int G = 16 * LPG;
     const int lane = threadIdx.x & (LPG - 1);
-    int64_t gis[U];
-    float vs[U][4];
+    const int64_t gi = (int64_t)blockIdx.x * (256 / LPG) + (threadIdx.x / LPG);
+    const bool valid = gi < n_groups;
+    float v[16];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        gis[u] = ((int64_t)blockIdx.x * U + u) * (256 / LPG) + (threadIdx.x / LPG);
+    for (int i = 0; i < 16; ++i) v[i] = 0.0f;
+    if (valid) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) vs[u][i] = 0.0f;
-        if (gis[u] < n_groups) load4<BF16>(W, gis[u] * G + lane * 4, vs[u]);
+        for (int j = 0; j < 4; ++j) load4<BF16>(W, gi * G + (lane + LPG * j) * 4, &v[4 * j]);
+    }
+    bool bad = false;
+    float lo = v[0], hi = v[0];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        bad |= !__builtin_isfinite(v[i]);
+        lo = fminf(lo, v[i]);
+        hi = fmaxf(hi, v[i]);
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int64_t gi = gis[u];
-        const bool valid = gi < n_groups;
-        const float* v = vs[u];
+    for (int d = LPG / 2; d >= 1; d >>= 1) {
+        lo = fminf(lo, __shfl_xor(lo, d, LPG));
+        hi = fmaxf(hi, __shfl_xor(hi, d, LPG));
+    }
+    float s, zc;
+    uint32_t c[16];
+    bool nonempty;
+    if constexpr (SYM) {
+        const float amax = fmaxf(fabsf(lo), fabsf(hi));
+        nonempty = amax > 0.0f;
+        s = nonempty ? amax / 7.0f : 1.0f;    // IEEE division
+        zc = 8.0f;
+        const float r = __builtin_amdgcn_rcpf(s);
+        const bool rcp_ok = s >= 0x1p-120f && s <= 0x1p120f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {   // rintf: halves to even; a NaN quotient clamps to -8
+            const float t = v[i] * r;
+            const float q = (rcp_ok && clear_of_half(t)) ? rintf(t) : rintf(v[i] / s);
+            c[i] = (uint32_t)(fminf(fmaxf(q, -8.0f), 7.0f) + 8.0f);
+        }
+    } else {
+        lo = fminf(lo, 0.0f);  // zero stays exactly representable
+        hi = fmaxf(hi, 0.0f);
+        nonempty = hi > lo;
+        s = nonempty ? (hi - lo) / 15.0f : 1.0f;   // IEEE division
+        zc = clamp_code_keep_nan(roundf(-lo / s));  // roundf: halves away from zero
+        const float r = __builtin_amdgcn_rcpf(s);
+        const bool rcp_ok = s >= 0x1p-120f && s <= 0x1p120f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float t = v[i] * r;
+            const float q = (rcp_ok && clear_of_half(t)) ? rintf(t) : roundf(v[i] / s);
+            c[i] = to_code(q + zc);
+        }
+    }
+    const uint32_t zbyte = to_code(zc);
+    // the odd neighbour's zero, LPG lanes up in the same wave (64 / LPG groups per wave, an
+    // even number, so an even group's partner never crosses the wave)
+    const uint32_t zodd = __shfl((int)zbyte, (int)(threadIdx.x & 63) + LPG, 64) & 0xFu;
 
-        bool bad = false;
-        float lo = v[0], hi = v[0];
+    if (valid) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            bad |= !__builtin_isfinite(v[i]);
-            lo = fminf(lo, v[i]);
-            hi = fmaxf(hi, v[i]);
-        }
-#pragma unroll
-        for (int d = LPG / 2; d >= 1; d >>= 1) {
-            lo = fminf(lo, __shfl_xor(lo, d, LPG));
-            hi = fmaxf(hi, __shfl_xor(hi, d, LPG));
-        }
-        float s, zc;
-        uint32_t c[4];
-        bool nonempty;
-        if constexpr (SYM) {
-            const float amax = fmaxf(fabsf(lo), fabsf(hi));
-            nonempty = amax > 0.0f;
-            s = nonempty ? amax / 7.0f : 1.0f;    // IEEE division
-            zc = 8.0f;
-            const float r = __builtin_amdgcn_rcpf(s);
-            const bool rcp_ok = s >= 0x1p-120f && s <= 0x1p120f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {   // rintf: halves to even; a NaN quotient clamps to -8
-                const float t = v[i] * r;
-                const float q = (rcp_ok && clear_of_half(t)) ? rintf(t) : rintf(v[i] / s);
-                c[i] = (uint32_t)(fminf(fmaxf(q, -8.0f), 7.0f) + 8.0f);
+        for (int j = 0; j < 4; ++j)
+            packed16[gi * (G / 4) + lane + LPG * j] =
+                (uint16_t)(c[4 * j] | (c[4 * j + 1] << 4) | (c[4 * j + 2] << 8) | (c[4 * j + 3] << 12));
+        if (bad && status) atomicOr(status, 1u);  // W4_STATUS_NONFINITE
+        if (lane == 0) {
+            const uint16_t s16 = scale_bf16 ? bf16_bits_rne(s)
+                                            : __builtin_bit_cast(uint16_t, (_Float16)s);  // nearest even
+            const uint32_t inf_bits = scale_bf16 ? 0x7F80u : 0x7C00u;
+            scales[gi] = s16;
+            if (!zero4) {
+                zeros[gi] = (uint8_t)zbyte;
+            } else if ((gi & 1) == 0) {
+                const bool pair = gi + 1 < n_groups;
+                zeros[gi >> 1] = (uint8_t)(zbyte | (pair ? zodd << 4 : 0u));
             }
-        } else {
-            lo = fminf(lo, 0.0f);  // zero stays exactly representable
-            hi = fmaxf(hi, 0.0f);
-            nonempty = hi > lo;
-            s = nonempty ? (hi - lo) / 15.0f : 1.0f;   // IEEE division
-            zc = clamp_code_keep_nan(roundf(-lo / s));  // roundf: halves away from zero
-            const float r = __builtin_amdgcn_rcpf(s);
-            const bool rcp_ok = s >= 0x1p-120f && s <= 0x1p120f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float t = v[i] * r;
-                const float q = (rcp_ok && clear_of_half(t)) ? rintf(t) : roundf(v[i] / s);
-                c[i] = to_code(q + zc);
-            }
-        }
-        const uint32_t zbyte = to_code(zc);
-        // the odd neighbour's zero, LPG lanes up in the same wave (64 / LPG groups per wave, an
-        // even number, so an even group's partner never crosses the wave)
-        const uint32_t zodd = __shfl((int)zbyte, (int)(threadIdx.x & 63) + LPG, 64) & 0xFu;
-
-        if (valid) {
-            packed16[gi * LPG + lane] = (uint16_t)(c[0] | (c[1] << 4) | (c[2] << 8) | (c[3] << 12));
-            if (bad && status) atomicOr(status, 1u);  // W4_STATUS_NONFINITE
-            if (lane == 0) {
-                const uint16_t s16 = scale_bf16 ? bf16_bits_rne(s)
-                                                : __builtin_bit_cast(uint16_t, (_Float16)s);  // nearest even
-                const uint32_t inf_bits = scale_bf16 ? 0x7F80u : 0x7C00u;
-                scales[gi] = s16;
-                if (!zero4) {
-                    zeros[gi] = (uint8_t)zbyte;
-                } else if ((gi & 1) == 0) {
-                    const bool pair = gi + 1 < n_groups;
-                    zeros[gi >> 1] = (uint8_t)(zbyte | (pair ? zodd << 4 : 0u));
-                }
-                uint32_t flags = 0;
-                if ((s16 & 0x7FFFu) == inf_bits) flags |= 2u;           // W4_STATUS_SCALE_OVERFLOW
-                if ((s16 & 0x7FFFu) == 0 && nonempty) flags |= 4u;     // W4_STATUS_SCALE_ZERO
-                if (flags && status) atomicOr(status, flags);
-            }
+            uint32_t flags = 0;
+            if ((s16 & 0x7FFFu) == inf_bits) flags |= 2u;           // W4_STATUS_SCALE_OVERFLOW
+            if ((s16 & 0x7FFFu) == 0 && nonempty) flags |= 4u;     // W4_STATUS_SCALE_ZERO
+            if (flags && status) atomicOr(status, flags);
         }
     }
 }
@@ -255,29 +250,22 @@ int64_t elementwise_blocks(int64_t work) {
 hipError_t launch_quantize(const void* W, bool bf16, const Fmt& f, int64_t n_groups,
                            uint8_t* packed, uint16_t* scales, uint8_t* zeros, uint32_t* status,
                            hipStream_t s) {
-    const int lpg = f.group / 4;
-    // four groups per thread: 0.224-0.228 ms against 0.272-0.275 ms for one (28672 x 8192
-    // binary32 on MI355X, fastest of ten calls; eight measured the same as four)
-    static const int unroll_env = [] {
-        const char* e = getenv("W4A16_QUANT_UNROLL");
-        return e ? atoi(e) : 4;
-    }();
-    const int unroll = unroll_env == 1 ? 1 : 4;
-    const int64_t per_block = (int64_t)(256 / lpg) * unroll;
-    const int64_t blocks = (n_groups + per_block - 1) / per_block;
+    // 16 weights per lane: 0.198-0.209 ms against 0.224-0.31 ms with 4 weights per lane
+    // (28672 x 8192 binary32 on MI355X; vector instructions 66 M against 119 M per call)
+    const int lpg = f.group / 16;
+    const int64_t blocks = (n_groups + (256 / lpg) - 1) / (256 / lpg);
     uint16_t* p16 = reinterpret_cast<uint16_t*>(packed);
-#define W4_Q(LPG, UN)                                                                          \
-    if (lpg == LPG && unroll == UN) {                                                          \
-        auto kern = bf16 ? (f.symmetric ? quantize_kernel<true, true, LPG, UN>                 \
-                                        : quantize_kernel<true, false, LPG, UN>)               \
-                         : (f.symmetric ? quantize_kernel<false, true, LPG, UN>                \
-                                        : quantize_kernel<false, false, LPG, UN>);             \
+#define W4_Q(LPG)                                                                              \
+    if (lpg == LPG) {                                                                          \
+        auto kern = bf16 ? (f.symmetric ? quantize_kernel<true, true, LPG>                     \
+                                        : quantize_kernel<true, false, LPG>)                   \
+                         : (f.symmetric ? quantize_kernel<false, true, LPG>                    \
+                                        : quantize_kernel<false, false, LPG>);                 \
         hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, s, W, n_groups, p16,    \
                            scales, zeros, status, f.scale_bf16 ? 1 : 0, f.zero4 ? 1 : 0);      \
         return hipGetLastError();                                                              \
     }
-    W4_Q(32, 1) W4_Q(16, 1) W4_Q(8, 1)
-    W4_Q(32, 4) W4_Q(16, 4) W4_Q(8, 4)
+    W4_Q(8) W4_Q(4) W4_Q(2)
 #undef W4_Q
     return hipErrorInvalidValue;
 }
