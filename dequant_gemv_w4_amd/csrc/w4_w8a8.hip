@@ -16,7 +16,8 @@
 //     matrix cores take as format 0; a value that rounds to zero keeps its sign;
 //   * INT8: the step is the largest magnitude over 127; codes are the quotients rounded to
 //     the nearest integer, halves to even, clamped to [-128, 127].
-// The scale is stored as binary32.
+// The scale is stored as binary32.  The kernel gives the codes of that binary64 arithmetic
+// while rounding most values in binary32 (e4m3_byte_recip, int8_byte_recip).
 //
 // Product: Y[m, n] = sx[m] * sw[n] * sum_k qx[m, k] * qw[n, k].  FP8 runs on
 // v_mfma_scale_f32_32x32x64_f8f6f4 (block scales left at 2^0) with binary32 accumulation
@@ -45,16 +46,18 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 constexpr int kQT = 256;          // threads of a quantizer workgroup (one row)
 constexpr double kFp8Max = 448.0;
 
-// E4M3 byte of a binary64 quotient t (the rounding described at the top of the file)
-__device__ __forceinline__ uint32_t e4m3_byte(double t) {
-    if (t == 0.0) return 0u;
-    const uint32_t sign = t < 0.0 ? 0x80u : 0u;
-    const double mag = fmin(fabs(t), kFp8Max);
+// E4M3 rounding of a magnitude m <= 448: u = m in units of its grid step 2^(ex-3)
+// (ex = its binary exponent, at least -6); scaling by a power of two is exact
+__device__ __forceinline__ double e4m3_units(double m, int& ex) {
     int e = 0;
-    (void)frexp(mag, &e);                          // mag = f * 2^e, f in [0.5, 1)
-    const int ex = max(e - 1, -6);
-    const double grid = ldexp(1.0, ex - 3);
-    const double r = fmin(rint(mag / grid) * grid, kFp8Max);
+    (void)frexp(m, &e);                            // m = f * 2^e, f in [0.5, 1)
+    ex = max(e - 1, -6);
+    return ldexp(m, 3 - ex);
+}
+
+// byte of the rounded magnitude q * 2^(ex-3) with the given sign bit
+__device__ __forceinline__ uint32_t e4m3_encode(uint32_t sign, double q, int ex) {
+    const double r = fmin(ldexp(q, ex - 3), kFp8Max);
     if (r == 0.0) return sign;
     if (r < 0x1p-6) return sign | (uint32_t)(r * 512.0);   // subnormal: r = m * 2^-9
     int E = 0;
@@ -62,8 +65,44 @@ __device__ __forceinline__ uint32_t e4m3_byte(double t) {
     return sign | ((uint32_t)(E + 6) << 3) | (uint32_t)((2.0 * f - 1.0) * 8.0);
 }
 
+// E4M3 byte of a binary64 quotient t (the rounding described at the top of the file)
+__device__ __forceinline__ uint32_t e4m3_byte(double t) {
+    if (t == 0.0) return 0u;
+    int ex = 0;
+    const double u = e4m3_units(fmin(fabs(t), kFp8Max), ex);
+    return e4m3_encode(t < 0.0 ? 0x80u : 0u, rint(u), ex);
+}
+
+// The codes without binary64 arithmetic per value.  r32 is 1 / s (correctly rounded in
+// binary64, then to binary32), so t = v * r32 in binary32 is within 2^-23 relative of v / s
+// and of its correctly rounded binary64 quotient.  In grid units (below 16 for E4M3, below
+// 128 for INT8) the two differ by less than 2^-19 and 2^-16; where t lies more than 2^-17
+// (E4M3) or 2^-13 (INT8) from a rounding boundary both give the same code.  The other
+// values (a few in 10^5), non-finite ones and scales outside [2^-100, 2^100] take the
+// binary64 quotient.  An E4M3 quotient below 2^-12 rounds to a zero with the sign of v.
+__device__ __forceinline__ bool clear_of_half(float u, float margin) {
+    return fabsf(__builtin_amdgcn_fractf(u) - 0.5f) > margin;
+}
+
+__device__ __forceinline__ uint32_t e4m3_byte_recip(float v, double s, float r32, bool rcp_ok) {
+    if (rcp_ok) {
+        const float m = fabsf(v * r32);
+        const uint32_t sign = v < 0.0f ? 0x80u : 0u;
+        if (m < 0x1p-12f) return sign;
+        const int ex = max(__builtin_amdgcn_frexp_expf(m) - 1, -6);   // binary exponent
+        const float u = ldexpf(m, 3 - ex);                              // in units of 2^(ex-3)
+        // below 448 * (1 + 2^-22), so u < 14.5 at ex = 8: no value rounds past 448
+        if (clear_of_half(u, 0x1p-17f)) {
+            // the byte of q * 2^(ex-3): exponent field ex + 7 and mantissa q - 8 for
+            // 8 <= q <= 16 (q = 16 carries into the exponent), the subnormal q < 8 at ex = -6
+            return sign | (uint32_t)(8 * ex + 48 + (int)rintf(u));
+        }
+    }
+    return e4m3_byte((double)v / s);
+}
+
 template <bool IN_BF16>
-__device__ __forceinline__ void load8(const void* a, int64_t i, float (&v)[8]) {
+__device__ __forceinline__ void load8(const void* a, int64_t i, float* v) {
     if constexpr (IN_BF16) {
         const u32x4_t w = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(a) + i);
 #pragma unroll
@@ -90,6 +129,35 @@ __device__ __forceinline__ uint32_t int8_byte(double t) {
     return (uint32_t)(uint8_t)(int8_t)(int)q;
 }
 
+__device__ __forceinline__ uint32_t int8_byte_recip(float v, double s, float r32, bool rcp_ok) {
+    const float t = v * r32;
+    if (rcp_ok && clear_of_half(t, 0x1p-13f))   // |t| <= 127 (1 + 2^-22): no clamp needed
+        return (uint32_t)(uint8_t)(int8_t)(int)rintf(t);
+    return int8_byte((double)v / s);
+}
+
+// values per thread kept in registers between the two steps when K <= kQT * kQVals
+constexpr int kQVals = 32;
+
+template <bool INT8>
+__device__ __forceinline__ uint2 w8_codes8(const float* v, double s, float rs, bool rcp_ok) {
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        if constexpr (INT8) {
+            lo |= int8_byte_recip(v[q], s, rs, rcp_ok) << (8 * q);
+            hi |= int8_byte_recip(v[4 + q], s, rs, rcp_ok) << (8 * q);
+        } else {
+            lo |= e4m3_byte_recip(v[q], s, rs, rcp_ok) << (8 * q);
+            hi |= e4m3_byte_recip(v[4 + q], s, rs, rcp_ok) << (8 * q);
+        }
+    }
+    return make_uint2(lo, hi);
+}
+
+// One workgroup per row.  Rows of up to kQT * kQVals values are loaded once, all loads
+// issued before the first is used, and kept in registers for the second step; longer rows
+// are read twice in a loop.
 template <bool IN_BF16, bool INT8>
 __global__ __launch_bounds__(kQT) void w8_quantize_rows_kernel(const void* __restrict__ a,
                                                                 int64_t K,
@@ -100,15 +168,36 @@ __global__ __launch_bounds__(kQT) void w8_quantize_rows_kernel(const void* __res
     const int64_t row = blockIdx.x;
     const void* src = IN_BF16 ? (const void*)(static_cast<const uint16_t*>(a) + row * K)
                               : (const void*)(static_cast<const float*>(a) + row * K);
+    uint8_t* dst = codes + row * K;
+    const bool cached = K <= (int64_t)kQT * kQVals;
+    float vc[kQVals];
     float amax = 0.0f;
     bool finite = true;
-    for (int64_t i = (int64_t)threadIdx.x * 8; i < K; i += kQT * 8) {
-        float v[8];
-        load8<IN_BF16>(src, i, v);
+    if (cached) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            finite &= isfinite(v[q]);
-            amax = fmaxf(amax, fabsf(v[q]));
+        for (int c = 0; c < kQVals / 8; ++c) {
+            const int64_t i = (int64_t)threadIdx.x * 8 + (int64_t)c * kQT * 8;
+            if (i < K) {
+                load8<IN_BF16>(src, i, &vc[8 * c]);
+            } else {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) vc[8 * c + q] = 0.0f;
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < kQVals; ++q) {
+            finite &= isfinite(vc[q]);
+            amax = fmaxf(amax, fabsf(vc[q]));
+        }
+    } else {
+        for (int64_t i = (int64_t)threadIdx.x * 8; i < K; i += kQT * 8) {
+            float v[8];
+            load8<IN_BF16>(src, i, v);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                finite &= isfinite(v[q]);
+                amax = fmaxf(amax, fabsf(v[q]));
+            }
         }
     }
 #pragma unroll
@@ -121,22 +210,20 @@ __global__ __launch_bounds__(kQT) void w8_quantize_rows_kernel(const void* __res
     for (int w = 1; w < kQT / 64; ++w) amax = fmaxf(amax, wmax[w]);
     const double s = amax == 0.0f ? 1.0 : (double)amax / (INT8 ? 127.0 : kFp8Max);
     if (threadIdx.x == 0) scales[row] = (float)s;
-    uint8_t* dst = codes + row * K;
-    for (int64_t i = (int64_t)threadIdx.x * 8; i < K; i += kQT * 8) {
-        float v[8];
-        load8<IN_BF16>(src, i, v);
-        uint32_t lo = 0, hi = 0;
+    const float rs = (float)(1.0 / s);
+    const bool rcp_ok = s >= 0x1p-100 && s <= 0x1p100;
+    if (cached) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            if constexpr (INT8) {
-                lo |= int8_byte((double)v[q] / s) << (8 * q);
-                hi |= int8_byte((double)v[4 + q] / s) << (8 * q);
-            } else {
-                lo |= e4m3_byte((double)v[q] / s) << (8 * q);
-                hi |= e4m3_byte((double)v[4 + q] / s) << (8 * q);
-            }
+        for (int c = 0; c < kQVals / 8; ++c) {
+            const int64_t i = (int64_t)threadIdx.x * 8 + (int64_t)c * kQT * 8;
+            if (i < K) *reinterpret_cast<uint2*>(dst + i) = w8_codes8<INT8>(&vc[8 * c], s, rs, rcp_ok);
         }
-        *reinterpret_cast<uint2*>(dst + i) = make_uint2(lo, hi);
+    } else {
+        for (int64_t i = (int64_t)threadIdx.x * 8; i < K; i += kQT * 8) {
+            float v[8];
+            load8<IN_BF16>(src, i, v);
+            *reinterpret_cast<uint2*>(dst + i) = w8_codes8<INT8>(v, s, rs, rcp_ok);
+        }
     }
 }
 

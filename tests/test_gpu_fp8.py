@@ -46,7 +46,28 @@ def test_quantize_rows_bit_exact_edge_rows():
     assert np.count_nonzero(rc[2] == 0x80) > 0 and np.count_nonzero((rc[2] & 0x78) == 0) > 100
 
 
-@pytest.mark.parametrize("rows,k", [(77, 8192), (5, 128), (130, 384)])
+def test_quantize_rows_exact_and_near_midpoints():
+    # rows whose largest magnitude is 448 * 2^j make the scale a power of two, so the
+    # quotients are the values themselves scaled: put them on the midpoints between
+    # neighbouring E4M3 values (exact ties, halves to even) and one binary32 ulp either side
+    pos = oracle.E4M3_VALUES[1:0x7F]
+    mids = ((pos[:-1] + pos[1:]) / 2).astype(np.float32)
+    rows = []
+    for j in (-3, 0, 5):
+        base = np.concatenate([mids, -mids, np.nextafter(mids, np.float32(0)),
+                               np.nextafter(mids, np.float32(1000))]).astype(np.float32)
+        base = np.resize(base, 1024).astype(np.float32)
+        base[0] = 448.0
+        rows.append((base * np.float32(2.0 ** j)).astype(np.float32))
+    a = np.stack(rows)
+    codes, scales = w4.w4_fp8_quantize_rows(torch.from_numpy(a).to(DEV))
+    torch.cuda.synchronize()
+    rc, rs = oracle.quantize_rows_fp8_ref(a)
+    assert np.all(rs == np.float32(2.0) ** np.array([-3, 0, 5], dtype=np.float32))
+    _check_codes(codes, scales, rc, rs, "midpoint rows")
+
+
+@pytest.mark.parametrize("rows,k", [(77, 8192), (5, 128), (130, 384), (3, 8320), (2, 65536)])
 def test_quantize_rows_bf16_activations(rows, k):
     X = synth.normal_activations(rows, k, 4200 + rows, DEV)
     X[:, : max(1, k // 100)] *= 20                # outlier channels

@@ -51,7 +51,7 @@ def test_quantize_rows_bit_exact_edge_rows():
     assert rc[1, 9] == -127 and rc[2, 0] == -32 and rc[2, 1] == -30
 
 
-@pytest.mark.parametrize("rows,k", [(77, 8192), (5, 128), (130, 384)])
+@pytest.mark.parametrize("rows,k", [(77, 8192), (5, 128), (130, 384), (3, 8320), (2, 65536)])
 def test_quantize_rows_bf16_activations(rows, k):
     X = synth.normal_activations(rows, k, 5200 + rows, DEV)
     X[:, : max(1, k // 100)] *= 20
