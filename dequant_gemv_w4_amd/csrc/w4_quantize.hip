@@ -41,7 +41,7 @@ __device__ __forceinline__ float clamp_code_keep_nan(float t) {
 // rounded quotient within 2^-24 relative; for |v / s| < 16, the range of every in-group
 // quotient, the two differ by less than 2^-18.  So where t lies more than 2^-17 from the
 // nearest k + 1/2, the rounded quotient and rintf(t) are the same integer.  Only the
-// other weights (about 3 in 10^5 of random data), NaN and infinite values, and groups
+// other weights (a window of 2^-16 per unit: about 1.5 in 10^5), NaN and infinite values, and groups
 // whose scale falls outside [2^-120, 2^120] take the IEEE division.
 __device__ __forceinline__ bool clear_of_half(float t) {
     return fabsf(__builtin_amdgcn_fractf(t) - 0.5f) > 0x1p-17f;
