@@ -474,11 +474,23 @@ def cpu_baseline():
     except Exception:
         pass
     del np
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
+    rate = nbytes / dt
+    step_bytes = 80 * sum(synth.LLAMA70B_FUSED_SHAPES[m][0] * synth.LLAMA70B_FUSED_SHAPES[m][1] // 2
+                          + synth.LLAMA70B_FUSED_SHAPES[m][0] * synth.LLAMA70B_FUSED_SHAPES[m][1] // 128 * 3
+                          + synth.LLAMA70B_FUSED_SHAPES[m][1] * 2 + synth.LLAMA70B_FUSED_SHAPES[m][0] * 4
+                          for m in synth.FUSED_ORDER)
+    return {"value": round(rate / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": f"70B o_proj {n}x{k}, M=1: oracle fp64 dequantize-then-dot (gemv_ref), "
                       f"{reps} repetitions, {dt:.2f} s each; quantization untimed",
-            "host_cpus": len(os.sched_getaffinity(0))}
+            "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": model,
+            "decode_step_s_extrapolated": round(step_bytes / rate, 1)}
 
 
 def main() -> int:
