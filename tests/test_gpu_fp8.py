@@ -133,3 +133,27 @@ def test_prefill_shape_sampled_outputs():
     # bf16 output: the binary32 result rounded to nearest even
     gb = to_np32(Yb)[np.ix_(rm, rn)]
     assert np.array_equal(gb, to_np32(torch.from_numpy(got).to(torch.bfloat16)))
+
+
+def test_quantize_rows_near_midpoints_general_scales():
+    # arbitrary row maxima (scales that are not powers of two); the other values are E4M3
+    # midpoints times the row's binary64 scale, rounded to binary32 and moved by 0 to 24
+    # ulps, so their quotients fall on both sides of every rounding decision the kernel's
+    # binary32 path could get wrong
+    rng = np.random.default_rng(61)
+    pos = oracle.E4M3_VALUES[1:0x7F]
+    mids = (pos[:-1] + pos[1:]) / 2
+    rows = []
+    for _ in range(256):
+        amax = np.float32(rng.uniform(0.5, 4.0) * 2.0 ** rng.integers(-20, 20))
+        s = np.float64(amax) / 448.0
+        pick = rng.choice(mids, 1023) * rng.choice([-1.0, 1.0], 1023)
+        base = (pick * s).astype(np.float32)
+        moved = (base.view(np.int32) + rng.integers(-24, 25, 1023).astype(np.int32)).view(np.float32)
+        moved = np.clip(moved, -amax, amax).astype(np.float32)
+        rows.append(np.concatenate([[amax], moved]).astype(np.float32))
+    a = np.stack(rows)
+    codes, scales = w4.w4_fp8_quantize_rows(torch.from_numpy(a).to(DEV))
+    torch.cuda.synchronize()
+    rc, rs = oracle.quantize_rows_fp8_ref(a)
+    _check_codes(codes, scales, rc, rs, "near-midpoint rows, general scales")

@@ -107,3 +107,24 @@ def test_prefill_shape_sampled_outputs():
     gb = to_np32(Yb)[np.ix_(rm, rn)]
     assert np.array_equal(gb, to_np32(torch.from_numpy(got).to(torch.bfloat16)))
     print(f"prefill shape: worst err/bound {r:.3e}")
+
+
+def test_quantize_rows_near_halves_general_scales():
+    # arbitrary row maxima; the other values are (k + 1/2) times the row's binary64 step,
+    # rounded to binary32 and moved by 0 to 24 ulps (both sides of the kernel's binary32
+    # rounding decisions)
+    rng = np.random.default_rng(62)
+    rows = []
+    for _ in range(256):
+        amax = np.float32(rng.uniform(0.5, 4.0) * 2.0 ** rng.integers(-20, 20))
+        s = np.float64(amax) / 127.0
+        k = rng.integers(-127, 127, 1023) + 0.5
+        base = (k * s).astype(np.float32)
+        moved = (base.view(np.int32) + rng.integers(-24, 25, 1023).astype(np.int32)).view(np.float32)
+        moved = np.clip(moved, -amax, amax).astype(np.float32)
+        rows.append(np.concatenate([[amax], moved]).astype(np.float32))
+    a = np.stack(rows)
+    codes, steps = w4.w4_int8_quantize_rows(torch.from_numpy(a).to(DEV))
+    torch.cuda.synchronize()
+    rc, rs = oracle.quantize_rows_int8_ref(a)
+    _check_codes(codes, steps, rc, rs, "near-half rows, general steps")
