@@ -212,10 +212,10 @@ def test_symmetric_weights_through_gemv_and_gemm():
 
 
 
-def _near_half_rows(rng, rows: int, symmetric: bool):
+def _near_half_rows(rng, rows: int, symmetric: bool, max_ulps: int = 4):
     """Groups whose binary32 quotients w / s lie on or within a few ulps of k + 1/2, for
     scales that are not powers of two.  The first one or two entries fix the group's range;
-    the others are (k + 1/2) * s rounded to binary32 and moved by up to 4 ulps."""
+    the others are (k + 1/2) * s rounded to binary32 and moved by up to max_ulps ulps."""
     out = []
     for _ in range(rows):
         if symmetric:
@@ -229,7 +229,7 @@ def _near_half_rows(rng, rows: int, symmetric: bool):
             s = np.float32(np.float32(hi - lo) / np.float32(15))
             ks = rng.integers(-15, 15, 126)
         base = ((ks + 0.5) * np.float64(s)).astype(np.float32)
-        moved = (base.view(np.int32) + rng.integers(-4, 5, base.size).astype(np.int32)).view(np.float32)
+        moved = (base.view(np.int32) + rng.integers(-max_ulps, max_ulps + 1, base.size).astype(np.int32)).view(np.float32)
         moved = np.clip(moved, lo, hi).astype(np.float32)
         head = [hi] if symmetric else [lo, hi]
         out.append(np.concatenate([np.array(head, dtype=np.float32), moved]))
@@ -247,14 +247,17 @@ def _half_distance(w, symmetric: bool):
     return np.abs(q - (np.floor(q) + np.float32(0.5)))
 
 
-@pytest.mark.parametrize("symmetric", [False, True])
-def test_quotients_on_and_near_halves_bit_exact(symmetric):
-    rng = np.random.default_rng(31 if symmetric else 30)
-    w = _near_half_rows(rng, 512, symmetric)
+@pytest.mark.parametrize("symmetric,max_ulps", [(False, 4), (True, 4), (False, 24), (True, 24)])
+def test_quotients_on_and_near_halves_bit_exact(symmetric, max_ulps):
+    rng = np.random.default_rng((31 if symmetric else 30) + max_ulps)
+    w = _near_half_rows(rng, 512, symmetric, max_ulps)
     d = _half_distance(w, symmetric)
-    # the draw holds exact ties and quotients a few ulps off them on both sides
-    assert np.count_nonzero(d == 0) > 1000
+    # the draw holds exact ties and quotients off them on both sides, inside the kernel's
+    # window of 2^-17 around each half (exact division) and, with 24 ulps, just outside it
+    assert np.count_nonzero(d == 0) > 100
     assert np.count_nonzero((d > 0) & (d < 2.0 ** -17)) > 1000
+    if max_ulps > 8:
+        assert np.count_nonzero((d > 2.0 ** -17) & (d < 2.0 ** -15)) > 1000
     gpu, st = (_gpu_quant_sym if symmetric else _gpu_quant)(torch.from_numpy(w).to(DEV))
     assert st == 0
     ref = oracle.quantize_symmetric_ref(w) if symmetric else oracle.quantize_ref(w)
