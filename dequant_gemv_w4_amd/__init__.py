@@ -20,8 +20,6 @@ __all__ = [
     "w4_gemv", "w4_gemm_workspace_bytes", "w4_gemm",
     "w4_status_string", "w4_last_hip_error", "w4_format_version", "w4_stream_read",
     "w4_fp8_quantize_rows", "w4_fp8_gemm", "w4_int8_quantize_rows", "w4_int8_gemm",
-    "W4ChainGemv", "w4_chain_plan_bytes", "w4_chain_workspace_bytes", "w4_chain_plan",
-    "w4_chain_run",
     "W4Format", "w4_zeros_bytes", "w4_quantize_fmt", "w4_prepared_bytes_fmt", "w4_prepare_fmt",
     "w4_unprepare_fmt", "w4_gemv_fmt",
     "W4_OK", "W4_F32", "W4_BF16", "GROUP",
@@ -107,14 +105,6 @@ def lib() -> ctypes.CDLL:
     L.w4_int8_quantize_rows.restype = i32
     L.w4_int8_gemm.argtypes = [vp, vp, i64, vp, vp, i64, i64, vp, i32, vp]
     L.w4_int8_gemm.restype = i32
-    L.w4_chain_plan_bytes.argtypes = [i64]
-    L.w4_chain_plan_bytes.restype = sz
-    L.w4_chain_workspace_bytes.argtypes = [i64]
-    L.w4_chain_workspace_bytes.restype = sz
-    L.w4_chain_plan.argtypes = [vp, i64, vp, sz]
-    L.w4_chain_plan.restype = i32
-    L.w4_chain_run.argtypes = [vp, vp, vp, sz, vp]
-    L.w4_chain_run.restype = i32
     fp = ctypes.POINTER(W4Format)
     L.w4_zeros_bytes.argtypes = [i64, i64, fp]
     L.w4_zeros_bytes.restype = sz
@@ -434,61 +424,6 @@ def w4_gemm(prepared, N: int, K: int, X, Y=None, out_dtype=None, workspace=None)
     _check(lib().w4_gemm(_ptr(prepared), N, K, _ptr(X), M, _ptr(Y), yt, ws_ptr, ws_len,
                          _stream(X)), "w4_gemm")
     return Y
-
-
-# --------------------------------------------------------------------------
-# GEMV chain (one persistent launch for a dependency-ordered list of GEMVs)
-# --------------------------------------------------------------------------
-
-class W4ChainGemv(ctypes.Structure):
-    """Mirror of the C struct w4_chain_gemv."""
-    _fields_ = [("prepared", ctypes.c_void_p), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p),
-                ("n", ctypes.c_int64), ("k", ctypes.c_int64), ("stage", ctypes.c_int32),
-                ("y_dtype", ctypes.c_int32)]
-
-
-def w4_chain_plan_bytes(count: int) -> int:
-    return int(lib().w4_chain_plan_bytes(int(count)))
-
-
-def w4_chain_workspace_bytes(count: int) -> int:
-    return int(lib().w4_chain_workspace_bytes(int(count)))
-
-
-def w4_chain_plan(entries):
-    """entries: iterable of (prepared, x [K] bf16, y [N] f32/bf16, N, K, stage).
-
-    Returns the plan as a host uint8 NumPy array (copy it unchanged to the GPU).
-    """
-    import numpy as np
-    import torch
-    entries = list(entries)
-    arr = (W4ChainGemv * len(entries))()
-    for i, (prep, x, y, n, k, stage) in enumerate(entries):
-        _require(prep, torch.uint8, None, "prepared")
-        _require(x, torch.bfloat16, None, "x")
-        _require(y, (torch.float32, torch.bfloat16), None, "y")
-        if x.numel() != k or y.numel() != n:
-            raise ValueError(f"entry {i}: x must hold K and y N elements")
-        if prep.numel() < w4_prepared_bytes(n, k):
-            raise ValueError(f"entry {i}: prepared buffer too small")
-        arr[i] = W4ChainGemv(prep.data_ptr(), x.data_ptr(), y.data_ptr(), int(n), int(k),
-                             int(stage), W4_F32 if y.dtype == torch.float32 else W4_BF16)
-    nbytes = w4_chain_plan_bytes(len(entries))
-    plan = np.zeros(nbytes, dtype=np.uint8)
-    _check(lib().w4_chain_plan(ctypes.cast(arr, ctypes.c_void_p), len(entries),
-                               ctypes.c_void_p(plan.ctypes.data), nbytes), "w4_chain_plan")
-    return plan
-
-
-def w4_chain_run(plan_dev, plan_host, workspace) -> None:
-    """Launch a planned chain on the current stream (workspace: zero-filled int32 tensor)."""
-    import torch
-    _require(plan_dev, torch.uint8, None, "plan_dev")
-    _require(workspace, torch.int32, None, "workspace")
-    _check(lib().w4_chain_run(_ptr(plan_dev), ctypes.c_void_p(plan_host.ctypes.data),
-                              _ptr(workspace), workspace.numel() * 4, _stream(plan_dev)),
-           "w4_chain_run")
 
 
 # --------------------------------------------------------------------------

@@ -19,7 +19,7 @@ OUT = os.path.join(PKG, "libw4a16.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["w4_api.hip", "w4_quantize.hip", "w4_gemv.hip", "w4_gemv_mfma.hip", "w4_gemm.hip",
-           "w4_chain.hip", "w4_probe.hip", "w4_w8a8.hip"]
+           "w4_probe.hip", "w4_w8a8.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

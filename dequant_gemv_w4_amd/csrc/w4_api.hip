@@ -1,5 +1,6 @@
 // C-ABI entry points of libw4a16: argument validation, device check, launch.
-// The kernels live in w4_quantize.hip, w4_gemv.hip, w4_gemm.hip and w4_chain.hip.
+// The kernels live in w4_quantize.hip, w4_gemv.hip, w4_gemv_mfma.hip, w4_gemm.hip and
+// w4_w8a8.hip.
 #include <atomic>
 #include <cstring>
 #include <string>
@@ -279,107 +280,6 @@ w4_status w4_gemm(const void* prepared, int64_t N, int64_t K, const void* X, int
     if (st != W4_OK) return st;
     hipError_t e = w4::launch_gemm(static_cast<const uint8_t*>(prepared), N, K, X, M, Y,
                                    yt == W4_BF16, workspace, stream);
-    return e == hipSuccess ? W4_OK : hip_fail(e);
-}
-
-size_t w4_chain_plan_bytes(int64_t count) {
-    if (count < 1) return 0;
-    return sizeof(w4::ChainHeader) + (size_t)count * sizeof(w4::ChainDesc) + (size_t)count * 4;
-}
-
-size_t w4_chain_workspace_bytes(int64_t count) {
-    if (count < 1) return 0;
-    return ((size_t)count + 2) * 4;
-}
-
-w4_status w4_chain_plan(const w4_chain_gemv* g, int64_t count, void* plan_host,
-                        size_t plan_bytes) {
-    if (!g || !plan_host) return W4_ERR_NULL;
-    if (count < 1 || count > (1 << 20)) return W4_ERR_SHAPE;
-    if (plan_bytes < w4_chain_plan_bytes(count)) return W4_ERR_BUFFER;
-    int max_k = 0;
-    for (int64_t i = 0; i < count; ++i) {
-        if (!g[i].prepared || !g[i].x || !g[i].y) return W4_ERR_NULL;
-        if (g[i].y_dtype != W4_F32 && g[i].y_dtype != W4_BF16) return W4_ERR_DTYPE;
-        w4_status st = check_nk(g[i].n, g[i].k);
-        if (st != W4_OK) return st;
-        if (g[i].k > W4_GEMV_MAX_K || g[i].stage < 0) return W4_ERR_SHAPE;
-        if (i > 0 && g[i].stage < g[i - 1].stage) return W4_ERR_SHAPE;
-        if (!aligned(g[i].prepared, 256) || !aligned(g[i].x, 16) ||
-            !aligned(g[i].y, g[i].y_dtype == W4_F32 ? 4 : 2))
-            return W4_ERR_ALIGN;
-        if (g[i].k > max_k) max_k = (int)g[i].k;
-    }
-    w4_status st = check_arch();
-    if (st != W4_OK) return st;
-    const int grid = w4::chain_grid(max_k);
-    if (grid < 1) return W4_ERR_HIP;
-
-    auto* h = static_cast<w4::ChainHeader*>(plan_host);
-    auto* d = reinterpret_cast<w4::ChainDesc*>(static_cast<uint8_t*>(plan_host) + sizeof(w4::ChainHeader));
-    // stages renumbered 0..n_stages-1 in order of appearance
-    int n_stages = 0;
-    int64_t items = 0;
-    std::vector<int32_t> stage_items;
-    for (int64_t i = 0; i < count;) {
-        int64_t j = i;
-        int64_t rows_total = 0;
-        while (j < count && g[j].stage == g[i].stage) rows_total += g[j++].n;
-        // rows per item: items of a stage spread evenly over the grid, at most 64 rows
-        const int64_t per_round = (int64_t)grid * 64;
-        const int64_t rounds = (rows_total + per_round - 1) / per_round;
-        int64_t rows = (rows_total + rounds * grid - 1) / (rounds * grid);
-        rows = (rows + 3) / 4 * 4;
-        if (rows > 64) rows = 64;
-        if (rows < 4) rows = 4;
-        int64_t stage_count = 0;
-        for (int64_t e = i; e < j; ++e) {
-            const int64_t n_items = (g[e].n + rows - 1) / rows;
-            d[e].w = static_cast<const uint8_t*>(g[e].prepared);
-            d[e].sz = static_cast<const uint8_t*>(g[e].prepared) + w4::sz_offset(g[e].n, g[e].k);
-            d[e].x = static_cast<const uint16_t*>(g[e].x);
-            d[e].y = g[e].y;
-            d[e].n = (int32_t)g[e].n;
-            d[e].k = (int32_t)g[e].k;
-            d[e].rows = (int32_t)rows;
-            d[e].first_item = (int32_t)items;
-            d[e].n_items = (int32_t)n_items;
-            d[e].stage = n_stages;
-            d[e].y_bf16 = g[e].y_dtype == W4_BF16 ? 1 : 0;
-            d[e].reserved = 0;
-            items += n_items;
-            stage_count += n_items;
-        }
-        if (items > 0x7FFFFFFF) return W4_ERR_SHAPE;
-        stage_items.push_back((int32_t)stage_count);
-        ++n_stages;
-        i = j;
-    }
-    int32_t* si = reinterpret_cast<int32_t*>(reinterpret_cast<uint8_t*>(d) + sizeof(w4::ChainDesc) * (size_t)count);
-    for (int s = 0; s < n_stages; ++s) si[s] = stage_items[s];
-    h->magic = w4::kChainMagic;
-    h->n_desc = (int32_t)count;
-    h->n_stages = n_stages;
-    h->total_items = (int32_t)items;
-    h->grid = grid;
-    h->max_k = max_k;
-    h->spin_limit = 1 << 21;  // about two seconds of polling
-    h->reserved = 0;
-    return W4_OK;
-}
-
-w4_status w4_chain_run(const void* plan_dev, const void* plan_host, void* workspace,
-                       size_t workspace_bytes, hipStream_t stream) {
-    if (!plan_dev || !plan_host || !workspace) return W4_ERR_NULL;
-    const auto* h = static_cast<const w4::ChainHeader*>(plan_host);
-    if (h->magic != w4::kChainMagic || h->n_desc < 1 || h->n_stages < 1 || h->grid < 1)
-        return W4_ERR_UNSUPPORTED;
-    if (workspace_bytes < w4_chain_workspace_bytes(h->n_desc)) return W4_ERR_WORKSPACE;
-    if (!aligned(plan_dev, 16) || !aligned(workspace, 4)) return W4_ERR_ALIGN;
-    w4_status st = check_arch();
-    if (st != W4_OK) return st;
-    hipError_t e = w4::launch_chain(*h, static_cast<const uint8_t*>(plan_dev),
-                                    static_cast<uint32_t*>(workspace), stream);
     return e == hipSuccess ? W4_OK : hip_fail(e);
 }
 

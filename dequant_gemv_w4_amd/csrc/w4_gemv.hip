@@ -1,61 +1,78 @@
 // Fused dequantizing matrix-vector product for decode (1 <= M <= 16).
 //
-// Computes y[m, n] = sum_g scale16[n, g] * (sum_{k in g} q[n, k] x[m, k]
-//                                          - zero[n, g] * sum_{k in g} x[m, k])
-// (page "Weight quantization", section "How it works": one multiply per group;
-// section "Code": the group loop of the dot routine) without writing any
-// dequantized weight to memory.  Decode reads every weight once, so the kernel
-// is a stream over HBM (page "LLM Quantization Architecture in Depth" › "Why
-// fewer bits make decoding faster").
+// Computes y[m, n] = sum_g scale16[n, g] * sum_{k in g} (q[n, k] - zero[n, g]) x[m, k]
+// (page "Weight quantization", section "How it works": the dequantized weight is
+// (code - zero) * scale, and the group's scale multiplies once per group; section "Code":
+// the group loop of the dot routine) without writing any dequantized weight to memory.
+// Decode reads every weight once, so the kernel is a stream over HBM (page "LLM
+// Quantization Architecture in Depth" › "Why fewer bits make decoding faster").
+//
+// Exact operands.  The matrix instructions and the dot2 instructions of gfx950 align all
+// addends of one instruction to the largest before rounding, so an operand carrying a
+// bias (for example 128 + q, with the bias removed later through sum x) loses bits in
+// proportion to the bias times |x|, not to the size of the result: a group whose codes
+// mostly equal its zero, with large x there, would come out far outside the tolerance.
+// Every product here multiplies the exact difference q - zero:
+//   * v_and_or_b32((word >> s), 0x000F000F, 0x64006400) gives the binary16 pair
+//     (1024 + q_a, 1024 + q_b) and one v_pk_add_f16 with (-(1024 + zero)) x 2 gives the
+//     exact pair (q_a - zero, q_b - zero).  The codes at bits 4..7 / 20..23 of a word are
+//     taken where they are, as (1024 + 16 q) - (1024 + 16 zero) = 16 (q - zero), and
+//     their activations carry a factor 2^-4 instead, so a word of eight codes needs one
+//     shift;
+//   * x (bf16) enters as binary16 x * 2^-E, with E chosen per lane slice (32 inputs) so
+//     that the largest value lands just under 2^16.  bf16 has 8 significant bits and
+//     binary16 11, so the conversion (integer steps on the bits) is exact for every value
+//     that lands on a normal binary16, i.e. within 2^25 of the slice's largest;
+//     v_dot2_f32_f16 then multiplies exactly and accumulates in f32, and the slice's share
+//     of the group term is ldexp(scale16, E) * D;
+//   * binary32 x, and a wave in which some slice has a bf16 value outside that window,
+//     take the exact path instead: the same exact codes, converted to binary32, times x
+//     in binary32 with one FMA per input (for bf16 x, one row at a time in a loop of its
+//     own that reads x again, so that the rare path adds no registers to the fast one).
+// Either way a code equal to its zero contributes exactly 0, and the rounding error is
+// a few binary32 ulps of the sums of |(q - zero) x|, far inside 1e-3 * sum |w_hat x|.
 //
 // Mapping (gfx950, wave64):
-//   * lane u of the workgroup owns the 16-byte slice u of every row (32
-//     inputs, a quarter of a group); its x values stay in registers as bf16
-//     pairs for the whole workgroup, so each row costs one 16-byte load per
-//     lane and a wave load covers 1 KiB of contiguous weights;
-//   * a workgroup holds ceil(K/2048) waves and walks rows_per_wg rows in
-//     chunks of CH steps of four rows; x is loaded first, then all loads of a
-//     chunk are issued before any is used (a scheduling barrier keeps them
-//     there), so step c computes while the later steps are still arriving and
-//     the compiler's in-order wait counts stay exact (no load crosses a loop
-//     iteration);
+//   * lane u of the workgroup owns the 16-byte slice u of every row (32 inputs, a
+//     quarter of a group); its x values stay in registers for the whole workgroup, so
+//     each row costs one 16-byte load per lane and a wave load covers 1 KiB of
+//     contiguous weights;
+//   * a workgroup holds ceil(K/2048) waves and walks rows_per_wg rows in chunks of two
+//     steps of four rows; x is loaded first, then all loads of a chunk are issued before
+//     any is used (a scheduling barrier keeps them there), so step c computes while the
+//     later steps are still arriving and the compiler's in-order wait counts stay exact;
 //   * groups of up to eight waves end the launch with a round of workgroups that take
 //     half the rows of the others, which shortens the tail of the weight stream;
-//   * the scale/zero words of the four rows of a step are one 16-byte load;
-//   * unpack: v_and_or_b32((word >> 4j), 0x000F000F, 0x43004300) turns the two
-//     codes of an input pair into the bf16 values 128+q, and v_dot2_f32_bf16
-//     multiplies the pair by the matching x pair and accumulates in f32:
-//     D = sum (128+q)*x.  The slice sum S = sum x is computed once per
-//     workgroup by the same instruction sequence with the pair (1, 1), so the
-//     slice's share of the group term is scale16 * (D - (128 + zero) * S) =
-//     scale16 * (sum q*x - zero * sum x).  Because scaling by 128 commutes
-//     with rounding, a slice whose codes are all 0 gives D = 128*S exactly and
-//     contributes exactly 0, and a one-hot x gives exactly (q - zero)*scale16;
+//   * the scale/zero words of the four rows of a step are one 16-byte load; two
+//     v_perm_b32 build the binary16 pairs -(1024 + zero) and -(1024 + 16 zero) from the
+//     zero bytes of the word;
 //   * reduction of the four rows across the wave: v_permlane32_swap and
-//     v_permlane16_swap transpose-and-add (each lane ends with one row), DPP
-//     row rotations finish the 16-lane sums; waves are combined through LDS.
-//     No atomics, so results are deterministic.
-// Binary32 activations are split into two bf16 parts (hi = bf16(x),
-// lo = bf16(x - hi)) that are accumulated separately and added at the end.
+//     v_permlane16_swap transpose-and-add (each lane ends with one row), DPP row
+//     rotations finish the 16-lane sums; waves are combined through LDS.  No atomics, so
+//     results are deterministic.
 #include <atomic>
-#include <cstdlib>
 
 #include "w4_internal.h"
 
 namespace w4 {
 namespace {
 
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kRowsPerStep = 4;
+constexpr int kChunk = 2;  // steps of four rows whose loads are issued together
 
 // one 16-byte weight slice, marked non-temporal: every byte is read exactly once
 __device__ __forceinline__ u32x4_t load_stream(const u32x4_t* p) { return __builtin_nontemporal_load(p); }
 
-__device__ __forceinline__ float dot2(uint32_t w, uint32_t x, float acc) {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w),
-                                           __builtin_bit_cast(bf16x2_t, x), acc, false);
+__device__ __forceinline__ float dot2h(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), acc,
+                                  false);
+}
+
+__device__ __forceinline__ uint32_t add2h(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, a) + __builtin_bit_cast(f16x2_t, b));
 }
 
 __device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
@@ -63,13 +80,20 @@ __device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// sum of the 32 bf16 values held as 16 pairs, accumulated by the same dot2
-// chain (same order, same instruction) that the weights use, with the pair (1, 1)
-__device__ __forceinline__ float pair_sum(const uint32_t (&p)[16]) {
-    float d = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) d = dot2(0x3F803F80u, p[i], d);
-    return d;
+typedef __attribute__((ext_vector_type(2))) unsigned short u16x2_t;
+
+__device__ __forceinline__ u16x2_t as_u16x2(uint32_t v) { return __builtin_bit_cast(u16x2_t, v); }
+__device__ __forceinline__ uint32_t as_u32(u16x2_t v) { return __builtin_bit_cast(uint32_t, v); }
+
+// bf16 pair -> binary16 pair of x * 2^-E by integer steps: with c = (F_max - 30) << 7 (or
+// (F_max - 26) << 7 for a further 2^-4), ((|bits| - c) << 3) re-biases the exponent field
+// from bf16 to binary16 and widens the 7 mantissa bits to 10; the sign is put back.  The
+// subtraction saturates at 0, so a zero stays zero.  Exact whenever the result is a normal
+// binary16 value, which the slice's range check guarantees.
+__device__ __forceinline__ uint32_t to_f16_pair(uint32_t xb, uint32_t c2) {
+    const u16x2_t mag = as_u16x2(xb & 0x7FFF7FFFu);
+    const u16x2_t r = __builtin_elementwise_sub_sat(mag, as_u16x2(c2)) << (unsigned short)3;
+    return as_u32(r) | (xb & 0x80008000u);
 }
 
 template <int CTRL>
@@ -109,18 +133,24 @@ __device__ __forceinline__ float reduce4(float a0, float a1, float a2, float a3)
     return k;
 }
 
+// scale bits of a scale/zero word (binary16, or bfloat16 for SBF16) as binary32
+template <bool SBF16>
+__device__ __forceinline__ float word_scale(uint32_t szw) {
+    return SBF16 ? __uint_as_float(szw << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)(szw & 0xFFFFu));
+}
+
 // SBF16: the scale bits are bfloat16 (else binary16); gshift: log2(group / 32), the slices
 // of one group (a group of 32, 64 or 128 inputs has its own scale/zero word)
-template <int MT, bool XF32, int SPT, int MAXT, int CH, bool RAGGED, bool SBF16>
+template <int MT, bool XF32, int SPT, int MAXT, bool RAGGED, bool SBF16>
 __global__ __launch_bounds__(MAXT) void gemv_kernel(const u32x4_t* __restrict__ wq,
                                                     const u32x4_t* __restrict__ sz4,
                                                     const void* __restrict__ xv,
                                                     void* __restrict__ yv, int y_bf16, int N,
                                                     int K, int M, int rows_per_wg, int gshift,
                                                     int tail_first, int tail_rows) {
-    constexpr int XE = XF32 ? 2 * MT : MT;  // bf16 operand rows
     constexpr int R = kRowsPerStep;
-    extern __shared__ float red[];          // [waves][rows_per_wg][XE]
+    constexpr int CH = kChunk;
+    extern __shared__ float red[];          // [waves][rows_per_wg][MT]
 
     const int S = K >> 5;
     const int Kg = K >> (5 + gshift);
@@ -151,56 +181,31 @@ __global__ __launch_bounds__(MAXT) void gemv_kernel(const u32x4_t* __restrict__ 
         soff[j] = (uint32_t)(slc >> gshift) * 16u;
     }
 
+    const char* wbase = reinterpret_cast<const char*>(wq);
+    const char* sbase = reinterpret_cast<const char*>(sz4);
+    const int64_t row_bytes = (int64_t)S * 16;
+
     // ---- x slices first: their loads complete before the weight stream that follows
-    uint32_t xr[SPT][XE][16];
-    float sx[SPT][XE];
+    uint32_t xb[SPT][MT][16];   // bf16 pairs (binary32 x is read by the exact path itself)
+    if constexpr (!XF32) {
 #pragma unroll
-    for (int j = 0; j < SPT; ++j) {
+        for (int j = 0; j < SPT; ++j)
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            const bool ok = act[j] && (MT == 1 || m < M);  // zero x for idle lanes and absent rows
-            if constexpr (XF32) {
-                const float4* px = reinterpret_cast<const float4*>(
-                    static_cast<const float*>(xv) + (int64_t)m * K + (int64_t)sl[j] * 32);
-#pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    const float4 f = ok ? px[q] : make_float4(0.f, 0.f, 0.f, 0.f);
-                    const float v[4] = {f.x, f.y, f.z, f.w};
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const uint32_t h0 = bf16_bits_rne(v[2 * h]);
-                        const uint32_t h1 = bf16_bits_rne(v[2 * h + 1]);
-                        const uint32_t l0 = bf16_bits_rne(v[2 * h] - __uint_as_float(h0 << 16));
-                        const uint32_t l1 = bf16_bits_rne(v[2 * h + 1] - __uint_as_float(h1 << 16));
-                        xr[j][2 * m][2 * q + h] = h0 | (h1 << 16);
-                        xr[j][2 * m + 1][2 * q + h] = l0 | (l1 << 16);
-                    }
-                }
-            } else {
+            for (int m = 0; m < MT; ++m) {
+                const bool ok = act[j] && (MT == 1 || m < M);  // zero x for idle lanes and absent rows
                 const uint4* px = reinterpret_cast<const uint4*>(
                     static_cast<const uint16_t*>(xv) + (int64_t)m * K + (int64_t)sl[j] * 32);
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const uint4 v = ok ? px[q] : make_uint4(0, 0, 0, 0);
-                    xr[j][m][4 * q + 0] = v.x;
-                    xr[j][m][4 * q + 1] = v.y;
-                    xr[j][m][4 * q + 2] = v.z;
-                    xr[j][m][4 * q + 3] = v.w;
+                    xb[j][m][4 * q + 0] = v.x;
+                    xb[j][m][4 * q + 1] = v.y;
+                    xb[j][m][4 * q + 2] = v.z;
+                    xb[j][m][4 * q + 3] = v.w;
                 }
             }
-        }
     }
-
     __builtin_amdgcn_sched_barrier(0);  // keep the x loads ahead of the weight stream
-
-    // constants of the unpack kept in registers so v_and_or_b32 is selected
-    uint32_t nib_mask, bias_bits;
-    asm volatile("s_mov_b32 %0, 0x000F000F" : "=s"(nib_mask));
-    asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(bias_bits));
-
-    const char* wbase = reinterpret_cast<const char*>(wq);
-    const char* sbase = reinterpret_cast<const char*>(sz4);
-    const int64_t row_bytes = (int64_t)S * 16;
 
     // rows_per_wg is a multiple of CH*4: every chunk is whole; rows past N repeat row N-1
     // (their sums are never stored)
@@ -226,66 +231,226 @@ __global__ __launch_bounds__(MAXT) void gemv_kernel(const u32x4_t* __restrict__ 
         // every load of the chunk is issued before any of it is used: step c computes while
         // the loads of the later steps are still in flight
     };
-    auto compute_chunk = [&](int c0) {
+
+    // binary32 x for the exact path, resident
+    uint32_t xs[XF32 ? SPT : 1][XF32 ? MT : 1][32];
+    if constexpr (XF32) {
 #pragma unroll
-        for (int c = 0; c < CH; ++c) {
-            float acc[R][XE];
+        for (int j = 0; j < SPT; ++j)
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                const bool ok = act[j] && (MT == 1 || m < M);
+                const uint4* px = reinterpret_cast<const uint4*>(
+                    static_cast<const float*>(xv) + (int64_t)m * K + (int64_t)sl[j] * 32);
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const uint4 v = ok ? px[q] : make_uint4(0, 0, 0, 0);
+                    xs[j][m][4 * q + 0] = v.x;
+                    xs[j][m][4 * q + 1] = v.y;
+                    xs[j][m][4 * q + 2] = v.z;
+                    xs[j][m][4 * q + 3] = v.w;
+                }
+            }
+    }
+
+    // ---- binary16 activations and the per-slice exponents (fast path)
+    uint32_t xp[SPT][MT][16];
+    int xe[SPT][MT];
+    bool exact = XF32;
+    if constexpr (!XF32) {
+        bool bad = false;
+#pragma unroll
+        for (int j = 0; j < SPT; ++j)
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                // largest magnitude and smallest non-zero magnitude of the slice (bf16 bits)
+                u16x2_t vmax = {0, 0}, vmin = {0xFFFF, 0xFFFF};
+#pragma unroll
+                for (int p = 0; p < 16; ++p) {
+                    const u16x2_t mag = as_u16x2(xb[j][m][p] & 0x7FFF7FFFu);
+                    vmax = __builtin_elementwise_max(vmax, mag);
+                    vmin = __builtin_elementwise_min(vmin, mag - (unsigned short)1);  // 0 -> 0xFFFF
+                }
+                const int fmax = (int)(max(vmax.x, vmax.y) >> 7);               // bf16 exponent field
+                const int mnz = (int)min(vmin.x, vmin.y) + 1;                   // 0x10000: all zero
+                // x * 2^-E puts the largest value in [2^15, 2^16); every non-zero value of the
+                // slice must land on a normal binary16 (also after the further 2^-4): within
+                // 2^25 of the largest.  Slices of tiny (below 2^-97) or non-finite values take
+                // the exact path; an all-zero slice converts to zeros whatever E is.
+                const int e = fmax - 127 - 15;
+                bad |= mnz != 0x10000 && (fmax < 30 || fmax == 255 || mnz < ((fmax - 25) << 7));
+                xe[j][m] = e;
+                const uint32_t ce = (uint32_t)((fmax - 30) << 7) * 0x00010001u;
+                const uint32_t co = (uint32_t)((fmax - 26) << 7) * 0x00010001u;
+#pragma unroll
+                for (int p = 0; p < 16; ++p)
+                    // pairs 1 and 3 of every word meet codes scaled by 16 (see the header)
+                    xp[j][m][p] = to_f16_pair(xb[j][m][p], (p & 1) ? co : ce);
+            }
+        exact = __builtin_amdgcn_ballot_w64(bad) != 0;
+    }
+
+    uint32_t m_lo, m_hi, magic, e4;
+    asm volatile("s_mov_b32 %0, 0x000F000F" : "=s"(m_lo));
+    asm volatile("s_mov_b32 %0, 0x00F000F0" : "=s"(m_hi));
+    asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
+    asm volatile("s_mov_b32 %0, 0xE4E4E4E4" : "=s"(e4));
+
+    // the codes of one row slice as exact binary16 pairs (q - zero, or 16 (q - zero) for the
+    // pairs that meet x * 2^-4)
+    auto unpack_codes = [&](const u32x4_t& wv, uint32_t szw, uint32_t (&pr)[16]) {
+        // -(1024 + zero) and -(1024 + 16 zero) as binary16 pairs (word bytes 2, 3)
+        const uint32_t z1 = __builtin_amdgcn_perm(e4, szw, 0x04020402u);
+        const uint32_t z16 = __builtin_amdgcn_perm(e4, szw, 0x04030403u);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const uint32_t w = wv[t];
+            const uint32_t u = w >> 8;
+            pr[4 * t + 0] = add2h((w & m_lo) | magic, z1);
+            pr[4 * t + 1] = add2h((w & m_hi) | magic, z16);
+            pr[4 * t + 2] = add2h((u & m_lo) | magic, z1);
+            pr[4 * t + 3] = add2h((u & m_hi) | magic, z16);
+        }
+    };
+
+    // one chunk (CH steps of four rows)
+    auto compute_chunk = [&](int c0) {
+        float acc[CH][R][MT];
+#pragma unroll
+        for (int c = 0; c < CH; ++c)
 #pragma unroll
             for (int rr = 0; rr < R; ++rr)
 #pragma unroll
-                for (int e = 0; e < XE; ++e) acc[rr][e] = 0.0f;
+                for (int m = 0; m < MT; ++m) acc[c][rr][m] = 0.0f;
+        if constexpr (!XF32) {
+            // v_dot2_f32_f16: binary16 exact codes times binary16 activations
 #pragma unroll
-            for (int j = 0; j < SPT; ++j) {
+            for (int c = 0; c < CH; ++c)
 #pragma unroll
-                for (int rr = 0; rr < R; ++rr) {
-                    const uint32_t szw = sb[c][j][rr];
-                    const float s = SBF16 ? __uint_as_float(szw << 16)
-                                          : (float)__builtin_bit_cast(_Float16, (uint16_t)(szw & 0xFFFFu));
-                    const float zb = (float)((szw >> 16) & 0xFFu);  // zero + 128
-                    uint32_t pr[16];
+                for (int j = 0; j < SPT; ++j)
 #pragma unroll
-                    for (int t = 0; t < 4; ++t)
+                    for (int rr = 0; rr < R; ++rr) {
+                        const uint32_t szw = sb[c][j][rr];
+                        // lanes past the last slice read real (unrelated) scales: weight 0
+                        const float s = act[j] ? word_scale<SBF16>(szw) : 0.0f;
+                        uint32_t pr[16];
+                        unpack_codes(wb[c][rr][j], szw, pr);
 #pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            pr[4 * t + q] = ((wb[c][rr][j][t] >> (4 * q)) & nib_mask) | bias_bits;
+                        for (int m = 0; m < MT; ++m) {
+                            float d = 0.0f;
 #pragma unroll
-                    for (int e = 0; e < XE; ++e) {
-                        float d = 0.0f;
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) d = dot2(pr[i], xr[j][e][i], d);
-                        acc[rr][e] = fmaf(s, fmaf(-zb, sx[j][e], d), acc[rr][e]);
+                            for (int i = 0; i < 16; ++i) d = dot2h(pr[i], xp[j][m][i], d);
+                            acc[c][rr][m] = fmaf(ldexpf(s, xe[j][m]), d, acc[c][rr][m]);
+                        }
                     }
-                }
-            }
-            if constexpr (RAGGED) {
-                // lanes past the last slice read real (unrelated) scales; drop their terms
-                bool any_off = false;
+        } else {
+            // binary32 x: exact codes times resident binary32 x, one FMA per input
 #pragma unroll
-                for (int j = 0; j < SPT; ++j) any_off |= !act[j];
-                if (any_off)
+            for (int c = 0; c < CH; ++c)
 #pragma unroll
-                    for (int rr = 0; rr < R; ++rr)
+                for (int j = 0; j < SPT; ++j)
 #pragma unroll
-                        for (int e = 0; e < XE; ++e) acc[rr][e] = 0.0f;
-            }
+                    for (int rr = 0; rr < R; ++rr) {
+                        const uint32_t szw = sb[c][j][rr];
+                        const float s = act[j] ? word_scale<SBF16>(szw) : 0.0f;
+                        uint32_t pr[16];
+                        unpack_codes(wb[c][rr][j], szw, pr);
+#pragma unroll
+                        for (int m = 0; m < MT; ++m) {
+                            float d = 0.0f;
+#pragma unroll
+                            for (int p = 0; p < 16; ++p) {
+                                const f16x2_t h = __builtin_bit_cast(f16x2_t, pr[p]);
+                                const float sc = (p & 1) ? 0.0625f : 1.0f;
+                                d = fmaf((float)h[0] * sc, __uint_as_float(xs[j][m][2 * p]), d);
+                                d = fmaf((float)h[1] * sc, __uint_as_float(xs[j][m][2 * p + 1]), d);
+                            }
+                            acc[c][rr][m] = fmaf(s, d, acc[c][rr][m]);
+                        }
+                    }
+        }
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
             const int rbase = c0 + c * R;
 #pragma unroll
-            for (int e = 0; e < XE; ++e) {
-                const float k = reduce4(acc[0][e], acc[1][e], acc[2][e], acc[3][e]);
-                if ((lane & 15) == 0) red[(wave * row_stride + rbase + (lane >> 4)) * XE + e] = k;
+            for (int m = 0; m < MT; ++m) {
+                const float k = reduce4(acc[c][0][m], acc[c][1][m], acc[c][2][m], acc[c][3][m]);
+                if ((lane & 15) == 0) red[(wave * row_stride + rbase + (lane >> 4)) * MT + m] = k;
             }
         }
     };
 
-    issue_chunk(0);
+    // bf16 x outside the binary16 window (rare): the wave runs the exact path, one row at a
+    // time with loads of its own -- a separate loop, so that it adds nothing to the
+    // registers of the pipelined fast path
+    auto run_exact_bf16 = [&]() {
+        float a0[MT], a1[MT], a2[MT], a3[MT];
+#pragma unroll 1
+        for (int i = 0; i < rows_per_wg; ++i) {
+            const int row = min(r0 + i, N - 1);
+            const char* srow = sbase + (int64_t)(row >> 2) * Kg * 16;
+            float v[MT];
 #pragma unroll
-    for (int j = 0; j < SPT; ++j)
+            for (int m = 0; m < MT; ++m) v[m] = 0.0f;
 #pragma unroll
-        for (int e = 0; e < XE; ++e) sx[j][e] = pair_sum(xr[j][e]);
-    compute_chunk(0);
-    for (int c0 = CH * R; c0 < rows_per_wg; c0 += CH * R) {
-        issue_chunk(c0);
-        compute_chunk(c0);
+            for (int j = 0; j < SPT; ++j) {
+                const u32x4_t wv = *reinterpret_cast<const u32x4_t*>(wbase + (int64_t)row * row_bytes + woff[j]);
+                const uint32_t szw = *reinterpret_cast<const uint32_t*>(srow + soff[j] + 4 * (row & 3));
+                const float s = act[j] ? word_scale<SBF16>(szw) : 0.0f;
+                uint32_t pr[16];
+                unpack_codes(wv, szw, pr);
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    const bool ok = act[j] && (MT == 1 || m < M);
+                    const uint4* px = reinterpret_cast<const uint4*>(
+                        static_cast<const uint16_t*>(xv) + (int64_t)m * K + (int64_t)sl[j] * 32);
+                    // read x again for every row (an opaque pointer keeps the loads, and the 32
+                    // binary32 values made from them, from being hoisted out of the row loop)
+                    asm volatile("" : "+v"(px));
+                    float d = 0.0f;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const uint4 xv4 = ok ? px[q] : make_uint4(0, 0, 0, 0);
+                        const uint32_t xq[4] = {xv4.x, xv4.y, xv4.z, xv4.w};
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) {
+                            // pair 4q + t of the slice; odd pairs carry codes x 16
+                            const f16x2_t h = __builtin_bit_cast(f16x2_t, pr[4 * q + t]);
+                            const float sc = (t & 1) ? 0.0625f : 1.0f;
+                            d = fmaf((float)h[0] * sc, __uint_as_float(xq[t] << 16), d);
+                            d = fmaf((float)h[1] * sc, __uint_as_float(xq[t] & 0xFFFF0000u), d);
+                        }
+                    }
+                    v[m] = fmaf(s, d, v[m]);
+                }
+            }
+            // four rows per reduction: rows i-3 .. i in a0 .. a3
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                a0[m] = a1[m];
+                a1[m] = a2[m];
+                a2[m] = a3[m];
+                a3[m] = v[m];
+            }
+            if ((i & 3) == 3) {
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    const float k = reduce4(a0[m], a1[m], a2[m], a3[m]);
+                    if ((lane & 15) == 0) red[(wave * row_stride + (i - 3) + (lane >> 4)) * MT + m] = k;
+                }
+            }
+        }
+    };
+
+    if (!XF32 && exact) {
+        run_exact_bf16();
+    } else {
+        issue_chunk(0);
+        compute_chunk(0);
+        for (int c0 = CH * R; c0 < rows_per_wg; c0 += CH * R) {
+            issue_chunk(c0);
+            compute_chunk(c0);
+        }
     }
     __syncthreads();
 
@@ -295,13 +460,7 @@ __global__ __launch_bounds__(MAXT) void gemv_kernel(const u32x4_t* __restrict__ 
         const int m = t - rloc * MT;
         if (m >= M) continue;
         float v = 0.0f;
-        for (int w = 0; w < n_waves; ++w) {
-            const float* p = red + (w * row_stride + rloc) * XE;
-            if constexpr (XF32)
-                v += p[2 * m] + p[2 * m + 1];
-            else
-                v += p[m];
-        }
+        for (int w = 0; w < n_waves; ++w) v += red[(w * row_stride + rloc) * MT + m];
         const int64_t o = (int64_t)m * N + r0 + rloc;
         if (y_bf16)
             static_cast<uint16_t*>(yv)[o] = (uint16_t)bf16_bits_rne(v);
@@ -320,11 +479,6 @@ struct GemvArgs {
     bool scale_bf16;
 };
 
-int env_int(const char* name, int dflt) {
-    const char* e = getenv(name);
-    return e ? atoi(e) : dflt;
-}
-
 constexpr int kMaxRowsPerWg = 64;
 
 int compute_units() {
@@ -340,59 +494,47 @@ int compute_units() {
     return cus;
 }
 
-// Rows per workgroup chosen from the number of resident workgroups: a whole
-// number of rounds (see below), rows a multiple of the chunk.
+// Rows per workgroup chosen from the number of resident workgroups: measured on MI355X,
+// groups of up to 8 waves stream best with about three rounds of resident groups (finer
+// work, shorter tail), the 14-wave groups of K ~ 28K with one; rows a multiple of the chunk.
 template <typename Kern>
-int rows_for(Kern kernel, int block, int n, int xe, int chunk_rows, std::atomic<int>* cache) {
+int rows_for(Kern kernel, int block, int n, int mt, int chunk_rows, std::atomic<int>* cache) {
     const int waves = block / 64;
     int resident = cache[waves].load(std::memory_order_relaxed);
     if (resident == 0) {
-        const size_t smem = (size_t)waves * kMaxRowsPerWg * xe * sizeof(float);
+        const size_t smem = (size_t)waves * kMaxRowsPerWg * mt * sizeof(float);
         int r = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&r, kernel, block, smem) != hipSuccess || r < 1)
             r = 1;
         cache[waves].store(r, std::memory_order_relaxed);
         resident = r;
     }
-    static const int forced = env_int("W4A16_GEMV_ROWS", 0);
-    static const int forced_rounds = env_int("W4A16_GEMV_ROUNDS", 0);
-    // measured on MI355X: groups of up to 8 waves stream best with about three rounds of
-    // resident groups (finer work, shorter tail); the 14-wave groups of K ~ 28K with one
-    int rounds = forced_rounds > 0 ? forced_rounds : (waves <= 8 ? 3 : 1);
-    int rows;
-    if (forced > 0) {
-        rows = forced;
-    } else {
-        const long wgs = (long)resident * compute_units() * rounds;
-        rows = (int)((n + wgs - 1) / wgs);
-    }
+    const int rounds = waves <= 8 ? 3 : 1;
+    const long wgs = (long)resident * compute_units() * rounds;
+    int rows = (int)((n + wgs - 1) / wgs);
     rows = (rows + chunk_rows - 1) / chunk_rows * chunk_rows;
     if (rows < chunk_rows) rows = chunk_rows;
     if (rows > kMaxRowsPerWg) rows = kMaxRowsPerWg / chunk_rows * chunk_rows;
     return rows;
 }
 
-template <int MT, bool XF32, int SPT, int MAXT, int CH, bool RAGGED, bool SBF16>
+template <int MT, bool XF32, int SPT, int MAXT, bool RAGGED, bool SBF16>
 hipError_t launch_var(GemvArgs a, dim3 block, hipStream_t s) {
-    constexpr int XE = XF32 ? 2 * MT : MT;
+    constexpr int CR = kChunk * kRowsPerStep;
     static std::atomic<int> cache[17];
-    auto kern = gemv_kernel<MT, XF32, SPT, MAXT, CH, RAGGED, SBF16>;
-    a.rows = rows_for(kern, (int)block.x, a.n, XE, CH * kRowsPerStep, cache);
+    auto kern = gemv_kernel<MT, XF32, SPT, MAXT, RAGGED, SBF16>;
+    a.rows = rows_for(kern, (int)block.x, a.n, MT, CR, cache);
     unsigned wgs = (unsigned)((a.n + a.rows - 1) / a.rows);
-    // A short last round: the last round of resident workgroups takes 1/tail of the rows.
+    // A short last round: the last round of resident workgroups takes half the rows.
     // Workgroups start in index order as earlier ones finish, so the final ones otherwise
     // start late with a full share and stream alone at the end.  Measured on MI355X
     // (57344x8192 at M = 1): 38.3-38.4 us against 39.5-40.0 us; the one-round 14-wave
     // groups of K ~ 28K run slower with it, so they keep equal shares.
     int tail_first = (int)wgs, tail_rows = a.rows;
-    static const int tail_env = env_int("W4A16_GEMV_TAIL", -1);
-    const int tail = tail_env >= 0 ? tail_env : (block.x <= 512 ? 2 : 0);
-    static const int tail_rounds = env_int("W4A16_GEMV_TAILROUNDS", 1);
-    const int half = tail > 0 ? a.rows / tail : 0;
-    if (tail > 1 && half * tail == a.rows && half >= CH * kRowsPerStep && half % (CH * kRowsPerStep) == 0) {
+    const int half = block.x <= 512 ? a.rows / 2 : 0;
+    if (half >= CR && half % CR == 0) {
         const long round = (long)cache[block.x / 64].load(std::memory_order_relaxed) * compute_units();
-        const long tail_rows_total = round * tail_rounds * half;
-        const long main_wgs = ((long)a.n - tail_rows_total) / a.rows;
+        const long main_wgs = ((long)a.n - round * half) / a.rows;
         if (main_wgs > 0) {
             tail_first = (int)main_wgs;
             tail_rows = half;
@@ -401,54 +543,40 @@ hipError_t launch_var(GemvArgs a, dim3 block, hipStream_t s) {
         }
     }
     const dim3 grid(wgs);
-    const size_t shmem = (size_t)(block.x / 64) * a.rows * XE * sizeof(float);
+    const size_t shmem = (size_t)(block.x / 64) * a.rows * MT * sizeof(float);
     hipLaunchKernelGGL(kern, grid, block, shmem, s, a.wq, a.sz4, a.x, a.y, a.y_bf16, a.n, a.k, a.m,
                        a.rows, a.gshift, tail_first, tail_rows);
     return hipGetLastError();
 }
 
-template <int MT, bool XF32, int SPT, int MAXT, int CH, bool SBF16>
+template <int MT, bool XF32, int SPT, int MAXT, bool SBF16>
 hipError_t launch_one(const GemvArgs& a, dim3 block, hipStream_t s) {
     const bool ragged = (int)block.x * SPT * 32 != a.k;
-    return ragged ? launch_var<MT, XF32, SPT, MAXT, CH, true, SBF16>(a, block, s)
-                  : launch_var<MT, XF32, SPT, MAXT, CH, false, SBF16>(a, block, s);
+    return ragged ? launch_var<MT, XF32, SPT, MAXT, true, SBF16>(a, block, s)
+                  : launch_var<MT, XF32, SPT, MAXT, false, SBF16>(a, block, s);
 }
 
-// Instantiated variants (MT = rows of x per launch, SPT = 16-byte slices per lane,
-// CH = steps of four rows whose loads are issued together):
-//   M=1 bf16:   SPT 1, up to 1024 threads (K <= 32768), CH 2 or 4
-//   otherwise:  up to 512 threads; SPT 1 for K <= 16384, SPT 2 up to 32768; CH 2 (1 for
-//               the SPT 2 variants with two x rows); MT up to 4 (bf16, SPT 1), 2 (bf16,
-//               SPT 2 / f32, SPT 1), 1 (f32, SPT 2) so that the registers fit the
-//               256-VGPR budget of a 512-thread group
+// Instantiated variants (MT = rows of x per launch, SPT = 16-byte slices per lane):
+//   M=1 bf16:   SPT 1, up to 1024 threads (K <= 32768)
+//   otherwise:  up to 512 threads; SPT 1 for K <= 16384, SPT 2 up to 32768; MT up to 3
+//               (bf16, SPT 1), 2 (binary32, SPT 1), 1 (SPT 2) so that the registers fit
+//               the 256-VGPR budget of a 512-thread group without spilling
 int max_mt(bool x_f32, int spt) {
-    if (!x_f32) return spt == 1 ? 4 : 2;
-    return spt == 1 ? 2 : 1;
+    if (spt != 1) return 1;
+    return x_f32 ? 2 : 3;
 }
 
-// SB: bfloat16 scale bits (the format variants take the default load chunk only)
 template <bool SB>
 hipError_t dispatch_t(bool x_f32, int spt, int mt, const GemvArgs& a, dim3 block, hipStream_t s) {
-    static const int chunk = SB ? 2 : env_int("W4A16_GEMV_CHUNK", 2);
-    if (!x_f32 && mt == 1 && spt == 1) {
-        if constexpr (!SB) {
-            if (block.x > 512) {
-                if (chunk == 1) return launch_one<1, false, 1, 1024, 1, SB>(a, block, s);
-                if (chunk == 4) return launch_one<1, false, 1, 1024, 4, SB>(a, block, s);
-            } else {
-                if (chunk == 1) return launch_one<1, false, 1, 512, 1, SB>(a, block, s);
-                if (chunk == 4) return launch_one<1, false, 1, 512, 4, SB>(a, block, s);
-            }
-        }
-        return block.x > 512 ? launch_one<1, false, 1, 1024, 2, SB>(a, block, s)
-                             : launch_one<1, false, 1, 512, 2, SB>(a, block, s);
-    }
-#define W4_CASE(MTV, XF, SP, NB) \
-    if (mt == MTV && x_f32 == XF && spt == SP) return launch_one<MTV, XF, SP, 512, NB, SB>(a, block, s);
-    W4_CASE(2, false, 1, 2) W4_CASE(3, false, 1, 2) W4_CASE(4, false, 1, 2)
-    W4_CASE(1, false, 2, 2) W4_CASE(2, false, 2, 1)
-    W4_CASE(1, true, 1, 2) W4_CASE(2, true, 1, 2)
-    W4_CASE(1, true, 2, 1)
+    if (!x_f32 && mt == 1 && spt == 1)
+        return block.x > 512 ? launch_one<1, false, 1, 1024, SB>(a, block, s)
+                             : launch_one<1, false, 1, 512, SB>(a, block, s);
+#define W4_CASE(MTV, XF, SP) \
+    if (mt == MTV && x_f32 == XF && spt == SP) return launch_one<MTV, XF, SP, 512, SB>(a, block, s);
+    W4_CASE(2, false, 1) W4_CASE(3, false, 1)
+    W4_CASE(1, false, 2)
+    W4_CASE(1, true, 1) W4_CASE(2, true, 1)
+    W4_CASE(1, true, 2)
 #undef W4_CASE
     return hipErrorInvalidValue;
 }
@@ -465,15 +593,12 @@ hipError_t launch_gemv(const uint8_t* prepared, int64_t n, int64_t k, const void
     // bf16 rows: the matrix-core kernels read the weights once for all rows.  The dot2
     // kernel below does M times the vector work per weight; it stays faster (measured on
     // MI355X at the 70B shapes) at one row, at two rows while it needs a single pass over
-    // the weights (K <= 16384; down 8192x28672 at M = 2: 36.4 us here against 26.0 us on the
-    // matrix cores), and at three rows on shapes with K and N <= 16384 that the ring kernel
-    // takes (qkv 10240x8192: 14.4 against 15.3 us; o 8192x8192 streams faster, 11.2 against
-    // 12.2 us).
-    static const int use_mfma = env_int("W4A16_GEMV_MFMA", 1);
+    // the weights (K <= 16384), and at three rows on shapes with K and N <= 16384 that the
+    // ring kernel takes.
     const bool one_pass = k <= 16384;
     const bool dot2_wins = m == 1 || (m == 2 && one_pass) ||
                            (m == 3 && one_pass && n <= 16384 && gemv_ring_takes(n, k));
-    if (!x_f32 && !dot2_wins && use_mfma)
+    if (!x_f32 && !dot2_wins)
         return launch_gemv_mfma(prepared, n, k, static_cast<const uint16_t*>(x), m, y, y_bf16, s);
     return launch_gemv_dot2(prepared, n, k, kGroup, false, x, x_f32, m, y, y_bf16, s);
 }

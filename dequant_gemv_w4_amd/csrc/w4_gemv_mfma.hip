@@ -1,14 +1,24 @@
 // Fused dequantizing product for a few activation rows (bf16 x, up to 16 rows; w4_gemv
 // sends most shapes with 2 <= M <= 16 here) on the matrix cores.
 //
-// The same group term as the one-row kernel, y[m, n] = sum_g scale16[n, g] *
-// (sum_{k in g} q[n, k] x[m, k] - zero[n, g] * sum_{k in g} x[m, k]) (page
-// "Weight quantization", section "How it works"), but the M dot products per
-// weight are done by v_mfma_f32_16x16x32_bf16 instead of the vector ALU.  The
-// weight stream stays the bound for every M up to 16: with VALU dot products
-// the work per weight grows with M, and past a few rows the vector units, not
-// HBM, set the pace (page "LLM Quantization Architecture in Depth" › "When it
-// helps and when it does not": batched decode moves towards compute).
+// y[m, n] = sum_g scale16[n, g] * sum_{k in g} (q[n, k] - zero[n, g]) x[m, k] (page
+// "Weight quantization", section "How it works": the dequantized weight is
+// (code - zero) * scale and the scale multiplies once per group), with the M dot
+// products per weight done by v_mfma_f32_16x16x32_bf16 instead of the vector ALU.  The
+// weight stream stays the bound for every M up to 16: with VALU dot products the work
+// per weight grows with M, and the pages note that batched decode moves towards compute
+// (page "Weight quantization" › "Implementation notes": past a batch of about 16-32,
+// dequantization inside the product turns compute-heavy).
+//
+// Exact operands: the matrix instruction aligns the 32 products of a step and the
+// accumulator to the largest before it rounds, so an operand with a bias (128 + q, the
+// bias removed later through sum x) would lose bits in proportion to the bias, not to the
+// result.  The B operand is the exact bf16 value q - zero of every code: v_and_or_b32
+// builds binary16 1024 + q (or 1024 + 16 q for the codes at bits 4..7 of a half word),
+// v_pk_add_f16 subtracts 1024 + zero (1024 + 16 zero) exactly, and two scaled conversions
+// (binary16 -> E4M3 -> bf16, exact for these small integers; the second one scales the
+// 16 (q - zero) values back by 2^-4) give bf16.  x enters unchanged as bf16, every product
+// is exact, and a code equal to its zero contributes exactly 0.
 //
 // Mapping (gfx950, wave64):
 //   * the waves of a workgroup split K: wave w takes groups [w*gpw, (w+1)*gpw);
@@ -22,21 +32,15 @@
 //     to registers.  XOR swizzles of the 16-byte chunks let each lane read
 //     its MFMA operands back with no bank conflicts.  The loads of the next
 //     pair are issued as soon as the current pair is read out of LDS, so they
-//     are in flight while the current pair is computed.  With the codes
-//     loaded straight into the lane order and no overlap, the 70B down shape
-//     (8192 x 28672) took 40-45 us per call at M = 4..16, now 27-38 us;
+//     are in flight while the current pair is computed;
 //   * MFMA step s (s = 0..3) of a group: A = x rows (lane l supplies row l % 16,
-//     k = 32*(l/16) + 8s .. +7), B = codes of the tile's 16 rows, unpacked by
-//     v_and_or_b32 into the exact bf16 values 128+q (lane l supplies column
-//     l % 16, same k).  Four steps give P[m][n] = sum (128+q) x for the group;
-//   * the group sums S[m] come from the same four steps with B = ones, so a
-//     group whose codes are all 0 gives P = 128*S exactly; the group's term is
-//     scale16 * (P - (128 + zero) * S), two FMAs per output element;
+//     k = 32*(l/16) + 8s .. +7), B = the exact codes of the tile's 16 rows (lane l
+//     supplies column l % 16, same k).  Four steps give P[m][n] = sum (q - zero) x for
+//     the group in a fresh accumulator, and acc += scale16 * P (one FMA per output);
 //   * the 16x16 result sits in lane l as column n = l % 16, rows
 //     m = 4*(l/16) + v (v = 0..3): one scale/zero word per lane and tile.
 #include <atomic>
 #include <type_traits>
-#include <cstdlib>
 
 #include "w4_internal.h"
 
@@ -50,6 +54,54 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kRedStride = 17;  // floats per row of the LDS partial sums (16 + pad)
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
+typedef __attribute__((ext_vector_type(2))) short s16x2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+__device__ __forceinline__ uint32_t add2h(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, a) + __builtin_bit_cast(f16x2_t, b));
+}
+
+// Constants of the code unpack, kept in registers so that v_and_or_b32 is selected.
+struct CodeConsts {
+    uint32_t m_lo, m_hi, magic, e4;
+    __device__ __forceinline__ CodeConsts() {
+        asm volatile("s_mov_b32 %0, 0x000F000F" : "=s"(m_lo));
+        asm volatile("s_mov_b32 %0, 0x00F000F0" : "=s"(m_hi));
+        asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
+        asm volatile("s_mov_b32 %0, 0xE4E4E4E4" : "=s"(e4));
+    }
+    // binary16 pairs -(1024 + zero) and -(1024 + 16 zero) from bytes 2 and 3 of a
+    // scale/zero word
+    __device__ __forceinline__ uint32_t z1(uint32_t szw) const { return __builtin_amdgcn_perm(e4, szw, 0x04020402u); }
+    __device__ __forceinline__ uint32_t z16(uint32_t szw) const { return __builtin_amdgcn_perm(e4, szw, 0x04030403u); }
+};
+
+// Scale of the bf16 conversion of the values 16 (q - zero): back to q - zero.
+constexpr float kSixteenthBack = 0.0625f;
+
+// The eight codes of a prepared word (inputs 0..7: pairs at bits 4j / 16 + 4j) as the
+// exact bf16 values q - zero, in input order.
+__device__ __forceinline__ u32x4_t exact_codes(uint32_t w, uint32_t z1, uint32_t z16, const CodeConsts& c) {
+    const uint32_t u = w >> 8;
+    const f16x2_t h0 = __builtin_bit_cast(f16x2_t, add2h((w & c.m_lo) | c.magic, z1));   // inputs 0, 1
+    const f16x2_t h1 = __builtin_bit_cast(f16x2_t, add2h((w & c.m_hi) | c.magic, z16));  // 2, 3 (x16)
+    const f16x2_t h2 = __builtin_bit_cast(f16x2_t, add2h((u & c.m_lo) | c.magic, z1));   // 4, 5
+    const f16x2_t h3 = __builtin_bit_cast(f16x2_t, add2h((u & c.m_hi) | c.magic, z16));  // 6, 7 (x16)
+    s16x2_t e01 = {0, 0}, e23 = {0, 0};
+    e01 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(e01, h0, 1.0f, false);
+    e01 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(e01, h1, 1.0f, true);
+    e23 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(e23, h2, 1.0f, false);
+    e23 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(e23, h3, 1.0f, true);
+    const uint32_t f01 = __builtin_bit_cast(uint32_t, e01), f23 = __builtin_bit_cast(uint32_t, e23);
+    const u32x4_t r = {
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f01, 1.0f, false)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f01, kSixteenthBack, true)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f23, 1.0f, false)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(f23, kSixteenthBack, true))};
+    return r;
+}
 
 __device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
     const uint32_t u = __float_as_uint(f);
@@ -126,10 +178,7 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(const uint8_t* __restric
         xsrc[i] = x + (int64_t)min(r, M - 1) * K + 8 * ((lane & 15) ^ (r & 15));
     }
 
-    uint32_t nib_mask, bias_bits;
-    asm volatile("s_mov_b32 %0, 0x000F000F" : "=s"(nib_mask));
-    asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(bias_bits));
-    const u32x4_t ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+    const CodeConsts cc;
     const f32x4_t zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
 
     f32x4_t acc[T];
@@ -186,31 +235,19 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(const uint8_t* __restric
         for (int c = 0; c < CH; ++c) {
             // a group past the wave's range is computed with scale 0 (no branch)
             const float keep = g + c < g1 ? 1.0f : 0.0f;
-            f32x4_t sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                as_bf16x8(xb[c][0]), as_bf16x8(ones), zero4, 0, 0, 0);
-#pragma unroll
-            for (int s = 1; s < 4; ++s)
-                sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xb[c][s]),
-                                                               as_bf16x8(ones), sacc, 0, 0, 0);
 #pragma unroll
             for (int t = 0; t < T; ++t) {
+                const uint32_t szw = sb[b][c][t];
+                const uint32_t z1 = cc.z1(szw), z16 = cc.z16(szw);
                 f32x4_t p = zero4;
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const uint32_t w = wb[c][t][s];
-                    const u32x4_t bw = {(w & nib_mask) | bias_bits,
-                                        ((w >> 4) & nib_mask) | bias_bits,
-                                        ((w >> 8) & nib_mask) | bias_bits,
-                                        ((w >> 12) & nib_mask) | bias_bits};
-                    p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xb[c][s]),
-                                                                as_bf16x8(bw), p, 0, 0, 0);
-                }
-                const uint32_t szw = sb[b][c][t];
+                for (int s = 0; s < 4; ++s)
+                    p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        as_bf16x8(xb[c][s]), as_bf16x8(exact_codes(wb[c][t][s], z1, z16, cc)), p, 0, 0, 0);
                 const float sc =
                     keep * (float)__builtin_bit_cast(_Float16, (uint16_t)(szw & 0xFFFFu));
-                const float zb = (float)((szw >> 16) & 0xFFu);  // zero + 128
 #pragma unroll
-                for (int v = 0; v < 4; ++v) acc[t][v] = fmaf(sc, fmaf(-zb, sacc[v], p[v]), acc[t][v]);
+                for (int v = 0; v < 4; ++v) acc[t][v] = fmaf(sc, p[v], acc[t][v]);
             }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -360,10 +397,7 @@ __global__ __launch_bounds__(512) void gemv_mfma_xr_kernel(const uint8_t* __rest
     const uint8_t* ring_p = smem + wave * kXrWaveRing;
     float* red = reinterpret_cast<float*>(smem + n_waves * kXrWaveRing);   // [2][waves][16][stride]
 
-    uint32_t nib_mask, bias_bits;
-    asm volatile("s_mov_b32 %0, 0x000F000F" : "=s"(nib_mask));
-    asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(bias_bits));
-    const u32x4_t ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+    const CodeConsts cc;
     const f32x4_t zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
 
     // loads of row step t into the ring half t & 1; rows past N repeat row N-1 (never stored)
@@ -417,16 +451,6 @@ __global__ __launch_bounds__(512) void gemv_mfma_xr_kernel(const uint8_t* __rest
         asm volatile("" ::: "memory");
     }
     issue_step(0);
-    f32x4_t sx[kXrGroups];
-#pragma unroll
-    for (int gi = 0; gi < kXrGroups; ++gi) {
-        sx[gi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[gi][0]), as_bf16x8(ones),
-                                                         zero4, 0, 0, 0);
-#pragma unroll
-        for (int s = 1; s < 4; ++s)
-            sx[gi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[gi][s]), as_bf16x8(ones),
-                                                             sx[gi], 0, 0, 0);
-    }
 
     for (int t = 0; t < steps; ++t) {
         const bool more = t + 1 < steps;
@@ -443,23 +467,19 @@ __global__ __launch_bounds__(512) void gemv_mfma_xr_kernel(const uint8_t* __rest
                            szw);
             const u32x4_t w4 = *reinterpret_cast<const u32x4_t*>(
                 wslots + (2 * (j >> 1) + (col >> 3)) * kXrSlotBytes + 16 * (8 * (col & 7) + 4 * (j & 1) + kb));
+            const uint32_t word = szw[j % 4];
+            const uint32_t z1 = cc.z1(word), z16 = cc.z16(word);
             f32x4_t p = zero4;
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const uint32_t w = w4[s];
-                const u32x4_t bw = {(w & nib_mask) | bias_bits, ((w >> 4) & nib_mask) | bias_bits,
-                                    ((w >> 8) & nib_mask) | bias_bits,
-                                    ((w >> 12) & nib_mask) | bias_bits};
-                p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[j][s]), as_bf16x8(bw), p,
+            for (int s = 0; s < 4; ++s)
+                p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[j][s]),
+                                                            as_bf16x8(exact_codes(w4[s], z1, z16, cc)), p,
                                                             0, 0, 0);
-            }
             // a group past the wave's range is computed with scale 0 (no branch)
-            const uint32_t word = szw[j % 4];
             const float keep = j < ng ? 1.0f : 0.0f;
             const float sc = keep * (float)__builtin_bit_cast(_Float16, (uint16_t)(word & 0xFFFFu));
-            const float zb = (float)((word >> 16) & 0xFFu);  // zero + 128
 #pragma unroll
-            for (int v = 0; v < 4; ++v) acc[v] = fmaf(sc, fmaf(-zb, sx[j][v], p[v]), acc[v]);
+            for (int v = 0; v < 4; ++v) acc[v] = fmaf(sc, p[v], acc[v]);
         }
         // partial sums of this row step: lane holds column (row) col, rows m = 4 kb + v
         float* rb = red + ((t & 1) * n_waves + wave) * 16 * kRedStride;
@@ -485,11 +505,6 @@ __global__ __launch_bounds__(512) void gemv_mfma_xr_kernel(const uint8_t* __rest
             }
         }
     }
-}
-
-int env_int(const char* name, int dflt) {
-    const char* e = getenv(name);
-    return e ? atoi(e) : dflt;
 }
 
 template <int T>
@@ -535,8 +550,7 @@ static int xr_rows(int n) {
             cu = 256;
         cus.store(cu, std::memory_order_relaxed);
     }
-    static const int rounds_env = env_int("W4A16_XR_ROUNDS", 1);
-    const long wgs = (long)cu * (rounds_env > 0 ? rounds_env : 1);
+    const long wgs = (long)cu;
     const int r = (int)((n + wgs - 1) / wgs);
     return (r + 15) / 16 * 16;
 }
@@ -565,9 +579,8 @@ static hipError_t launch_xr(const uint8_t* wq, const uint32_t* sz, const uint16_
 }
 
 bool gemv_ring_takes(int64_t n, int64_t k) {
-    static const int use_xr = env_int("W4A16_GEMV_XR", 1);
-    if (!use_xr || k / kGroup > kXrGroups * 8) return false;
-    return use_xr == 2 || xr_rows((int)n) >= 48;
+    if (k / kGroup > kXrGroups * 8) return false;
+    return xr_rows((int)n) >= 48;
 }
 
 hipError_t launch_gemv_mfma(const uint8_t* prepared, int64_t n, int64_t k, const uint16_t* x,
@@ -576,8 +589,7 @@ hipError_t launch_gemv_mfma(const uint8_t* prepared, int64_t n, int64_t k, const
     if (gemv_ring_takes(n, k))
         return launch_xr(prepared, reinterpret_cast<const uint32_t*>(prepared + sz_offset(n, k)),
                          x, y, y_bf16 ? 1 : 0, (int)n, (int)k, (int)m, xr_rows((int)n), s);
-    static const int per_wave = env_int("W4A16_MFMA_GPW", 8);
-    static const int forced_t = env_int("W4A16_MFMA_TILES", 0);
+    constexpr int per_wave = 8;
     int waves = (kg + per_wave - 1) / per_wave;
     if (waves > 8) waves = 8;
     if (waves < 1) waves = 1;
@@ -587,8 +599,6 @@ hipError_t launch_gemv_mfma(const uint8_t* prepared, int64_t n, int64_t k, const
     const uint32_t* sz = reinterpret_cast<const uint32_t*>(prepared + sz_offset(n, k));
     const int yb = y_bf16 ? 1 : 0;
     const int N = (int)n, K = (int)k, M = (int)m;
-    // tiles of 16 rows per workgroup (1 or 2)
-    if (forced_t == 1) return launch_t<1>(wq, sz, x, y, yb, N, K, M, gpw, waves, s);
     return launch_t<2>(wq, sz, x, y, yb, N, K, M, gpw, waves, s);
 }
 

@@ -1,6 +1,6 @@
 // Internal definitions shared by the libw4a16 kernels and host code.
 //
-// Prepared ("kernel") layout, format version 2.  The canonical arrays are
+// Prepared ("kernel") layout, format version 3.  The canonical arrays are
 // rearranged so that one 16-byte load feeds 32 codes to a lane and the unpack
 // needs no data movement between lanes (page "LLM Quantization Architecture in
 // Depth" › "Kernels and memory layout: the format is a contract": packed
@@ -19,8 +19,11 @@
 //                         n and group g is at ((n/4) * (K/128) + g) * 4 + n%4, so
 //                         the words of four consecutive rows of one group form
 //                         one 16-byte load.  Word: bits 0..15 the binary16
-//                         scale, bits 16..23 the zero plus 128 (mod 256), bits
-//                         24..31 zero.  Rows past N are zero words.
+//                         scale, bits 16..23 the zero, bits 24..31 the zero times
+//                         16 (mod 256): with the byte 0xE4 these two bytes form
+//                         the binary16 values -(1024 + zero) and -(1024 + 16 zero)
+//                         that turn the unpacked codes into exact q - zero.  Rows
+//                         past N are zero words.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -74,36 +77,6 @@ __device__ __forceinline__ uint32_t to_canonical_word(uint32_t p) {
     o = (o | (o << 4)) & 0x0F0F0F0Fu;
     return e | (o << 4);
 }
-
-// ---- GEMV chain plan (device copy written by the host planner, read by chain_kernel)
-// layout: ChainHeader | ChainDesc[n_desc] | int32 stage_items[n_stages]
-struct ChainHeader {
-    int32_t magic;        // kChainMagic
-    int32_t n_desc;
-    int32_t n_stages;
-    int32_t total_items;
-    int32_t grid;         // workgroups (one resident round)
-    int32_t max_k;
-    int32_t spin_limit;   // polls before a stage wait gives up (status bit 1)
-    int32_t reserved;
-};
-struct ChainDesc {
-    const uint8_t* w;     // prepared region A
-    const uint8_t* sz;    // prepared region B
-    const uint16_t* x;    // bf16 [K]
-    void* y;              // [N] f32 or bf16
-    int32_t n, k;
-    int32_t rows;         // rows per item
-    int32_t first_item;   // global index of the first item
-    int32_t n_items;
-    int32_t stage;        // 0 .. n_stages-1, non-decreasing
-    int32_t y_bf16;
-    int32_t reserved;
-};
-constexpr int32_t kChainMagic = 0x57344348;  // "W4CH"
-size_t chain_lds_bytes(int max_k);
-int chain_grid(int max_k);
-hipError_t launch_chain(const ChainHeader& h, const uint8_t* plan_dev, uint32_t* ws, hipStream_t s);
 
 // Launch wrappers (defined in the .hip files); return hipSuccess or the launch error.
 // Storage variant of the weight format: group of 32, 64 or 128 inputs, scale stored as

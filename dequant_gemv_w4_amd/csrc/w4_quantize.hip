@@ -195,7 +195,7 @@ __global__ __launch_bounds__(256) void prepare_kernel(const uint4* __restrict__ 
             const int64_t src = row * kg + g;
             const uint32_t z = zero4 ? ((uint32_t)zeros[src >> 1] >> (4 * (src & 1))) & 0xFu
                                      : (uint32_t)zeros[src];
-            v = (uint32_t)scales[src] | (((z + 128u) & 0xFFu) << 16);
+            v = (uint32_t)scales[src] | ((z & 0xFFu) << 16) | (((z << 4) & 0xFFu) << 24);
         }
         out_sz[i] = v;
     }
@@ -219,13 +219,13 @@ __global__ __launch_bounds__(256) void unprepare_kernel(const uint4* __restrict_
     }
     auto zero_of = [&](int64_t i) {
         const int64_t row = i / kg;
-        return (((sz[sz_index(row, i - row * kg, kg)] >> 16) - 128u) & 0xFFu);
+        return (sz[sz_index(row, i - row * kg, kg)] >> 16) & 0xFFu;
     };
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_groups; i += stride) {
         const int64_t row = i / kg;
         const uint32_t v = sz[sz_index(row, i - row * kg, kg)];
         scales[i] = (uint16_t)(v & 0xFFFFu);
-        if (!zero4) zeros[i] = (uint8_t)(((v >> 16) - 128u) & 0xFFu);
+        if (!zero4) zeros[i] = (uint8_t)((v >> 16) & 0xFFu);
     }
     if (zero4) {
         // one thread per byte: groups 2i and 2i+1

@@ -25,15 +25,12 @@
 // with exact int32 sums.  w8_gemm_ring_kernel (the default for both): 512 threads per
 // 128 x 256 output tile, wave (wm, wn) owns 64 x 64 as 2 x 2 MFMA tiles, a K step is 128
 // inputs loaded straight into a three-stage LDS ring two steps ahead.
-// fp8_gemm_staged_kernel (FP8, other tile shapes) stages the loads through two register
-// sets into a double-buffered LDS tile.  In LDS, 16-byte chunk c of row r sits at slot
+// In LDS, 16-byte chunk c of row r sits at slot
 // c ^ ((r / 2) & 7) (w8_slot), so the operand reads of 16 consecutive rows, which share a
 // cycle, touch 16 different 16-byte bank groups.  For FP8 a lane
 // supplies row (lane % 32) and the 32 inputs 32 * (lane / 32) .. +31 of a 64-input MFMA
 // step, the same inputs for both operands, so each output is a dot product over matching
 // inputs whatever order the unit sums them in.
-#include <cstdlib>
-
 #include "w4_internal.h"
 
 namespace w4 {
@@ -237,144 +234,6 @@ constexpr int kFK = 128;  // K step (bytes = inputs)
 // The map is its own inverse: the loader fetches chunk w8_slot(r, s) into slot s.
 __device__ __forceinline__ int w8_slot(int r, int c) { return c ^ ((r >> 1) & 7); }
 
-// Output tile (WGM * TM * 32) x (WGN * TN * 32): WGM x WGN waves, each owning TM x TN MFMA
-// tiles of 32 x 32.
-template <int TM, int TN, int WGM, int WGN>
-__global__ __launch_bounds__(64 * WGM * WGN) void fp8_gemm_staged_kernel(
-    const uint8_t* __restrict__ X, const float* __restrict__ sx, const uint8_t* __restrict__ W,
-    const float* __restrict__ sw, void* __restrict__ Y, int y_bf16, int M, int N, int K,
-    int tiles_n) {
-    constexpr int T = 64 * WGM * WGN;
-    constexpr int BM = WGM * TM * 32;
-    constexpr int BN = WGN * TN * 32;
-    constexpr int UX = BM * kFK / 16 / T;   // 16-byte chunks per thread and step
-    constexpr int UW = BN * kFK / 16 / T;
-    static_assert(UX * T * 16 == BM * kFK && UW * T * 16 == BN * kFK, "tile not covered");
-    __shared__ __attribute__((aligned(16))) uint8_t ldsx[2][BM * kFK];
-    __shared__ __attribute__((aligned(16))) uint8_t ldsw[2][BN * kFK];
-    const int tid = threadIdx.x;
-    const int wave = tid >> 6;
-    const int lane = tid & 63;
-    const int wm = wave / WGN;
-    const int wn = wave % WGN;
-    const int m0 = (int)(blockIdx.x / tiles_n) * BM;
-    const int n0 = (int)(blockIdx.x % tiles_n) * BN;
-
-    // staging: chunk i = tid + T u of a tile is row i / 8, 16-byte chunk i % 8
-    const uint8_t* gx[UX];
-    const uint8_t* gw[UW];
-    uint32_t sxo[UX], swo[UW];
-#pragma unroll
-    for (int u = 0; u < UX; ++u) {
-        const int i = tid + T * u, r = i >> 3, c = i & 7;
-        gx[u] = X + (int64_t)min(m0 + r, M - 1) * K + 16 * c;   // rows past M repeat M-1
-        sxo[u] = (uint32_t)(r * kFK + (w8_slot(r, c) << 4));
-    }
-#pragma unroll
-    for (int u = 0; u < UW; ++u) {
-        const int i = tid + T * u, r = i >> 3, c = i & 7;
-        gw[u] = W + (int64_t)min(n0 + r, N - 1) * K + 16 * c;
-        swo[u] = (uint32_t)(r * kFK + (w8_slot(r, c) << 4));
-    }
-    // two register sets, so a step's loads are issued two steps before they are stored:
-    // set 0 holds the even steps, set 1 the odd ones.  Loads past the last step repeat it
-    // (no branch, so the compiler's wait counts stay exact).
-    u32x4_t rx[2][UX], rw[2][UW];
-    const int Kt = K / kFK;
-    auto load = [&](int set, int kt) {
-        kt = min(kt, Kt - 1);
-#pragma unroll
-        for (int u = 0; u < UX; ++u) rx[set][u] = *reinterpret_cast<const u32x4_t*>(gx[u] + (int64_t)kt * kFK);
-#pragma unroll
-        for (int u = 0; u < UW; ++u) rw[set][u] = *reinterpret_cast<const u32x4_t*>(gw[u] + (int64_t)kt * kFK);
-    };
-    auto store = [&](int set, int b) {
-#pragma unroll
-        for (int u = 0; u < UX; ++u) *reinterpret_cast<u32x4_t*>(&ldsx[b][sxo[u]]) = rx[set][u];
-#pragma unroll
-        for (int u = 0; u < UW; ++u) *reinterpret_cast<u32x4_t*>(&ldsw[b][swo[u]]) = rw[set][u];
-    };
-    // the 32 inputs 64 kh + 32 (lane / 32) .. +31 of row r of an operand tile
-    auto operand = [&](const uint8_t* t, int r, int kh) {
-        const int c0 = 4 * kh + 2 * (lane >> 5);
-        const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(&t[r * kFK + (w8_slot(r, c0) << 4)]);
-        const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(&t[r * kFK + (w8_slot(r, c0 + 1) << 4)]);
-        const v8i_t v = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                         (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-        return v;
-    };
-
-    f32x16_t acc[TM][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = (f32x16_t){};
-
-    auto compute = [&](int b) {
-        // both 64-input halves of the step are read before the first MFMA
-        v8i_t xa[2][TM], wb[2][TN];
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-#pragma unroll
-            for (int i = 0; i < TM; ++i) xa[kh][i] = operand(ldsx[b], TM * 32 * wm + 32 * i + (lane & 31), kh);
-#pragma unroll
-            for (int j = 0; j < TN; ++j) wb[kh][j] = operand(ldsw[b], TN * 32 * wn + 32 * j + (lane & 31), kh);
-        }
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    // formats 0 / 0: E4M3 for both operands; block scales 127 = 2^0
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        xa[kh][i], wb[kh][j], acc[i][j], 0, 0, 0, 127, 0, 127);
-    };
-
-    // the scheduling barriers keep every load ahead of the step it overlaps (the scheduler
-    // would otherwise sink it next to its store and leave a single step of latency cover)
-    load(0, 0);
-    load(1, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    store(0, 0);
-    __syncthreads();
-    for (int kt = 0; kt < Kt; kt += 2) {
-        load(0, kt + 2);          // step kt + 2 into set 0 (its step kt is in LDS buffer 0)
-        __builtin_amdgcn_sched_barrier(0);
-        compute(0);
-        store(1, 1);              // step kt + 1, issued two steps ago
-        __syncthreads();
-        load(1, kt + 3);
-        __builtin_amdgcn_sched_barrier(0);
-        if (kt + 1 < Kt) compute(1);
-        store(0, 0);              // step kt + 2
-        __syncthreads();
-    }
-
-    // element v of a 32 x 32 result: column lane % 32, row 8 (v / 4) + 4 (lane / 32) + v % 4
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int c = n0 + TN * 32 * wn + 32 * j + (lane & 31);
-            if (c >= N) continue;
-            const float scw = sw[c];
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int r = m0 + TM * 32 * wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                if (r >= M) continue;
-                const float y = acc[i][j][v] * sx[r] * scw;
-                const int64_t o = (int64_t)r * N + c;
-                if (y_bf16) {
-                    const uint32_t u = __float_as_uint(y);
-                    static_cast<uint16_t*>(Y)[o] = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-                } else {
-                    static_cast<float*>(Y)[o] = y;
-                }
-            }
-        }
-}
-
 // 16 bytes per lane from global memory straight into LDS: lane l of the wave writes bytes
 // [16 l, 16 l + 16) after the wave-uniform LDS address.  Inline assembly, so the compiler
 // does not order the LDS reads of other stages behind these loads; the kernel waits for
@@ -386,7 +245,7 @@ __device__ __forceinline__ void w8_load_lds16(const void* g, uint32_t lds_addr) 
                  : "memory", "m0");
 }
 
-// The same product with a three-stage LDS ring filled by direct loads two steps ahead:
+// The product with a three-stage LDS ring filled by direct loads two steps ahead:
 // 512 threads, 128 x 256 output tile, wave (wm, wn) owns 64 x 64 (2 x 2 MFMA tiles).  A
 // stage is the X tile (128 rows x 128 inputs, 16 KiB) and the W tile (256 x 128, 32 KiB),
 // chunk c of row r at slot w8_slot(r, c): each wave issues 2 X and 4 W loads of 8 rows x
@@ -549,30 +408,15 @@ __global__ __launch_bounds__(512) void w8_gemm_ring_kernel(
         }
 }
 
-template <int TM, int TN, int WGM, int WGN>
-hipError_t launch_fp8_gemm_t(const uint8_t* xq, const float* sx, int64_t m, const uint8_t* wq,
-                             const float* sw, int64_t n, int64_t k, void* y, bool y_bf16,
-                             hipStream_t s) {
-    constexpr int BM = WGM * TM * 32, BN = WGN * TN * 32;
-    const int tiles_n = (int)((n + BN - 1) / BN);
-    const int64_t tiles = ((m + BM - 1) / BM) * tiles_n;
-    hipLaunchKernelGGL((fp8_gemm_staged_kernel<TM, TN, WGM, WGN>), dim3((unsigned)tiles),
-                       dim3(64 * WGM * WGN), 0, s, xq, sx, wq, sw, y, y_bf16 ? 1 : 0, (int)m,
-                       (int)n, (int)k, tiles_n);
-    return hipGetLastError();
-}
-
 template <bool INT8>
 hipError_t launch_ring(const uint8_t* xq, const float* sx, int64_t m, const uint8_t* wq,
                        const float* sw, int64_t n, int64_t k, void* y, bool y_bf16,
                        hipStream_t s) {
-    static const int group_env = [] {
-        const char* e = getenv("W4A16_W8_GROUP_M");
-        return e ? atoi(e) : 8;
-    }();
+    // bands of 8 M tiles in the XCD-aware order (measured on MI355X at 4096 x 28672 x 8192:
+    // bands of 4, 16 and 32 ran 1-4 % slower for FP8)
     const int tiles_n = (int)((n + 255) / 256);
     const int tiles_m = (int)((m + 127) / 128);
-    const int group_m = group_env < 1 ? 1 : (group_env > tiles_m ? tiles_m : group_env);
+    const int group_m = tiles_m < 8 ? tiles_m : 8;
     const int per_xcd = (tiles_m * tiles_n + kW8Xcds - 1) / kW8Xcds;
     hipLaunchKernelGGL(w8_gemm_ring_kernel<INT8>, dim3((unsigned)(per_xcd * kW8Xcds)), dim3(512),
                        0, s, xq, sx, wq, sw, y, y_bf16 ? 1 : 0, (int)m, (int)n, (int)k, tiles_m,
@@ -609,16 +453,9 @@ hipError_t launch_fp8_gemm(const uint8_t* xq, const float* sx, int64_t m, const 
                            const float* sw, int64_t n, int64_t k, void* y, bool y_bf16,
                            hipStream_t s) {
     // measured on MI355X at 4096 x 28672 x 8192: the three-stage ring 1.09-1.10 ms; register
-    // staging two steps ahead 1.14-1.16 ms with 128 x 256 tiles (W4A16_FP8_TILE=256), 1.16 ms
-    // with 256 x 128, 1.58 ms with 128 x 128 tiles (W4A16_FP8_TILE=128)
-    static const int tile = [] {
-        const char* e = getenv("W4A16_FP8_TILE");
-        return e ? atoi(e) : 1;
-    }();
-    if (tile == 128)
-        return launch_fp8_gemm_t<2, 2, 2, 2>(xq, sx, m, wq, sw, n, k, y, y_bf16, s);
-    if (tile != 256) return launch_ring<false>(xq, sx, m, wq, sw, n, k, y, y_bf16, s);
-    return launch_fp8_gemm_t<2, 2, 2, 4>(xq, sx, m, wq, sw, n, k, y, y_bf16, s);
+    // staging two steps ahead 1.14-1.16 ms with 128 x 256 tiles, 1.16 ms with 256 x 128,
+    // 1.58 ms with 128 x 128 tiles
+    return launch_ring<false>(xq, sx, m, wq, sw, n, k, y, y_bf16, s);
 }
 
 }  // namespace w4

@@ -13,7 +13,7 @@ from __future__ import annotations
 import ctypes
 from dataclasses import dataclass
 
-from . import W4_BF16, W4_F32, W4Error, lib, w4_chain_plan, w4_chain_run, w4_chain_workspace_bytes
+from . import W4_BF16, W4_F32, W4Error, lib
 
 
 @dataclass
@@ -70,57 +70,6 @@ class DecodeStep:
         """Record the whole step once into a graph (replayed by run())."""
         import torch
         self.run_eager()                      # warm caches and the device check outside capture
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            self.run_eager()
-        torch.cuda.synchronize()
-        self._graph = g
-
-    def run(self) -> None:
-        if self._graph is not None:
-            self._graph.replay()
-        else:
-            self.run_eager()
-
-
-class GemvChain:
-    """The same products as a DecodeStep, as stages of one persistent launch.
-
-    ``stages`` is a list of lists of GemvCall with M = 1; calls within a stage are
-    independent, and a stage may read what earlier stages wrote.
-    """
-
-    def __init__(self, stages):
-        import torch
-        entries = []
-        self.calls = []
-        for s, calls in enumerate(stages):
-            for c in calls:
-                if c.x.shape[0] != 1:
-                    raise ValueError("the chain runs M = 1 products")
-                entries.append((c.prepared, c.x.reshape(-1), c.y.reshape(-1), c.n, c.k, s))
-                self.calls.append(c)
-        dev = self.calls[0].x.device
-        self.plan_host = w4_chain_plan(entries)
-        self.plan_dev = torch.from_numpy(self.plan_host).to(dev)
-        nws = (w4_chain_workspace_bytes(len(entries)) + 3) // 4
-        self.workspace = torch.zeros(nws, dtype=torch.int32, device=dev)
-        self._graph = None
-
-    def algorithmic_bytes(self) -> int:
-        return sum(c.algorithmic_bytes() for c in self.calls)
-
-    def status(self) -> int:
-        """Status word (bit 0: a stage wait gave up); synchronizes."""
-        return int(self.workspace[0].item())
-
-    def run_eager(self) -> None:
-        w4_chain_run(self.plan_dev, self.plan_host, self.workspace)
-
-    def capture(self) -> None:
-        import torch
-        self.run_eager()
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):

@@ -21,7 +21,8 @@
  *     the low nibble; scales [N, K/128] binary16 bit patterns (the binary32
  *     scale rounded to nearest even); zeros [N, K/128] bytes.
  *   - w_hat = (code - zero) * scale16 and the products use, per group,
- *     scale16 * (sum code*x - zero * sum x): one multiply per group.
+ *     scale16 * sum (code - zero) * x: one multiply per group, with the exact
+ *     difference code - zero as the operand of every product.
  *
  * Readings of points the pages leave open are fixed above: halves away from
  * zero, codes from the binary32 scale, fp16 stored scale, byte zero.
@@ -48,7 +49,7 @@ extern "C" {
 #endif
 
 #define W4_GROUP 128
-#define W4_FORMAT_VERSION 2
+#define W4_FORMAT_VERSION 3
 #define W4_GEMV_MAX_M 16
 #define W4_GEMV_MAX_K 32768
 #define W4_FP8_MAX_K 65536
@@ -113,6 +114,8 @@ w4_status w4_quantize_symmetric(const void* W, w4_dtype wt, int64_t N, int64_t K
  *   packed/scales_f16/zeros  canonical arrays as produced by w4_quantize
  *                            (packed 16-B aligned, scales 2-B aligned).
  *   prepared                 [w4_prepared_bytes(N, K)] bytes, 256-B aligned.
+ * The products read zeros 0..15 (what w4_quantize writes); the round trip holds for
+ * any byte.
  */
 size_t w4_prepared_bytes(int64_t N, int64_t K);
 w4_status w4_prepare(const uint8_t* packed, const uint16_t* scales_f16, const uint8_t* zeros,
@@ -126,7 +129,12 @@ w4_status w4_unprepare(const void* prepared, int64_t N, int64_t K,
  * w4_gemv -- decode-sized product y[m, n] = sum_k w_hat[n, k] * x[m, k] for
  * 1 <= M <= 16, never forming w_hat in memory (page "Weight quantization",
  * "How it works": the per-group factored dot; architecture page stage "Fused
- * Kernels": dequantization inside the product).
+ * Kernels": dequantization inside the product).  Every product multiplies the exact
+ * value q - zero of a code (a code equal to its zero adds exactly 0); bf16 x enters
+ * the one-row kernel as binary16 x * 2^-E per 32-input slice (exact within 2^25 of the
+ * slice's largest value; a wave with a slice outside that window, and binary32 x, use
+ * one binary32 FMA per input instead) and the matrix-core kernels (2 <= M <= 16) as
+ * bf16 with bf16 q - zero codes.
  *   prepared  from w4_prepare (256-B aligned).
  *   x         [M, K] row-major, bfloat16 (xt = W4_BF16) or binary32 (W4_F32); 16-B aligned.
  *   y         [M, N] row-major, binary32 (yt = W4_F32) or bfloat16 (W4_BF16); must
@@ -194,7 +202,7 @@ w4_status w4_unprepare_fmt(const void* prepared, int64_t N, int64_t K, const w4_
 
 /*
  * w4_gemv_fmt -- w4_gemv on the prepared layout of format *fmt (page "Weight
- * quantization", "How it works": scale * (sum code*x - zero * sum x) per group).  The
+ * quantization", "How it works": scale * sum (code - zero) * x per group).  The
  * canonical-layout formats (group 128, binary16 scales) take w4_gemv's kernels; the
  * others run on its one-row (VALU) kernel at every M, in steps of up to four rows of x.
  * Arguments, limits and errors as w4_gemv.
@@ -207,16 +215,20 @@ w4_status w4_gemv_fmt(const void* prepared, int64_t N, int64_t K, const w4_forma
  * w4_gemm -- prefill-sized product Y[M, N] = X[M, K] * w_hat^T for any M >= 1
  * (page "LLM Quantization Architecture in Depth" › "Why fewer bits make
  * decoding faster": prefill is compute bound and weight-only formats must turn
- * weights back into 16-bit values before the matrix units).  The codes enter
- * bf16 MFMA as the exact values 128+q; per group the f32 accumulator receives
- * scale16 * (P - (128+zero) * sum x) (page "Weight quantization", "How it
- * works": the factored group dot), so no weight is rounded.
+ * weights back into 16-bit values before the matrix units).  The codes enter the
+ * binary16 MFMA as the exact values q - zero and X as binary16 X * 2^-E[m] (E per
+ * row, exact for every value within 2^25 of the row's largest); per group the f32
+ * accumulator receives scale16 * P (page "Weight quantization", "How it works": the
+ * dequantized weight (code - zero) * scale, one multiply per group), so no weight
+ * and no activation is rounded.  Rows of X with a value outside that window are
+ * recomputed by a fix-up pass with one binary32 FMA per weight.
  *   prepared  from w4_prepare.
  *   X         [M, K] bfloat16 row-major; 16-B aligned.
  *   Y         [M, N] row-major, binary32 or bfloat16; 4-B aligned.
- *   workspace device scratch of w4_gemm_workspace_bytes(M, N, K) bytes (per-group
- *             sums of X; K/128 * ceil(M/128)*128 floats), 16-B aligned; contents
- *             need no initialisation.  Calls sharing a workspace must be ordered.
+ *   workspace device scratch of w4_gemm_workspace_bytes(M, N, K) bytes (the binary16
+ *             copy of X, then per row its exponent and a window flag, each part
+ *             256-B aligned), 16-B aligned; contents need no initialisation.  Calls
+ *             sharing a workspace must be ordered.
  * Limits: N, K as w4_prepare; 1 <= M <= 65535*128; at most 2^31 - 9 output tiles of
  * 128 x 256 (else W4_ERR_SHAPE).
  */
@@ -224,47 +236,6 @@ size_t w4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 w4_status w4_gemm(const void* prepared, int64_t N, int64_t K,
                   const void* X, int64_t M, void* Y, w4_dtype yt,
                   void* workspace, size_t workspace_bytes, hipStream_t stream);
-
-/*
- * GEMV chain -- a decode step's products (M = 1, bf16 x) in one persistent launch.
- * Entries with the same stage are independent; stage s may read what stages < s
- * wrote (an x may be an earlier y), so every item of stage s is computed after all
- * of stage s-1 has been stored, while weight loads run ahead across the boundary
- * (page "Weight quantization", "Complexity and constants": decode time is bytes
- * read / bandwidth; "LLM Quantization Architecture in Depth", "Kernels and memory
- * layout": fused kernels).  Within one stage no y may overlap any x.
- *
- *   w4_chain_plan_bytes(count)       host/device plan size for `count` entries.
- *   w4_chain_plan(gemvs, count, plan_host, plan_bytes)
- *       validates the entries (host memory) and writes the plan into plan_host
- *       (host memory, caller-owned); the caller copies it unchanged to device memory
- *       (plan_dev, 16-B aligned).  stage values must be non-decreasing; K <= 32768.
- *   w4_chain_workspace_bytes(count)  device workspace size: 32-bit word 0 is a status
- *       word, the others are counters.  The workspace must be zero-filled once before
- *       its first use; every completed launch leaves the counters zeroed again.  Bit 0
- *       of the status word is set (never cleared) if a stage wait gave up after about
- *       two seconds of polling (results are then incomplete).  Launches sharing one
- *       workspace must be ordered (same stream).
- *   w4_chain_run(plan_dev, plan_host, workspace, workspace_bytes, stream)
- *       launches the chain described by the plan (plan_host is read for the launch
- *       geometry only).  Results equal w4_gemv's up to f32 summation order.
- */
-typedef struct w4_chain_gemv {
-    const void* prepared;  /* from w4_prepare, 256-B aligned */
-    const void* x;         /* [K] bfloat16, 16-B aligned */
-    void* y;               /* [N] binary32 or bfloat16 (y_dtype), 4-B aligned */
-    int64_t n;
-    int64_t k;
-    int32_t stage;
-    int32_t y_dtype;       /* W4_F32 or W4_BF16 */
-} w4_chain_gemv;
-
-size_t w4_chain_plan_bytes(int64_t count);
-size_t w4_chain_workspace_bytes(int64_t count);
-w4_status w4_chain_plan(const w4_chain_gemv* gemvs, int64_t count, void* plan_host,
-                        size_t plan_bytes);
-w4_status w4_chain_run(const void* plan_dev, const void* plan_host, void* workspace,
-                       size_t workspace_bytes, hipStream_t stream);
 
 /*
  * W8A8 in FP8 E4M3 for prefill (page "LLM Quantization Architecture in Depth" › "Why fewer

@@ -249,3 +249,57 @@ def page_error_matrix(seed: int = 11, rows: int = 256, cols: int = 1024) -> np.n
         w[r, c] = sign * 0.6
     return w
 
+
+
+# --------------------------------------------------------------------------
+# Sparse groups and wide-range activations (edge cases of the products)
+# --------------------------------------------------------------------------
+
+def sparse_group_weights(n: int, k: int, seed: int, group: int = 128):
+    """W [n, k] f32 in which every group of ``group`` inputs has 1-3 non-zero weights at
+    positions shared by all rows (the rest exact 0.0), one of them negative and one
+    positive where there are two or more, so that the zero point of most groups is neither
+    0 nor 15 and most codes equal it.  Returns (W, positions [k] bool).
+    """
+    rng = np.random.default_rng(seed)
+    pos = np.zeros(k, dtype=bool)
+    for g in range(k // group):
+        cnt = int(rng.integers(1, 4))
+        pos[g * group + rng.choice(group, cnt, replace=False)] = True
+    w = np.zeros((n, k), dtype=np.float32)
+    idx = np.flatnonzero(pos)
+    mag = (0.02 * (0.5 + rng.random((n, idx.size)))).astype(np.float32)
+    sign = np.where(rng.random((n, idx.size)) < 0.5, -1.0, 1.0).astype(np.float32)
+    # the first non-zero of each group negative, the second positive (when present)
+    g_of = idx // group
+    first = np.r_[True, g_of[1:] != g_of[:-1]]
+    second = np.r_[False, first[:-1] & (g_of[1:] == g_of[:-1])]
+    sign[:, first] = -1.0
+    sign[:, second] = 1.0
+    w[:, idx] = mag * sign
+    return w, pos
+
+
+def sparse_group_activations(m: int, positions: np.ndarray, seed: int, small: float = 1e-2,
+                             large: float = 3.0):
+    """x [m, k] f32: about ``small`` in magnitude at ``positions``, about ``large`` elsewhere,
+    random signs."""
+    rng = np.random.default_rng(seed)
+    k = positions.size
+    mag = np.where(positions, small, large) * (1.0 + 0.1 * rng.standard_normal((m, k)))
+    sign = np.where(rng.random((m, k)) < 0.5, -1.0, 1.0)
+    return (mag * sign).astype(np.float32)
+
+
+def wide_range_activations(m: int, k: int, seed: int, span_log2: int = 40):
+    """x [m, k] f32 ~ N(0, 1) in which every fourth 32-input slice also holds one value
+    2^(span/2) times larger and one 2^(span/2) times smaller than the rest, so that a slice
+    spans about 2^span in magnitude."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((m, k))
+    half = 2.0 ** (span_log2 // 2)
+    for s in range(0, k // 32, 4):
+        a, b = rng.choice(32, 2, replace=False)
+        x[:, 32 * s + a] *= half
+        x[:, 32 * s + b] /= half
+    return x.astype(np.float32)

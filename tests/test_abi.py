@@ -21,7 +21,7 @@ def test_library_loads_and_exports_declared_symbols():
 
 
 def test_format_version_and_status_strings():
-    assert w4.w4_format_version() == 2
+    assert w4.w4_format_version() == 3
     assert w4.w4_status_string(0) == "ok"
     assert "gfx950" in w4.w4_status_string(6)
     assert w4.w4_status_string(99) == "unknown status"
@@ -35,8 +35,9 @@ def test_prepared_bytes_closed_form():
     assert w4.w4_prepared_bytes(5, 128) == 512 + 8 * 1 * 4
     assert w4.w4_prepared_bytes(1, 100) == 0     # K not a multiple of 128
     assert w4.w4_prepared_bytes(0, 128) == 0
-    assert w4.w4_gemm_workspace_bytes(4096, 28672, 8192) == 64 * 4096 * 4
-    assert w4.w4_gemm_workspace_bytes(200, 300, 384) == 3 * 256 * 4
+    # binary16 copy of X, then the rows' exponents and exactness flags (each 256-B aligned)
+    assert w4.w4_gemm_workspace_bytes(4096, 28672, 8192) == 4096 * 8192 * 2 + 2 * 4096 * 4
+    assert w4.w4_gemm_workspace_bytes(200, 300, 384) == 200 * 384 * 2 + 2 * 1024
 
 
 def _fake(addr=0x100000):

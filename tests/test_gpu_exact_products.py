@@ -1,0 +1,116 @@
+"""GPU parity of the products on inputs where exact operands matter.
+
+* Sparse groups: 1-3 non-zero weights per group of 128, the rest exact 0.0, one weight
+  negative and one positive, so the zero point is neither 0 nor 15 and every zero weight
+  encodes to it (page "Weight quantization" › "Code": the range is widened so that 0 stays
+  exactly representable).  Activations are about 3 where the codes equal the zero point and
+  about 1e-2 at the non-zero weights, so sum |w_hat x| is tiny next to sum |x|: a product
+  that carried a bias through the code (128 + q, corrected by zero * sum x) would miss the
+  tolerance by orders of magnitude.
+* Wide activations: 32-input slices spanning about 2^40, outside the binary16 window of
+  the one-row kernel (its exact path then runs) and of the GEMM pre-pass (its fix-up pass
+  recomputes the row).
+
+Bar as everywhere: |y - y_ref| <= 1e-3 * sum_k |w_hat[n, k] x[m, k]| for every output,
+y_ref the oracle's fp64 dequantize-then-dot; codes bit-exact.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import dequant_gemv_w4_amd as w4
+import oracle
+import synth
+from _util import assert_quant_equal, assert_within, quant_arrays_np, to_np32
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+# (N, K) reaching each product kernel: the one-row kernel at M = 1..3 on every shape; for
+# bf16 x at larger M the streaming matrix-core kernel (few rows, or K > 64 groups) and the
+# ring kernel (K <= 64 groups, at least 48 rows per workgroup over 256 compute units)
+SHAPES = {"small": (300, 1024), "ring": (12288, 1024), "stream": (520, 9216)}
+M_VALUES = (1, 2, 3, 4, 8, 16)
+
+
+def _quant_prepare(w):
+    p, s, z = w4.w4_quantize(torch.from_numpy(w).to(DEV))
+    ref = oracle.quantize_ref(w)
+    assert_quant_equal(quant_arrays_np(p, s, z), ref, "codes")
+    return w4.w4_prepare(p, s, z), ref
+
+
+def _check_gemv(prep, ref, n, k, x, what):
+    rp, rs, rz = ref
+    y = to_np32(w4.w4_gemv(prep, n, k, x))
+    xn = to_np32(x)
+    return assert_within(y, oracle.gemv_ref(rp, rs, rz, xn), oracle.tolerance_ref(rp, rs, rz, xn), what)
+
+
+def _check_gemm(prep, ref, n, k, X, what):
+    rp, rs, rz = ref
+    Y = to_np32(w4.w4_gemm(prep, n, k, X))
+    Xn = to_np32(X)
+    return assert_within(Y, oracle.gemv_ref(rp, rs, rz, Xn), oracle.tolerance_ref(rp, rs, rz, Xn), what)
+
+
+@pytest.mark.parametrize("shape", list(SHAPES))
+def test_sparse_groups_with_nonzero_zero_point(shape):
+    n, k = SHAPES[shape]
+    w, pos = synth.sparse_group_weights(n, k, seed=31 + n)
+    prep, ref = _quant_prepare(w)
+    rp, rs, rz = ref
+    # the case at stake: most codes equal a zero point that is neither 0 nor 15
+    codes = oracle.unpack_codes(rp)
+    zeros_per_input = np.repeat(rz, 128, axis=1)
+    assert np.mean(codes == zeros_per_input) > 0.95
+    assert np.mean((rz > 0) & (rz < 15)) > 0.5
+    x = synth.sparse_group_activations(16, pos, seed=32 + n)
+    worst = 0.0
+    for dtype in (torch.bfloat16, torch.float32):
+        for m in M_VALUES:
+            xm = torch.from_numpy(x[:m]).to(DEV).to(dtype).contiguous()
+            worst = max(worst, _check_gemv(prep, ref, n, k, xm, f"{shape} M={m} {dtype}"))
+    X = torch.from_numpy(np.tile(x, (13, 1))[:200]).to(DEV).to(torch.bfloat16)
+    worst = max(worst, _check_gemm(prep, ref, n, k, X, f"{shape} GEMM M=200"))
+    print(f"{shape}: worst err/bound {worst:.3e}")
+
+
+@pytest.mark.parametrize("shape", list(SHAPES))
+def test_wide_range_activations(shape):
+    n, k = SHAPES[shape]
+    rng = np.random.default_rng(41 + n)
+    w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
+    prep, ref = _quant_prepare(w)
+    x = synth.wide_range_activations(16, k, seed=42 + n)
+    worst = 0.0
+    for dtype in (torch.bfloat16, torch.float32):
+        for m in M_VALUES:
+            xm = torch.from_numpy(x[:m]).to(DEV).to(dtype).contiguous()
+            worst = max(worst, _check_gemv(prep, ref, n, k, xm, f"{shape} M={m} {dtype}"))
+    # GEMM: odd rows wide (fix-up pass), even rows ordinary (matrix cores)
+    X = rng.standard_normal((150, k)).astype(np.float32)
+    X[1::2] = np.tile(x, (5, 1))[: X[1::2].shape[0]]
+    worst = max(worst, _check_gemm(prep, ref, n, k, torch.from_numpy(X).to(DEV).to(torch.bfloat16),
+                                   f"{shape} GEMM M=150"))
+    print(f"{shape}: worst err/bound {worst:.3e}")
+
+
+def test_zero_weights_and_exact_zero_rows():
+    """Rows of exact zeros (zero point 0) and groups of one repeated negative value give
+    exact results whatever x is."""
+    n, k = 96, 2048
+    rng = np.random.default_rng(5)
+    w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
+    w[3] = 0.0
+    w[10, :128] = -0.5     # one-signed group: zero 15, codes 0
+    prep, ref = _quant_prepare(w)
+    x = (100.0 * rng.standard_normal((16, k))).astype(np.float32)
+    for m in (1, 3, 16):
+        xm = torch.from_numpy(x[:m]).to(DEV).to(torch.bfloat16)
+        y = to_np32(w4.w4_gemv(prep, n, k, xm))
+        assert np.all(y[:, 3] == 0.0)
+        _check_gemv(prep, ref, n, k, xm, f"M={m}")
+    Y = to_np32(w4.w4_gemm(prep, n, k, torch.from_numpy(x).to(DEV).to(torch.bfloat16)))
+    assert np.all(Y[:, 3] == 0.0)
