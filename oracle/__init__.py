@@ -4,7 +4,7 @@ from .w4_oracle import (  # noqa: F401
     GROUP, QMAX, f32, ieee_div, round_away, clamp_code, to_code, fp16_bits, fp16_value,
     quantize_group_scalar, quantize_scalar, dot_scalar, dot_factored_exact,
     quantize_ref, unpack_codes, dequant_ref, gemv_ref, gemv_factored_ref,
-    tolerance_ref, gemm_ref_rows, bits_per_weight, quantize_symmetric_ref, SYM_ZERO,
+    tolerance_ref, bits_per_weight, quantize_symmetric_ref, SYM_ZERO,
     quantize_ref_f32, quantize_symmetric_ref_f32,
 )
 from .w4_formats import (  # noqa: F401

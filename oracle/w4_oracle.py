@@ -351,12 +351,6 @@ def tolerance_ref(packed, scales16, zeros, x, group: int = GROUP, rows=None,
     return rel * out
 
 
-def gemm_ref_rows(packed, scales16, zeros, X, m_rows, group: int = GROUP, chunk: int = 2048):
-    """Rows ``m_rows`` of Y = X @ w_hat.T in fp64 (all N columns)."""
-    X = np.asarray(X)
-    return gemv_ref(packed, scales16, zeros, X[np.asarray(m_rows)], group, chunk=chunk)
-
-
 def bits_per_weight(n_weights: int, packed_len: int, n_scales: int, n_zeros: int,
                     scale_bits: int = 16, zero_bits: int = 8) -> float:
     """Storage bits per weight of a quantized tensor."""
