@@ -51,3 +51,19 @@ def assert_within(y_gpu: np.ndarray, y_ref: np.ndarray, bound: np.ndarray, what=
 def oracle_quant_rows(W32: np.ndarray, rows):
     """Oracle quantization of selected rows (groups never cross rows)."""
     return oracle.quantize_ref(np.ascontiguousarray(W32[rows]))
+
+
+def check_quant_and_oracle_products(W, p, s, z, x32: np.ndarray, chunk: int = 2048, what=""):
+    """Oracle quantization of every row of the GPU weights W (copied in row chunks), checked
+    bit-exact against the GPU's canonical arrays (p, s, z), and the oracle's products with
+    x32 [M, K] and their bounds for every row.  Returns (y_ref [M, N], bound [M, N])."""
+    n = W.shape[0]
+    yr = np.empty((x32.shape[0], n), dtype=np.float64)
+    bound = np.empty_like(yr)
+    for r0 in range(0, n, chunk):
+        r1 = min(n, r0 + chunk)
+        ref = oracle.quantize_ref(to_np32(W[r0:r1]))
+        assert_quant_equal(quant_arrays_np(p[r0:r1], s[r0:r1], z[r0:r1]), ref, f"{what} rows {r0}..{r1}")
+        yr[:, r0:r1] = oracle.gemv_ref(*ref, x32)
+        bound[:, r0:r1] = oracle.tolerance_ref(*ref, x32)
+    return yr, bound

@@ -14,7 +14,8 @@ import torch
 import bench
 import oracle
 import synth
-from _util import assert_within, to_np32
+import dequant_gemv_w4_amd as w4
+from _util import assert_quant_equal, assert_within, quant_arrays_np, to_np32
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -57,8 +58,9 @@ def test_bench_step_sampled_rows_against_oracle():
 
 def test_full_80_layer_step_sampled_rows_against_oracle():
     # the headline workload at its full size: 80 fused layers (about 36 GB resident), M = 1,
-    # replayed from the captured graph exactly as the benchmark times it; 16 seeded rows of
-    # every matrix of every layer against the oracle, and two replays bit-identical
+    # replayed from the captured graph exactly as the benchmark times it; 512 seeded rows of
+    # every matrix of every layer against the oracle (codes and products), and two replays
+    # bit-identical
     layers = 80
     prepared = bench.build_stack(layers, DEV, fused=True)
     step = bench.make_step(prepared, layers, 1, DEV, fused=True)
@@ -78,12 +80,19 @@ def test_full_80_layer_step_sampled_rows_against_oracle():
         layer, j = divmod(i, len(order))
         name = order[j]
         n, k = shapes[name]
-        rows = np.unique(np.concatenate([[0, n - 1], rng.choice(n, 14, replace=False)]))
+        rows = np.unique(np.concatenate([[0, n - 1], rng.choice(np.arange(1, n - 1), 510, replace=False)]))
+        assert rows.size == 512
         seed = synth.seed_for(4, synth.FUSED_PARTS[name][0], layer) + 10000
         W = synth.normal_weights(n, k, seed, DEV)
         w32 = to_np32(W[torch.from_numpy(rows).to(DEV)])
         del W
         p, s, z = oracle.quantize_ref(w32)
+        # the codes the step reads: the prepared matrix taken back to the canonical arrays
+        gp, gs, gz = w4.w4_unprepare(prepared[(layer, name)], n, k)
+        sel = torch.from_numpy(rows).to(DEV)
+        assert_quant_equal(quant_arrays_np(gp[sel], gs[sel], gz[sel]), (p, s, z),
+                           f"80-layer step layer {layer} {name} codes")
+        del gp, gs, gz
         x32 = to_np32(call.x)
         r = assert_within(to_np32(call.y)[:, rows], oracle.gemv_ref(p, s, z, x32),
                           oracle.tolerance_ref(p, s, z, x32), f"80-layer step layer {layer} {name}")
@@ -95,7 +104,6 @@ def test_stream_read_probe_reads_without_writing():
     # the bandwidth probe leaves its sink alone unless the folded words equal its fixed
     # word; a zero buffer folds to 0, and a ragged size (not a multiple of the share)
     # must read in bounds
-    import dequant_gemv_w4_amd as w4
     sink = torch.full((1,), 7, dtype=torch.int32, device=DEV)
     for nbytes in (16, 4096 * 16 + 48, 3 << 20):
         buf = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)

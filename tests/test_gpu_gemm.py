@@ -1,4 +1,4 @@
-"""GPU parity of w4_gemm (bf16 MFMA with weights dequantized in LDS) against the oracle."""
+"""GPU parity of w4_gemm (binary16 MFMA on exact q - zero codes) against the oracle."""
 
 import numpy as np
 import pytest
@@ -7,7 +7,7 @@ import torch
 import dequant_gemv_w4_amd as w4
 import oracle
 import synth
-from _util import assert_within, to_np32
+from _util import assert_within, check_quant_and_oracle_products, to_np32
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -33,30 +33,31 @@ def test_small_full(m, n, k):
     print(f"worst err/bound {r:.3e}")
 
 
-def test_prefill_shape_sampled_outputs():
+def test_prefill_shape_rows_and_full_sub_gemm():
+    # the prefill shape (M 4096, K 8192, N 28672): every code bit-exact; 64 seeded rows of Y
+    # with all 28672 columns; and a full M = 256 product, every output
     W, X = synth.prefill_operands(device=DEV)
     n, k = W.shape
     m = X.shape[0]
-    prep = _prep(W)
+    p, s, z = w4.w4_quantize(W)
+    prep = w4.w4_prepare(p, s, z)
+    rng = np.random.default_rng(31)
+    mrows = np.unique(np.concatenate([[0, m - 1], rng.choice(np.arange(1, m - 1), 62, replace=False)]))
+    assert mrows.size == 64
+    x32 = to_np32(X[torch.from_numpy(mrows).to(DEV)])
+    x256 = to_np32(X[:256])
+    yr, bound = check_quant_and_oracle_products(W, p, s, z, np.concatenate([x32, x256]),
+                                                what="prefill W")
+    del W
     Y = w4.w4_gemm(prep, n, k, X)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(31)
-    mrows = np.unique(np.concatenate([[0, m - 1], rng.choice(m, 62, replace=False)]))
-    ncols = np.unique(np.concatenate([[0, n - 1], rng.choice(n, 510, replace=False)]))
-    p, s, z = oracle.quantize_ref(to_np32(W[torch.from_numpy(ncols).to(DEV)]))
-    x32 = to_np32(X[torch.from_numpy(mrows).to(DEV)])
-    yr = oracle.gemv_ref(p, s, z, x32)
-    bound = oracle.tolerance_ref(p, s, z, x32)
-    yg = to_np32(Y)[np.ix_(mrows, ncols)]
-    r = assert_within(yg, yr, bound, "prefill 4096x8192x28672 sampled")
-    print(f"worst err/bound {r:.3e}")
-    # a full 256-row block against 512 columns
-    cols = np.arange(512)
-    p, s, z = oracle.quantize_ref(to_np32(W[:512]))
-    x32 = to_np32(X[:256])
-    r = assert_within(to_np32(Y[:256, :512]), oracle.gemv_ref(p, s, z, x32),
-                      oracle.tolerance_ref(p, s, z, x32), "prefill 256x512 block")
-    del cols
+    r = assert_within(to_np32(Y)[mrows], yr[:64], bound[:64], "prefill 4096x8192x28672, 64 rows")
+    print(f"64 rows x all columns: worst err/bound {r:.3e}")
+    del Y
+    Y256 = w4.w4_gemm(prep, n, k, X[:256].contiguous())
+    torch.cuda.synchronize()
+    r = assert_within(to_np32(Y256), yr[64:], bound[64:], "prefill M=256 sub-GEMM")
+    print(f"M=256 sub-GEMM: worst err/bound {r:.3e}")
 
 
 def test_gemm_deterministic():
