@@ -31,12 +31,11 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
-# HBM bytes per launch of the batch-1 fused step, measured with rocprofv3 counters on the
-# current w4_gemv kernel: FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by what the
-# counter reads for a 256 MiB device copy (FETCH_SIZE x2, WRITE_SIZE x1); average of the four
-# launches of a layer (qkv, o, gate_up, down).  Source: the profile summary
-# profiles/w4_gemv_llama70b_fused_step_hbm_traffic.md
-GEMV_STEP_TRAFFIC_BYTES_PER_LAUNCH = 114039772
+# HBM bytes per launch of the batch-1 fused step from rocprofv3 counters on the current
+# w4_gemv kernel (FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by what the counter
+# reads for a 256 MiB device copy), or None while the kernel has changed since they were
+# taken.
+GEMV_STEP_TRAFFIC_BYTES_PER_LAUNCH = None
 BF16_DENSE_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 W8_DENSE_TOPS = 5000.0         # MI355X dense fp8 MFMA TFLOP/s, and int8 TOP/s
 METRIC = "W4A16 g128 GEMV achieved HBM GB/s (% of peak), 70B layer shapes, batch 1"
@@ -368,8 +367,25 @@ def prefill_gemm(prepared, dev: str, reps: int = 20, warmup: int = 10):
     end.synchronize()
     ms = start.elapsed_time(end) / reps
     tflops = 2.0 * m * n * k / (ms * 1e-3) / 1e12
+    # context on the same box: a dense bf16 product of the same shape through torch
+    # (hipBLASLt): what a library GEMM on uncompressed 16-bit weights reaches
+    Wt = torch.randn(k, n, device=dev, dtype=torch.float32).mul_(0.02).to(torch.bfloat16)
+    for _ in range(warmup):
+        Yd = torch.mm(X, Wt)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(reps):
+        Yd = torch.mm(X, Wt)
+    end.record()
+    end.synchronize()
+    ms_d = start.elapsed_time(end) / reps
+    del Wt, Yd
     return {"M": m, "N": n, "K": k, "ms": round(ms, 3), "TFLOP/s": round(tflops, 1),
-            "mfma_util_vs_2.5PF_dense_bf16": round(tflops / BF16_DENSE_TFLOPS, 4)}
+            "mfma_util_vs_2.5PF_dense_bf16": round(tflops / BF16_DENSE_TFLOPS, 4),
+            "dense_bf16_torch_matmul": {"ms": round(ms_d, 3),
+                                        "TFLOP/s": round(2.0 * m * n * k / (ms_d * 1e-3) / 1e12, 1),
+                                        "note": "torch.mm bf16 x bf16 -> bf16 (hipBLASLt), same "
+                                                "shape, uncompressed weights"}}
 
 
 def prefill_w8a8(dev: str, w4a16_ms: float | None, fmt: str = "fp8", reps: int = 20,
@@ -448,49 +464,100 @@ def quantizer_rate(dev: str, reps: int = 3):
     return {"N": n, "K": k, "ms": round(ms, 3), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1)}
 
 
+def _gemv_bytes(n: int, k: int, m: int, x_bytes: int) -> int:
+    """Algorithmic bytes of one product: codes, fp16 scales, byte zeros, x, fp32 y."""
+    return n * k // 2 + (n * k // 128) * 3 + m * k * x_bytes + m * n * 4
+
+
 def cpu_baseline():
-    """The oracle's dequantize-then-dot (fp64) on one 8192x8192 matrix at M=1, on host cores."""
+    """The oracle on the host cores, on a bounded sample of the workloads.
+
+    Each configuration runs the oracle as it stands -- quantize_ref (binary32 emulation),
+    then gemv_ref (fp64 dequantize-then-dot) -- on synthetic inputs drawn on the host:
+    the page's 4096x4096 layer (binary32 x), one 7B-shaped layer and one 70B-shaped layer
+    at M=1.  The 80-layer decode step is extrapolated as 80 x the 70B layer, and the
+    prefill GEMM from 64 sampled rows of X (x 4096/64); both are labelled as such.
+    ``value`` is the oracle's product rate on the 70B layer in the GPU metric's unit.
+    """
     import numpy as np
 
     import oracle
     import synth
 
-    n, k = 8192, 8192
-    W = synth.normal_weights(n, k, synth.seed_for(4, "o", 0), "cpu").numpy()
-    x = synth.normal_activations(1, k, 40002, "cpu").float().numpy()
-    p, s, z = oracle.quantize_ref(W)
-    # repetitions until about 10 s of host work
-    reps = 0
+    def run(mats):
+        tq = tg = 0.0
+        nbytes = 0
+        for W, x, x_bytes in mats():
+            t0 = time.perf_counter()
+            p, s, z = oracle.quantize_ref(W)
+            t1 = time.perf_counter()
+            oracle.gemv_ref(p, s, z, x)
+            t2 = time.perf_counter()
+            tq += t1 - t0
+            tg += t2 - t1
+            nbytes += _gemv_bytes(W.shape[0], W.shape[1], x.shape[0], x_bytes)
+            del W, x, p, s, z
+        return {"quantize_s": round(tq, 3), "gemv_s": round(tg, 3), "gemv_bytes": int(nbytes),
+                "gemv_GB/s": round(nbytes / tg / 1e9, 4)}
+
+    def page():
+        w, x = synth.page_single_layer(4096, 4096)
+        yield w, x, 4                      # binary32 x
+
+    def layer7b():
+        for name in synth.MATRIX_ORDER:
+            W, x = synth.llama7b_layer_matrix(name, device="cpu")
+            yield W.numpy(), x.float().numpy(), 2   # bf16 x
+
+    def layer70b():
+        for name in synth.MATRIX_ORDER:
+            W, x = synth.llama70b_layer_matrix(name, device="cpu")
+            yield W.numpy(), x.float().numpy(), 2
+
+    res = {"page_single_layer_m1": run(page)}
+    res["llama7b_layer_m1"] = run(layer7b)
+    res["llama70b_layer_m1"] = run(layer70b)
+    l70 = res["llama70b_layer_m1"]
+    res["decode_step_m1_extrapolated"] = {
+        "from": "80 x the 70B layer", "quantize_s": round(80 * l70["quantize_s"], 1),
+        "gemv_s": round(80 * l70["gemv_s"], 1)}
+    W, X = synth.prefill_operands(device="cpu")
+    rows = np.random.default_rng(31).choice(X.shape[0], 64, replace=False)
     t0 = time.perf_counter()
-    while reps < 3 or time.perf_counter() - t0 < 10.0:
-        oracle.gemv_ref(p, s, z, x)
-        reps += 1
-    dt = (time.perf_counter() - t0) / reps
-    nbytes = n * k // 2 + (n * k // 128) * 3 + k * 2 + n * 4
+    p, s, z = oracle.quantize_ref(W.numpy())
+    t1 = time.perf_counter()
+    oracle.gemv_ref(p, s, z, X[torch_index(rows)].float().numpy())
+    t2 = time.perf_counter()
+    res["prefill_gemm_extrapolated"] = {
+        "from": "64 sampled rows of X x 4096/64", "quantize_s": round(t1 - t0, 3),
+        "gemm_s": round((t2 - t1) * X.shape[0] / 64, 2),
+        "TFLOP/s": round(2.0 * X.shape[0] * W.shape[0] * W.shape[1] / ((t2 - t1) * X.shape[0] / 64) / 1e12, 5)}
+    del W, X, p, s, z
+
     threads = 1
     try:
         from threadpoolctl import threadpool_info
         threads = max([1] + [int(i.get("num_threads", 1)) for i in threadpool_info()])
     except Exception:
         pass
-    del np
     model = ""
     try:
         with open("/proc/cpuinfo") as f:
             model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
     except OSError:
         pass
-    rate = nbytes / dt
-    step_bytes = 80 * sum(synth.LLAMA70B_FUSED_SHAPES[m][0] * synth.LLAMA70B_FUSED_SHAPES[m][1] // 2
-                          + synth.LLAMA70B_FUSED_SHAPES[m][0] * synth.LLAMA70B_FUSED_SHAPES[m][1] // 128 * 3
-                          + synth.LLAMA70B_FUSED_SHAPES[m][1] * 2 + synth.LLAMA70B_FUSED_SHAPES[m][0] * 4
-                          for m in synth.FUSED_ORDER)
-    return {"value": round(rate / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"70B o_proj {n}x{k}, M=1: oracle fp64 dequantize-then-dot (gemv_ref), "
-                      f"{reps} repetitions, {dt:.2f} s each; quantization untimed",
-            "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": model,
-            "decode_step_s_extrapolated": round(step_bytes / rate, 1)}
+    return {"value": l70["gemv_GB/s"], "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "oracle quantize_ref + gemv_ref (fp64) on the 4096x4096 page layer, one "
+                      "7B-shaped and one 70B-shaped layer at M=1; value = gemv_ref rate on the "
+                      "70B layer's algorithmic bytes; decode step and prefill GEMM extrapolated",
+            "host_cpus": len(os.sched_getaffinity(0)), "blas_threads": threads,
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS"), "cpu_model": model,
+            "configs": res}
+
+
+def torch_index(rows):
+    import torch
+    return torch.from_numpy(rows)
 
 
 def main() -> int:
