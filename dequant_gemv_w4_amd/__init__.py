@@ -17,7 +17,7 @@ import re
 __all__ = [
     "W4Error", "lib", "declared_symbols",
     "w4_quantize", "w4_quantize_symmetric", "w4_prepared_bytes", "w4_prepare", "w4_unprepare",
-    "w4_gemv", "w4_gemm_workspace_bytes", "w4_gemm",
+    "w4_gemv", "w4_gemm_workspace_bytes", "w4_gemm", "w4_gemm_noalloc", "GEMM_NOALLOC_MAX_WORKSPACE",
     "w4_status_string", "w4_last_hip_error", "w4_format_version", "w4_stream_read",
     "w4_fp8_quantize_rows", "w4_fp8_gemm", "w4_int8_quantize_rows", "w4_int8_gemm",
     "W4Format", "w4_zeros_bytes", "w4_quantize_fmt", "w4_prepared_bytes_fmt", "w4_prepare_fmt",
@@ -33,6 +33,7 @@ GROUP = 128
 W4_OK = 0
 W4_F32 = 0
 W4_BF16 = 1
+GEMM_NOALLOC_MAX_WORKSPACE = 16 << 20
 STATUS_NONFINITE = 1
 STATUS_SCALE_OVERFLOW = 2
 STATUS_SCALE_ZERO = 4
@@ -89,6 +90,8 @@ def lib() -> ctypes.CDLL:
     L.w4_gemm_workspace_bytes.restype = sz
     L.w4_gemm.argtypes = [vp, i64, i64, vp, i64, vp, i32, vp, sz, vp]
     L.w4_gemm.restype = i32
+    L.w4_gemm_noalloc.argtypes = [vp, i64, i64, vp, i64, vp, i32, vp]
+    L.w4_gemm_noalloc.restype = i32
     L.w4_status_string.argtypes = [i32]
     L.w4_status_string.restype = ctypes.c_char_p
     L.w4_last_hip_error.argtypes = []
@@ -423,6 +426,24 @@ def w4_gemm(prepared, N: int, K: int, X, Y=None, out_dtype=None, workspace=None)
     yt = W4_F32 if Y.dtype == torch.float32 else W4_BF16
     _check(lib().w4_gemm(_ptr(prepared), N, K, _ptr(X), M, _ptr(Y), yt, ws_ptr, ws_len,
                          _stream(X)), "w4_gemm")
+    return Y
+
+
+def w4_gemm_noalloc(prepared, N: int, K: int, X, Y):
+    """w4_gemm into a caller's Y [M, N] with the library's own fixed device workspace.
+
+    The C call allocates nothing; calls that may overlap on one GPU race (they share
+    that GPU's workspace)."""
+    import torch
+    _require(prepared, torch.uint8, None, "prepared")
+    _require(X, torch.bfloat16, None, "X")
+    M = X.shape[0]
+    if X.shape[1] != K:
+        raise ValueError("X must be [M, K]")
+    _require(Y, (torch.float32, torch.bfloat16), (M, N), "Y")
+    yt = W4_F32 if Y.dtype == torch.float32 else W4_BF16
+    _check(lib().w4_gemm_noalloc(_ptr(prepared), N, K, _ptr(X), M, _ptr(Y), yt, _stream(X)),
+           "w4_gemm_noalloc")
     return Y
 
 

@@ -3,6 +3,7 @@
 // w4_w8a8.hip.
 #include <atomic>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -55,6 +56,39 @@ w4_status to_fmt(const w4_format* in, w4::Fmt* out) {
     out->scale_bf16 = in->scale_bf16 == 1;
     out->zero4 = in->zero_bits == 4;
     out->symmetric = in->symmetric == 1;
+    return W4_OK;
+}
+
+}  // namespace
+
+// Workspace of w4_gemm_noalloc.  In host code this name is only a stand-in for the
+// symbol: its device address (one per GPU) comes from hipGetSymbolAddress and is the
+// only form passed to kernels.
+static __device__ __align__(256) uint8_t scratch[W4_GEMM_NOALLOC_MAX_WORKSPACE];
+
+namespace {
+
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current device's scratch, looked up once per device.
+w4_status scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    if (dev < 0 || dev >= kMaxDevices) return W4_ERR_ARCH;
+    void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return hip_fail(e);
+            if (!p) return W4_ERR_WORKSPACE;
+            g_scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
     return W4_OK;
 }
 
@@ -280,6 +314,27 @@ w4_status w4_gemm(const void* prepared, int64_t N, int64_t K, const void* X, int
     if (st != W4_OK) return st;
     hipError_t e = w4::launch_gemm(static_cast<const uint8_t*>(prepared), N, K, X, M, Y,
                                    yt == W4_BF16, workspace, stream);
+    return e == hipSuccess ? W4_OK : hip_fail(e);
+}
+
+w4_status w4_gemm_noalloc(const void* prepared, int64_t N, int64_t K, const void* X, int64_t M,
+                          void* Y, w4_dtype yt, hipStream_t stream) {
+    if (!prepared || !X || !Y) return W4_ERR_NULL;
+    if (yt != W4_F32 && yt != W4_BF16) return W4_ERR_DTYPE;
+    w4_status st = check_nk(N, K);
+    if (st != W4_OK) return st;
+    if (M < 1 || (M + 127) / 128 > 65535) return W4_ERR_SHAPE;
+    if (((M + 127) / 128) * ((N + 255) / 256) > (int64_t)INT32_MAX - 8) return W4_ERR_SHAPE;
+    if (w4_gemm_workspace_bytes(M, N, K) > W4_GEMM_NOALLOC_MAX_WORKSPACE) return W4_ERR_WORKSPACE;
+    if (!aligned(prepared, 256) || !aligned(X, 16) || !aligned(Y, yt == W4_F32 ? 4 : 2))
+        return W4_ERR_ALIGN;
+    st = check_arch();
+    if (st != W4_OK) return st;
+    void* ws = nullptr;
+    st = scratch_address(&ws);
+    if (st != W4_OK) return st;
+    hipError_t e = w4::launch_gemm(static_cast<const uint8_t*>(prepared), N, K, X, M, Y,
+                                   yt == W4_BF16, ws, stream);
     return e == hipSuccess ? W4_OK : hip_fail(e);
 }
 

@@ -238,6 +238,26 @@ w4_status w4_gemm(const void* prepared, int64_t N, int64_t K,
                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * w4_gemm_noalloc -- w4_gemm for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * product, same kernels, bit-identical Y; the workspace is a fixed array of
+ * W4_GEMM_NOALLOC_MAX_WORKSPACE bytes in the library's device data, one copy per GPU,
+ * held until the process ends.  The call allocates nothing (no hipMalloc, no allocating
+ * library routine); its first call on a device looks up that device's copy once.
+ *   Arguments, alignment and limits as w4_gemm, and in addition
+ *   w4_gemm_workspace_bytes(M, N, K) <= W4_GEMM_NOALLOC_MAX_WORKSPACE, else
+ *   W4_ERR_WORKSPACE before any device work (about M * K <= 8.3e6: M = 256 at
+ *   K = 28672, M = 1024 at K = 8192).
+ * Every call on one GPU shares that GPU's array, which keeps the last call's contents
+ * (each call writes all it reads, nothing needs clearing): calls that may overlap on one
+ * GPU -- on different streams without ordering, or from several threads -- race and give
+ * undefined Y.  Order them on one stream, or use w4_gemm with workspaces of their own.
+ */
+#define W4_GEMM_NOALLOC_MAX_WORKSPACE (16u << 20)
+w4_status w4_gemm_noalloc(const void* prepared, int64_t N, int64_t K,
+                          const void* X, int64_t M, void* Y, w4_dtype yt, hipStream_t stream);
+
+/*
  * W8A8 in FP8 E4M3 for prefill (page "LLM Quantization Architecture in Depth" › "Why fewer
  * bits make decoding faster": prefill is compute bound, so its arithmetic must be narrower,
  * with activations quantized too; › "Number formats, scales and granularity": E4M3, largest

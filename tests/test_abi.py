@@ -70,6 +70,16 @@ def test_validation_errors_before_device_work():
     assert L.w4_gemm(_fake(), 2**31 - 1, 128, _fake(), 65535 * 128, _fake(), 0, _fake(), big, s) == 2
     assert L.w4_fp8_gemm(_fake(), _fake(), 2**31 - 1, _fake(), _fake(), 2**31 - 1, 128, _fake(), 0, s) == 2
     assert L.w4_int8_gemm(_fake(), _fake(), 2**31 - 1, _fake(), _fake(), 2**31 - 1, 128, _fake(), 0, s) == 2
+    # the fixed-workspace GEMM: validated like w4_gemm, and a workspace beyond its array
+    # (M = 300 at K = 28672 needs 300 * 28672 * 2 bytes > 16 MiB) refused before device work
+    assert L.w4_gemm_noalloc(_fake(), 4, 128, NULL, 1, _fake(), 0, s) == 1
+    assert L.w4_gemm_noalloc(_fake(), 4, 128, _fake(), 1, _fake(), 3, s) == 4
+    assert L.w4_gemm_noalloc(_fake(), 4, 192, _fake(), 4, _fake(), 0, s) == 2
+    assert L.w4_gemm_noalloc(_fake(), 4, 128, _fake(), 0, _fake(), 0, s) == 2
+    assert w4.w4_gemm_workspace_bytes(300, 4, 28672) > w4.GEMM_NOALLOC_MAX_WORKSPACE
+    assert L.w4_gemm_noalloc(_fake(), 4, 28672, _fake(), 300, _fake(), 0, s) == 7
+    assert w4.w4_gemm_workspace_bytes(256, 4, 28672) <= w4.GEMM_NOALLOC_MAX_WORKSPACE
+    assert L.w4_gemm_noalloc(_fake(0x100010), 4, 28672, _fake(), 256, _fake(), 0, s) == 3
     # alignment
     assert L.w4_quantize(_fake(0x100004), 0, 4, 128, _fake(), _fake(), _fake(), NULL, s) == 3
     assert L.w4_gemv(_fake(0x100010), 4, 128, _fake(), 1, 1, _fake(), 0, s) == 3
