@@ -108,7 +108,8 @@ def test_bf16_output():
     p, s, z = oracle.quantize_ref(w)
     x32 = to_np32(X)
     yr = oracle.gemv_ref(p, s, z, x32)
-    # the bf16 store adds at most half an ulp of bf16 (2^-9 relative)
+    # the bf16 store adds at most half an ulp of bf16: 8 significant bits, so at most
+    # 2^-8 of the value (at the bottom of a binade)
     assert_within(to_np32(Y), yr, oracle.tolerance_ref(p, s, z, x32), "bf16 Y",
                   extra=np.abs(yr) * 2.0 ** -8)
 

@@ -150,7 +150,8 @@ def test_bf16_output():
     y = _run(prep, n, k, x.to(DEV), out_dtype=torch.bfloat16)
     assert y.dtype == torch.bfloat16
     yr, bound, _ = _ref_from_oracle(w, to_np32(x))
-    # the bf16 store adds at most half an ulp of bf16 (2^-9 relative)
+    # the bf16 store adds at most half an ulp of bf16: 8 significant bits, so at most
+    # 2^-8 of the value (at the bottom of a binade)
     assert_within(to_np32(y), yr, bound, "bf16 y", extra=np.abs(yr) * 2.0 ** -8)
 
 
