@@ -40,7 +40,8 @@
 //   * a workgroup holds ceil(K/2048) waves and walks rows_per_wg rows in steps of four
 //     rows through two register buffers: the loads of the next step are issued before a
 //     step is computed (scheduling barriers keep them in order, so the compiler's in-order
-//     wait counts stay exact and a step waits only for its own loads);
+//     wait counts stay exact and a step waits only for its own loads).  The first step's
+//     loads follow x's directly, so they are in flight while x is converted;
 //   * groups of up to eight waves end the launch with a round of workgroups that take
 //     half the rows of the others, which shortens the tail of the weight stream;
 //   * the scale/zero words of the four rows of a step are one 16-byte load; two
@@ -63,7 +64,6 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kRowsPerStep = 4;
 constexpr int kChunk = 2;  // steps of four rows in registers at a time (two buffers)
-constexpr bool kPipelined = true;   // measured on MI355X: 0.5-1 us faster on gate_up and down
 
 // one 16-byte weight slice, marked non-temporal: every byte is read exactly once
 __device__ __forceinline__ u32x4_t load_stream(const u32x4_t* p) { return __builtin_nontemporal_load(p); }
@@ -187,28 +187,6 @@ __global__ __launch_bounds__(MAXT) void gemv_kernel(const u32x4_t* __restrict__ 
     const char* sbase = reinterpret_cast<const char*>(sz4);
     const int64_t row_bytes = (int64_t)S * 16;
 
-    // ---- x slices first: their loads complete before the weight stream that follows
-    uint32_t xb[SPT][MT][16];   // bf16 pairs (binary32 x is read by the exact path itself)
-    if constexpr (!XF32) {
-#pragma unroll
-        for (int j = 0; j < SPT; ++j)
-#pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                const bool ok = act[j] && (MT == 1 || m < M);  // zero x for idle lanes and absent rows
-                const uint4* px = reinterpret_cast<const uint4*>(
-                    static_cast<const uint16_t*>(xv) + (int64_t)m * K + (int64_t)sl[j] * 32);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint4 v = ok ? px[q] : make_uint4(0, 0, 0, 0);
-                    xb[j][m][4 * q + 0] = v.x;
-                    xb[j][m][4 * q + 1] = v.y;
-                    xb[j][m][4 * q + 2] = v.z;
-                    xb[j][m][4 * q + 3] = v.w;
-                }
-            }
-    }
-    __builtin_amdgcn_sched_barrier(0);  // keep the x loads ahead of the weight stream
-
     // rows_per_wg is a multiple of CH*4: every chunk is whole; rows past N repeat row N-1
     // (their sums are never stored)
     u32x4_t wb[CH][R][SPT];
@@ -231,6 +209,33 @@ __global__ __launch_bounds__(MAXT) void gemv_kernel(const u32x4_t* __restrict__ 
         // loads stay in step order, so a step only waits for its own loads
         __builtin_amdgcn_sched_barrier(0);
     };
+
+    // ---- x slices first: their loads complete before the weight stream that follows
+    uint32_t xb[SPT][MT][16];   // bf16 pairs (binary32 x is read by the exact path itself)
+    if constexpr (!XF32) {
+#pragma unroll
+        for (int j = 0; j < SPT; ++j)
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                const bool ok = act[j] && (MT == 1 || m < M);  // zero x for idle lanes and absent rows
+                const uint4* px = reinterpret_cast<const uint4*>(
+                    static_cast<const uint16_t*>(xv) + (int64_t)m * K + (int64_t)sl[j] * 32);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint4 v = ok ? px[q] : make_uint4(0, 0, 0, 0);
+                    xb[j][m][4 * q + 0] = v.x;
+                    xb[j][m][4 * q + 1] = v.y;
+                    xb[j][m][4 * q + 2] = v.z;
+                    xb[j][m][4 * q + 3] = v.w;
+                }
+            }
+    }
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+    __builtin_amdgcn_sched_barrier(0);  // x loads first: waiting for x never waits for weights
+    // the first step's weight loads go out right behind x, so their latency overlaps the
+    // conversion of x (they are not used if the exact path runs)
+    issue_step(B0{}, 0);
 
     // binary32 x for the exact path, resident
     uint32_t xs[XF32 ? SPT : 1][XF32 ? MT : 1][32];
@@ -433,14 +438,11 @@ __global__ __launch_bounds__(MAXT) void gemv_kernel(const u32x4_t* __restrict__ 
         }
     };
 
-    using B0 = std::integral_constant<int, 0>;
-    using B1 = std::integral_constant<int, 1>;
     if (!XF32 && exact) {
         run_exact_bf16();
-    } else if constexpr (kPipelined) {
+    } else {
         // two buffers of one step: the next step's loads are in flight while a step is
         // computed (rows_per_wg is a multiple of 8)
-        issue_step(B0{}, 0);
         int rb = 0;
         for (; rb + 2 * R < rows_per_wg; rb += 2 * R) {
             issue_step(B1{}, rb + R);
@@ -451,14 +453,6 @@ __global__ __launch_bounds__(MAXT) void gemv_kernel(const u32x4_t* __restrict__ 
         issue_step(B1{}, rb + R);
         compute_step(B0{}, rb);
         compute_step(B1{}, rb + R);
-    } else {
-        // chunks of two steps: all loads of a chunk are issued before any is used
-        for (int rb = 0; rb < rows_per_wg; rb += 2 * R) {
-            issue_step(B0{}, rb);
-            issue_step(B1{}, rb + R);
-            compute_step(B0{}, rb);
-            compute_step(B1{}, rb + R);
-        }
     }
     __syncthreads();
 
