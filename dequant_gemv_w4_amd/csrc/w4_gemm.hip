@@ -48,6 +48,7 @@ constexpr int GT = 512;                  // threads per workgroup
 constexpr int kXcds = 8;                 // accelerator complex dies of MI355X, each with its own L2
 constexpr int kGroupM = 8;               // M tiles per band of the XCD-aware tile order
 constexpr int kPrepThreads = 256;
+constexpr int kPrepKeep = 4;             // 16-byte chunks per thread kept between the passes
 
 __device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
     const uint32_t u = __float_as_uint(f);
@@ -80,8 +81,22 @@ __global__ __launch_bounds__(kPrepThreads) void xprep_kernel(const uint16_t* __r
     const int chunks = K / 8;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
+    // the first kPrepKeep chunks of each thread stay in registers between the two passes
+    // (all of a row up to K = 8192); the rest is read again
+    uint4 keep[kPrepKeep];
     uint32_t ef = 1;  // an all-zero or subnormal row uses the smallest normal exponent
-    for (int c = threadIdx.x; c < chunks; c += kPrepThreads) {
+#pragma unroll
+    for (int j = 0; j < kPrepKeep; ++j) {
+        const int c = threadIdx.x + j * kPrepThreads;
+        keep[j] = c < chunks ? row[c] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < kPrepKeep; ++j) {
+        const uint32_t w[4] = {keep[j].x, keep[j].y, keep[j].z, keep[j].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ef = max(ef, max((w[i] >> 7) & 0xFFu, (w[i] >> 23) & 0xFFu));
+    }
+    for (int c = threadIdx.x + kPrepKeep * kPrepThreads; c < chunks; c += kPrepThreads) {
         const uint4 v = row[c];
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -96,8 +111,8 @@ __global__ __launch_bounds__(kPrepThreads) void xprep_kernel(const uint16_t* __r
     const int e = (int)ef - 127 - 15;  // the row's largest value lands in [2^15, 2^16)
 
     bool b = false;
-    for (int c = threadIdx.x; c < chunks; c += kPrepThreads) {
-        const uint4 v = row[c];
+    for (int c = threadIdx.x, j = 0; c < chunks; c += kPrepThreads, ++j) {
+        const uint4 v = j < kPrepKeep ? keep[min(j, kPrepKeep - 1)] : row[c];
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
         uint32_t h[4];
 #pragma unroll
@@ -345,6 +360,10 @@ __global__ __launch_bounds__(256) void fixup_kernel(const uint8_t* __restrict__ 
     const int Kg = K / kGroup;
     const int S = K / 32;                 // 16-byte slices per row
     const int64_t row_bytes = K / 2;
+    // the common case, no marked row: all threads scan the flags at once and leave
+    bool any = false;
+    for (int i = threadIdx.x; i < M; i += blockDim.x) any |= bad[i] != 0;
+    if (!__syncthreads_or(any ? 1 : 0)) return;
     for (int mb = 0; mb < M; mb += 64) {
         const int mi = mb + lane;
         uint64_t marked = __builtin_amdgcn_ballot_w64(mi < M && bad[mi] != 0);

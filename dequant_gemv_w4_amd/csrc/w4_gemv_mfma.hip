@@ -103,6 +103,39 @@ __device__ __forceinline__ u32x4_t exact_codes(uint32_t w, uint32_t z1, uint32_t
     return r;
 }
 
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+typedef __attribute__((ext_vector_type(2))) unsigned short u16x2_t;
+
+__device__ __forceinline__ f16x8_t as_f16x8(u32x4_t v) { return __builtin_bit_cast(f16x8_t, v); }
+
+// The eight codes of a prepared word as the exact binary16 values q - zero (inputs 0, 1, 4,
+// 5) and 16 (q - zero) (inputs 2, 3, 6, 7), in input order.
+__device__ __forceinline__ u32x4_t exact_codes_f16(uint32_t w, uint32_t z1, uint32_t z16, const CodeConsts& c) {
+    const uint32_t u = w >> 8;
+    const u32x4_t r = {add2h((w & c.m_lo) | c.magic, z1), add2h((w & c.m_hi) | c.magic, z16),
+                       add2h((u & c.m_lo) | c.magic, z1), add2h((u & c.m_hi) | c.magic, z16)};
+    return r;
+}
+
+__device__ __forceinline__ u16x2_t as_u16x2(uint32_t v) { return __builtin_bit_cast(u16x2_t, v); }
+
+// bf16 pair -> binary16 pair of x * 2^-E by integer steps (c2 = (F_max - 30) << 7 in both
+// halves, or (F_max - 26) << 7 for a further 2^-4): exact whenever the result is a normal
+// binary16 value, which the caller's range check guarantees; a zero stays zero.
+__device__ __forceinline__ uint32_t to_f16_pair(uint32_t xb, uint32_t c2) {
+    const u16x2_t mag = as_u16x2(xb & 0x7FFF7FFFu);
+    const u16x2_t r = __builtin_elementwise_sub_sat(mag, as_u16x2(c2)) << (unsigned short)3;
+    return __builtin_bit_cast(uint32_t, r) | (xb & 0x80008000u);
+}
+
+__device__ __forceinline__ uint32_t max_across_rows(uint32_t v) {
+    // maximum over the four lanes l % 16 + 16 j (j = 0..3)
+    const auto h = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    const uint32_t a = max((uint32_t)h[0], (uint32_t)h[1]);
+    const auto q = __builtin_amdgcn_permlane16_swap(a, a, false, false);
+    return max((uint32_t)q[0], (uint32_t)q[1]);
+}
+
 __device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
     const uint32_t u = __float_as_uint(f);
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
@@ -289,8 +322,8 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(const uint8_t* __restric
 }
 
 // Variant for K <= 8192 (at most eight groups per wave, at most eight waves).
-//   * Each wave keeps the A operands of its groups (x, four MFMA steps per group) and their
-//     group sums in registers, then walks all rows of the workgroup in steps of 16.  The A
+//   * Each wave keeps the A operands of its groups (x, four MFMA steps per group) in
+//     registers, then walks all rows of the workgroup in steps of 16.  The A
 //     operands arrive through the wave's ring before the weights do, in two rounds of four
 //     groups, with loads of 4 rows x 256 contiguous bytes.
 //   * Weights and scale/zero words go straight from global memory into a ring in LDS that
@@ -372,6 +405,8 @@ __device__ __forceinline__ void bcast_rows(uint32_t v, uint32_t (&b)[4]) {
     b[3] = (uint32_t)hi[1];
 }
 
+// TRY_F16: convert x to binary16 where it converts exactly (workgroups with enough row steps)
+template <bool TRY_F16>
 __global__ __launch_bounds__(512) void gemv_mfma_xr_kernel(const uint8_t* __restrict__ wq,
                                                          const uint32_t* __restrict__ sz,
                                                          const uint16_t* __restrict__ x,
@@ -452,6 +487,63 @@ __global__ __launch_bounds__(512) void gemv_mfma_xr_kernel(const uint8_t* __rest
     }
     issue_step(0);
 
+    // binary16 x (TRY_F16, on workgroups with enough row steps to pay for the conversion):
+    // x * 2^-E per row of x, E putting the largest value of the row over this
+    // wave's groups just under 2^16; exact when every non-zero value lands on a normal
+    // binary16 (within 2^25 of the largest, also after the further 2^-4 at the inputs of the
+    // 16 (q - zero) codes).  The codes then need no bf16 conversion.  A wave whose rows do
+    // not all pass keeps bf16 x.
+    bool f16 = false;
+    int ev[4] = {0, 0, 0, 0};   // E of the rows 4 kb + v this lane accumulates
+    if constexpr (TRY_F16) {
+        u16x2_t vmax = {0, 0}, vmin = {0xFFFF, 0xFFFF};
+        // (scheduling barriers per group keep the compiler from spreading the work over many
+        // temporaries beside the 128 registers of x)
+#pragma unroll
+        for (int j = 0; j < kXrGroups; ++j) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const u16x2_t mag = as_u16x2(xa[j][s][d] & 0x7FFF7FFFu);
+                    vmax = __builtin_elementwise_max(vmax, mag);
+                    vmin = __builtin_elementwise_min(vmin, mag - (unsigned short)1);  // 0 -> 0xFFFF
+                }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        const int fmax = (int)(max_across_rows(max(vmax.x, vmax.y)) >> 7);
+        const int mnz = 0xFFFF - (int)max_across_rows(0xFFFFu - min(vmin.x, vmin.y)) + 1;
+        const bool bad = mnz != 0x10000 && (fmax < 30 || fmax == 255 || mnz < ((fmax - 25) << 7));
+        f16 = __builtin_amdgcn_ballot_w64(bad) == 0;
+        if (f16) {
+            // x passes through an empty asm statement so that the conversion recomputes the
+            // magnitudes instead of keeping the 128 from the range check alive
+#pragma unroll
+            for (int j = 0; j < kXrGroups; ++j)
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        uint32_t v = xa[j][s][d];
+                        asm volatile("" : "+v"(v));
+                        xa[j][s][d] = v;
+                    }
+            const uint32_t ce = (uint32_t)((fmax - 30) << 7) * 0x00010001u;
+            const uint32_t co = (uint32_t)((fmax - 26) << 7) * 0x00010001u;
+#pragma unroll
+            for (int j = 0; j < kXrGroups; ++j) {
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) xa[j][s][d] = to_f16_pair(xa[j][s][d], (d & 1) ? co : ce);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            const int e = fmax - 127 - 15;   // of row col
+#pragma unroll
+            for (int v = 0; v < 4; ++v) ev[v] = __shfl(e, 4 * kb + v);
+        }
+    }
+
     for (int t = 0; t < steps; ++t) {
         const bool more = t + 1 < steps;
         if (more) issue_step(t + 1);
@@ -470,11 +562,19 @@ __global__ __launch_bounds__(512) void gemv_mfma_xr_kernel(const uint8_t* __rest
             const uint32_t word = szw[j % 4];
             const uint32_t z1 = cc.z1(word), z16 = cc.z16(word);
             f32x4_t p = zero4;
+            if (TRY_F16 && f16) {
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
-                p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[j][s]),
-                                                            as_bf16x8(exact_codes(w4[s], z1, z16, cc)), p,
-                                                            0, 0, 0);
+                for (int s = 0; s < 4; ++s)
+                    p = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(xa[j][s]),
+                                                               as_f16x8(exact_codes_f16(w4[s], z1, z16, cc)),
+                                                               p, 0, 0, 0);
+            } else {
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[j][s]),
+                                                                as_bf16x8(exact_codes(w4[s], z1, z16, cc)),
+                                                                p, 0, 0, 0);
+            }
             // a group past the wave's range is computed with scale 0 (no branch)
             const float keep = j < ng ? 1.0f : 0.0f;
             const float sc = keep * (float)__builtin_bit_cast(_Float16, (uint16_t)(word & 0xFFFFu));
@@ -486,7 +586,7 @@ __global__ __launch_bounds__(512) void gemv_mfma_xr_kernel(const uint8_t* __rest
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const int m = 4 * kb + v;
-            if (m < M) rb[col * kRedStride + m] = acc[v];
+            if (m < M) rb[col * kRedStride + m] = ldexpf(acc[v], ev[v]);   // ev = 0 for bf16 x
         }
         lds_barrier();
         for (int i = tid; i < 16 * M; i += blockDim.x) {
@@ -565,16 +665,24 @@ static hipError_t launch_xr(const uint8_t* wq, const uint32_t* sz, const uint16_
     if (shmem > 65536) {
         static std::atomic<int> raised{0};
         if (!raised.load(std::memory_order_relaxed)) {
-            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_mfma_xr_kernel),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               (int)(8 * (kXrWaveRing + kXrRedBytes)));
-            if (e != hipSuccess) return e;
+            for (const void* f : {reinterpret_cast<const void*>(gemv_mfma_xr_kernel<false>),
+                                  reinterpret_cast<const void*>(gemv_mfma_xr_kernel<true>)}) {
+                hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                   (int)(8 * (kXrWaveRing + kXrRedBytes)));
+                if (e != hipSuccess) return e;
+            }
             raised.store(1, std::memory_order_relaxed);
         }
     }
     const dim3 grid((unsigned)((n + R - 1) / R));
-    hipLaunchKernelGGL(gemv_mfma_xr_kernel, grid, dim3((unsigned)(64 * waves)), shmem, s, wq, sz,
-                       x, y, yb, n, k, m, gpw, R);
+    const dim3 block((unsigned)(64 * waves));
+    // binary16 x costs about 1000 vector instructions per lane and workgroup and saves 256 per
+    // row step: taken from six row steps on (measured on MI355X: gate|up 57344 x 8192 at
+    // M = 4, 8, 16 in 58.5-61.1 us against 63.3-63.9 with bf16 x)
+    if (R / 16 >= 6)
+        hipLaunchKernelGGL(gemv_mfma_xr_kernel<true>, grid, block, shmem, s, wq, sz, x, y, yb, n, k, m, gpw, R);
+    else
+        hipLaunchKernelGGL(gemv_mfma_xr_kernel<false>, grid, block, shmem, s, wq, sz, x, y, yb, n, k, m, gpw, R);
     return hipGetLastError();
 }
 

@@ -29,8 +29,11 @@ DEV = "cuda:0"
 
 # (N, K) reaching each product kernel: the one-row kernel at M = 1..3 on every shape; for
 # bf16 x at larger M the streaming matrix-core kernel (few rows, or K > 64 groups) and the
-# ring kernel (K <= 64 groups, at least 48 rows per workgroup over 256 compute units)
-SHAPES = {"small": (300, 1024), "ring": (12288, 1024), "stream": (520, 9216)}
+# ring kernel (K <= 64 groups, at least 48 rows per workgroup over 256 compute units), which
+# converts x to binary16 from six 16-row steps per workgroup on (24576 rows) and keeps bf16
+# x below that (12288 rows) or where a wave's x does not convert exactly
+SHAPES = {"small": (300, 1024), "ring": (12288, 1024), "ring_f16": (24576, 4096),
+          "stream": (520, 9216)}
 M_VALUES = (1, 2, 3, 4, 8, 16)
 
 
@@ -95,6 +98,27 @@ def test_wide_range_activations(shape):
     worst = max(worst, _check_gemm(prep, ref, n, k, torch.from_numpy(X).to(DEV).to(torch.bfloat16),
                                    f"{shape} GEMM M=150"))
     print(f"{shape}: worst err/bound {worst:.3e}")
+
+
+def test_ring_binary16_x_some_waves_fall_back():
+    """The ring kernel on 24576 x 4096 (four waves of eight groups, six row steps): x wide
+    only in the first 1024 inputs, so the first wave of every workgroup keeps bf16 x and the
+    other three convert it to binary16; every output against the oracle at M = 4, 8, 16."""
+    n, k = SHAPES["ring_f16"]
+    rng = np.random.default_rng(61)
+    w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
+    prep, ref = _quant_prepare(w)
+    x = rng.standard_normal((16, k)).astype(np.float32)
+    x[:, :1024] = synth.wide_range_activations(16, 1024, seed=62)
+    worst = 0.0
+    for m in (4, 8, 16):
+        xm = torch.from_numpy(x[:m]).to(DEV).to(torch.bfloat16).contiguous()
+        worst = max(worst, _check_gemv(prep, ref, n, k, xm, f"ring mixed M={m}"))
+        # only rows 0..m-1 matter: a wide row among ordinary ones
+        xm2 = torch.from_numpy(rng.standard_normal((m, k)).astype(np.float32)).to(torch.bfloat16)
+        xm2[m // 2] = torch.from_numpy(x[0]).to(torch.bfloat16)
+        worst = max(worst, _check_gemv(prep, ref, n, k, xm2.to(DEV).contiguous(), f"ring one wide row M={m}"))
+    print(f"ring mixed: worst err/bound {worst:.3e}")
 
 
 def test_zero_weights_and_exact_zero_rows():

@@ -72,10 +72,10 @@ def test_gemm_deterministic():
 
 
 def test_one_hot_rows_and_zero_weight_rows_exact():
-    """The group term is folded as scale16 * (P - (128 + zero) * S) with S from the same MFMA
-    steps as P (page "Weight quantization", section "How it works"), so a one-hot row of X
-    returns a dequantized weight column exactly, and weight rows that are all zero give
-    exactly 0 for any X."""
+    """The B operand is the exact q - zero of every code and the group term is scale16 * P
+    (page "Weight quantization", section "How it works"), so a one-hot row of X returns a
+    dequantized weight column exactly, and weight rows that are all zero give exactly 0 for
+    any X."""
     rng = np.random.default_rng(41)
     n, k, m = 300, 1024, 130
     w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
