@@ -19,14 +19,15 @@
 //     taken where they are, as (1024 + 16 q) - (1024 + 16 zero) = 16 (q - zero), and
 //     their activations carry a factor 2^-4 instead, so a word of eight codes needs one
 //     shift;
-//   * x (bf16) enters as binary16 x * 2^-E, with E chosen per lane slice (32 inputs) so
-//     that the largest value lands just under 2^16.  bf16 has 8 significant bits and
-//     binary16 11, so the conversion (integer steps on the bits) is exact for every value
-//     that lands on a normal binary16, i.e. within 2^25 of the slice's largest;
-//     v_dot2_f32_f16 then multiplies exactly and accumulates in f32, and the slice's share
-//     of the group term is ldexp(scale16, E) * D;
-//   * binary32 x, and a wave in which some slice has a bf16 value outside that window,
-//     take the exact path instead: the same exact codes, converted to binary32, times x
+//   * x (bf16) enters as binary16 x * 2^-E, with E chosen per wave (its 64 slices, 2048
+//     inputs) so that the largest value lands just under 2^16.  bf16 has 8 significant bits
+//     and binary16 11, so the conversion (integer steps on the bits) is exact for every
+//     value that lands on a normal binary16, i.e. within 2^25 of the wave's largest;
+//     v_dot2_f32_f16 then multiplies exactly and accumulates in f32, the group term is
+//     scale16 * D (one v_fma_mix_f32 takes the binary16 scale as it is), and the wave's row
+//     sums are scaled by 2^E before the waves are combined;
+//   * binary32 x, and a wave with a bf16 value outside that window, take the exact path
+//     instead: the same exact codes, converted to binary32, times x
 //     in binary32 with one FMA per input (for bf16 x, one row at a time in a loop of its
 //     own that reads x again, so that the rare path adds no registers to the fast one).
 // Either way a code equal to its zero contributes exactly 0, and the rounding error is
@@ -118,6 +119,24 @@ __device__ __forceinline__ void swap16(float& a, float& b) {
                                                     __builtin_bit_cast(uint32_t, b), false, false);
     a = __builtin_bit_cast(float, (uint32_t)r[0]);
     b = __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+
+// maximum over the 64 lanes of the wave, in every lane (permlane swaps, then DPP rotations)
+__device__ __forceinline__ int wave_max(int v) {
+    const auto h = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+    v = max((int)h[0], (int)h[1]);
+    const auto q = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+    v = max((int)q[0], (int)q[1]);
+    v = max(v, dpp_i<0x128>(v));  // row_ror:8
+    v = max(v, dpp_i<0x124>(v));  // row_ror:4
+    v = max(v, dpp_i<0x122>(v));  // row_ror:2
+    v = max(v, dpp_i<0x121>(v));  // row_ror:1
+    return v;
 }
 
 // four per-lane row values -> lane l holds the wave-wide sum of row (l >> 4) & 3
@@ -258,17 +277,23 @@ __global__ __launch_bounds__(MAXT) void gemv_kernel(const u32x4_t* __restrict__ 
             }
     }
 
-    // ---- binary16 activations and the per-slice exponents (fast path)
+    // ---- binary16 activations and the per-wave exponents (fast path): x * 2^-E puts the
+    // wave's largest value in [2^15, 2^16); every non-zero value must land on a normal
+    // binary16 (also after the further 2^-4 at pairs 1 and 3 of every word, which meet codes
+    // scaled by 16): within 2^25 of the largest.  Waves with tiny (below 2^-97) or
+    // non-finite values take the exact path; an all-zero wave converts to zeros.
     uint32_t xp[SPT][MT][16];
-    int xe[SPT][MT];
+    int xw[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) xw[m] = 0;
     bool exact = XF32;
     if constexpr (!XF32) {
         bool bad = false;
+        int fmx[SPT][MT], mz[SPT][MT];
 #pragma unroll
         for (int j = 0; j < SPT; ++j)
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
-                // largest magnitude and smallest non-zero magnitude of the slice (bf16 bits)
                 u16x2_t vmax = {0, 0}, vmin = {0xFFFF, 0xFFFF};
 #pragma unroll
                 for (int p = 0; p < 16; ++p) {
@@ -276,22 +301,25 @@ __global__ __launch_bounds__(MAXT) void gemv_kernel(const u32x4_t* __restrict__ 
                     vmax = __builtin_elementwise_max(vmax, mag);
                     vmin = __builtin_elementwise_min(vmin, mag - (unsigned short)1);  // 0 -> 0xFFFF
                 }
-                const int fmax = (int)(max(vmax.x, vmax.y) >> 7);               // bf16 exponent field
-                const int mnz = (int)min(vmin.x, vmin.y) + 1;                   // 0x10000: all zero
-                // x * 2^-E puts the largest value in [2^15, 2^16); every non-zero value of the
-                // slice must land on a normal binary16 (also after the further 2^-4): within
-                // 2^25 of the largest.  Slices of tiny (below 2^-97) or non-finite values take
-                // the exact path; an all-zero slice converts to zeros whatever E is.
-                const int e = fmax - 127 - 15;
-                bad |= mnz != 0x10000 && (fmax < 30 || fmax == 255 || mnz < ((fmax - 25) << 7));
-                xe[j][m] = e;
-                const uint32_t ce = (uint32_t)((fmax - 30) << 7) * 0x00010001u;
-                const uint32_t co = (uint32_t)((fmax - 26) << 7) * 0x00010001u;
-#pragma unroll
-                for (int p = 0; p < 16; ++p)
-                    // pairs 1 and 3 of every word meet codes scaled by 16 (see the header)
-                    xp[j][m][p] = to_f16_pair(xb[j][m][p], (p & 1) ? co : ce);
+                fmx[j][m] = (int)(max(vmax.x, vmax.y) >> 7);
+                mz[j][m] = (int)min(vmin.x, vmin.y) + 1;
             }
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            int fw = fmx[0][m];
+#pragma unroll
+            for (int j = 1; j < SPT; ++j) fw = max(fw, fmx[j][m]);
+            fw = wave_max(fw);
+            xw[m] = fw - 127 - 15;
+            const uint32_t ce = (uint32_t)((fw - 30) << 7) * 0x00010001u;
+            const uint32_t co = (uint32_t)((fw - 26) << 7) * 0x00010001u;
+#pragma unroll
+            for (int j = 0; j < SPT; ++j) {
+                bad |= mz[j][m] != 0x10000 && (fw < 30 || fw == 255 || mz[j][m] < ((fw - 25) << 7));
+#pragma unroll
+                for (int p = 0; p < 16; ++p) xp[j][m][p] = to_f16_pair(xb[j][m][p], (p & 1) ? co : ce);
+            }
+        }
         exact = __builtin_amdgcn_ballot_w64(bad) != 0;
     }
 
@@ -339,10 +367,12 @@ __global__ __launch_bounds__(MAXT) void gemv_kernel(const u32x4_t* __restrict__ 
                     unpack_codes(wb[c][rr][j], szw, pr);
 #pragma unroll
                     for (int m = 0; m < MT; ++m) {
-                        float d = 0.0f;
+                        // the chain starts with the three-operand form and a zero accumulator
+                        float d;
+                        asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(d) : "v"(pr[0]), "v"(xp[j][m][0]));
 #pragma unroll
-                        for (int i = 0; i < 16; ++i) d = dot2h(pr[i], xp[j][m][i], d);
-                        acc[rr][m] = fmaf(ldexpf(s, xe[j][m]), d, acc[rr][m]);
+                        for (int i = 1; i < 16; ++i) d = dot2h(pr[i], xp[j][m][i], d);
+                        acc[rr][m] = fmaf(s, d, acc[rr][m]);
                     }
                 }
         } else {
@@ -372,7 +402,7 @@ __global__ __launch_bounds__(MAXT) void gemv_kernel(const u32x4_t* __restrict__ 
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
             const float k = reduce4(acc[0][m], acc[1][m], acc[2][m], acc[3][m]);
-            if ((lane & 15) == 0) red[(wave * row_stride + rb + (lane >> 4)) * MT + m] = k;
+            if ((lane & 15) == 0) red[(wave * row_stride + rb + (lane >> 4)) * MT + m] = ldexpf(k, xw[m]);
         }
     };
 
