@@ -55,6 +55,8 @@ def parse_args():
     ap.add_argument("--skip-extras", action="store_true",
                     help="only the headline step (no batch sweep, per-shape, GEMM, quantizer)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only the W4A16 prefill GEMM leg, three timed calls (for profiler runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 256 MiB device-to-device copy (a known-size kernel that "
                          "scales the byte counters of a profiler run)")
@@ -575,6 +577,10 @@ def main() -> int:
     dev = "cuda:0"
     torch.cuda.set_device(0)
     w4.lib()
+    if args.prefill_only:
+        unfused = build_stack(1, dev, fused=False)
+        print(json.dumps({"prefill_gemm": prefill_gemm(unfused, dev, reps=3, warmup=2)}), flush=True)
+        return 0
     log(f"device {torch.cuda.get_device_name(0)}; building {args.layers} fused layers")
     prepared = build_stack(args.layers, dev, fused=True)
 
