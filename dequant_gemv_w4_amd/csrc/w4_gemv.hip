@@ -19,8 +19,9 @@
 //     taken where they are, as (1024 + 16 q) - (1024 + 16 zero) = 16 (q - zero), and
 //     their activations carry a factor 2^-4 instead, so a word of eight codes needs one
 //     shift;
-//   * x (bf16) enters as binary16 x * 2^-E, with E chosen per wave (its 64 slices, 2048
-//     inputs) so that the largest value lands just under 2^16.  bf16 has 8 significant bits
+//   * x (bf16) enters as binary16 x * 2^-E, with E chosen per wave and row of x (the
+//     wave's 2048 inputs, 4096 with two slices per lane) so that the largest value lands
+//     just under 2^16.  bf16 has 8 significant bits
 //     and binary16 11, so the conversion (integer steps on the bits) is exact for every
 //     value that lands on a normal binary16, i.e. within 2^25 of the wave's largest;
 //     v_dot2_f32_f16 then multiplies exactly and accumulates in f32, the group term is
