@@ -18,7 +18,8 @@
 // v_pk_add_f16 subtracts 1024 + zero (1024 + 16 zero) exactly, and two scaled conversions
 // (binary16 -> E4M3 -> bf16, exact for these small integers; the second one scales the
 // 16 (q - zero) values back by 2^-4) give bf16.  x enters unchanged as bf16, every product
-// is exact, and a code equal to its zero contributes exactly 0.
+// is exact, and a code equal to its zero contributes exactly 0.  (The ring kernel further
+// down takes binary16 x and the binary16 codes themselves where that pays.)
 //
 // Mapping (gfx950, wave64):
 //   * the waves of a workgroup split K: wave w takes groups [w*gpw, (w+1)*gpw);
@@ -340,6 +341,11 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(const uint8_t* __restric
 //     swaps give every lane of the column the words of all four groups.
 //   * Partial sums of the waves meet in LDS after every row step (double-buffered, one
 //     barrier per step).
+//   * With six or more row steps per workgroup (TRY_F16), a wave whose x converts exactly
+//     to binary16 with one power-of-two exponent per row of x (over the wave's groups)
+//     keeps binary16 x in its A operands and uses the exact binary16 codes with
+//     v_mfma_f32_16x16x32_f16: 9 instead of 17 vector instructions per eight codes, for
+//     about 1000 once per workgroup; its row sums are scaled by 2^E before the reduction.
 constexpr int kXrGroups = 8;                        // groups per wave
 constexpr int kXrSlotBytes = 1024;                  // one group of one 16-row tile
 constexpr int kXrSzBytes = 256;                     // one scale/zero word per lane
