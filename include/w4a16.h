@@ -131,10 +131,11 @@ w4_status w4_unprepare(const void* prepared, int64_t N, int64_t K,
  * "How it works": the per-group factored dot; architecture page stage "Fused
  * Kernels": dequantization inside the product).  Every product multiplies the exact
  * value q - zero of a code (a code equal to its zero adds exactly 0); bf16 x enters
- * the one-row kernel as binary16 x * 2^-E per 32-input slice (exact within 2^25 of the
- * slice's largest value; a wave with a slice outside that window, and binary32 x, use
- * one binary32 FMA per input instead) and the matrix-core kernels (2 <= M <= 16) as
- * bf16 with bf16 q - zero codes.
+ * the one-row kernel as binary16 x * 2^-E, E per wave of 2048 inputs (exact within 2^25
+ * of the wave's largest value; a wave with a value outside that window, and binary32 x,
+ * use one binary32 FMA per input instead), and the matrix-core kernels (2 <= M <= 16)
+ * as bf16 with bf16 q - zero codes, or, on workgroups with six or more 16-row steps, as
+ * binary16 x * 2^-E per row of x with binary16 codes where x converts exactly.
  *   prepared  from w4_prepare (256-B aligned).
  *   x         [M, K] row-major, bfloat16 (xt = W4_BF16) or binary32 (W4_F32); 16-B aligned.
  *   y         [M, N] row-major, binary32 (yt = W4_F32) or bfloat16 (W4_BF16); must
@@ -217,7 +218,7 @@ w4_status w4_gemv_fmt(const void* prepared, int64_t N, int64_t K, const w4_forma
  * decoding faster": prefill is compute bound and weight-only formats must turn
  * weights back into 16-bit values before the matrix units).  The codes enter the
  * binary16 MFMA as the exact values q - zero and X as binary16 X * 2^-E[m] (E per
- * row, exact for every value within 2^25 of the row's largest); per group the f32
+ * row, exact for every value within 2^28 of the row's largest); per group the f32
  * accumulator receives scale16 * P (page "Weight quantization", "How it works": the
  * dequantized weight (code - zero) * scale, one multiply per group), so no weight
  * and no activation is rounded.  Rows of X with a value outside that window are
