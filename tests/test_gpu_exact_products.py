@@ -121,6 +121,20 @@ def test_ring_binary16_x_some_waves_fall_back():
     print(f"ring mixed: worst err/bound {worst:.3e}")
 
 
+@pytest.mark.parametrize("m", [4, 5, 7, 13, 16])
+def test_ring_binary16_ragged_rows(m):
+    """The ring kernel's binary16 path with a ragged last workgroup (24616 rows: 220
+    workgroups of 112 rows, the last with 88, whose loads for the 24 missing rows repeat row
+    N-1) and M not a multiple of four; every output against the oracle."""
+    n, k = 24616, 4096
+    rng = np.random.default_rng(70 + m)
+    w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
+    prep, ref = _quant_prepare(w)
+    x = torch.from_numpy(rng.standard_normal((m, k)).astype(np.float32)).to(torch.bfloat16)
+    r = _check_gemv(prep, ref, n, k, x.to(DEV).contiguous(), f"ring ragged M={m}")
+    print(f"M={m}: worst err/bound {r:.3e}")
+
+
 def test_zero_weights_and_exact_zero_rows():
     """Rows of exact zeros (zero point 0) and groups of one repeated negative value give
     exact results whatever x is."""
