@@ -550,35 +550,48 @@ __global__ __launch_bounds__(512) void gemv_mfma_xr_kernel(const uint8_t* __rest
         }
     }
 
-    for (int t = 0; t < steps; ++t) {
-        const bool more = t + 1 < steps;
-        if (more) issue_step(t + 1);
+    // one row step; F: binary16 x and codes (else bf16), MORE: the next row step's loads are
+    // issued here.  Both are compile-time, so the group loop is straight-line code and the
+    // LDS reads of group j + 1 are issued before group j is computed.
+    auto row_step = [&](auto fc, auto mc, int t) {
+        constexpr bool F = decltype(fc)::value;
+        constexpr bool MORE = decltype(mc)::value;
+        if constexpr (MORE) issue_step(t + 1);
         const uint8_t* wslots = ring_p + (t & 1) * 8 * kXrSlotBytes;
         const uint8_t* sslots = ring_p + 16 * kXrSlotBytes + (t & 1) * 2 * kXrSzBytes;
+        auto codes_of = [&](int j) {
+            return *reinterpret_cast<const u32x4_t*>(
+                wslots + (2 * (j >> 1) + (col >> 3)) * kXrSlotBytes + 16 * (8 * (col & 7) + 4 * (j & 1) + kb));
+        };
         f32x4_t acc = zero4;
-        uint32_t szw[4];
+        uint32_t szw[2][4];
+        u32x4_t wcur, wnext;
+        wait_group(0, MORE);
+        bcast_rows(*reinterpret_cast<const uint32_t*>(sslots + 4 * lane), szw[0]);
+        wcur = codes_of(0);
 #pragma unroll
         for (int j = 0; j < kXrGroups; ++j) {
-            wait_group(j, more);
-            if (j % 4 == 0)
-                bcast_rows(*reinterpret_cast<const uint32_t*>(sslots + (j / 4) * kXrSzBytes + 4 * lane),
-                           szw);
-            const u32x4_t w4 = *reinterpret_cast<const u32x4_t*>(
-                wslots + (2 * (j >> 1) + (col >> 3)) * kXrSlotBytes + 16 * (8 * (col & 7) + 4 * (j & 1) + kb));
-            const uint32_t word = szw[j % 4];
+            if (j + 1 < kXrGroups) {
+                wait_group(j + 1, MORE);
+                if ((j + 1) % 4 == 0)
+                    bcast_rows(*reinterpret_cast<const uint32_t*>(sslots + ((j + 1) / 4) * kXrSzBytes + 4 * lane),
+                               szw[(j + 1) / 4]);
+                wnext = codes_of(j + 1);
+            }
+            const uint32_t word = szw[j / 4][j % 4];
             const uint32_t z1 = cc.z1(word), z16 = cc.z16(word);
             f32x4_t p = zero4;
-            if (TRY_F16 && f16) {
+            if constexpr (F) {
 #pragma unroll
                 for (int s = 0; s < 4; ++s)
                     p = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(xa[j][s]),
-                                                               as_f16x8(exact_codes_f16(w4[s], z1, z16, cc)),
+                                                               as_f16x8(exact_codes_f16(wcur[s], z1, z16, cc)),
                                                                p, 0, 0, 0);
             } else {
 #pragma unroll
                 for (int s = 0; s < 4; ++s)
                     p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[j][s]),
-                                                                as_bf16x8(exact_codes(w4[s], z1, z16, cc)),
+                                                                as_bf16x8(exact_codes(wcur[s], z1, z16, cc)),
                                                                 p, 0, 0, 0);
             }
             // a group past the wave's range is computed with scale 0 (no branch)
@@ -586,6 +599,7 @@ __global__ __launch_bounds__(512) void gemv_mfma_xr_kernel(const uint8_t* __rest
             const float sc = keep * (float)__builtin_bit_cast(_Float16, (uint16_t)(word & 0xFFFFu));
 #pragma unroll
             for (int v = 0; v < 4; ++v) acc[v] = fmaf(sc, p[v], acc[v]);
+            wcur = wnext;
         }
         // partial sums of this row step: lane holds column (row) col, rows m = 4 kb + v
         float* rb = red + ((t & 1) * n_waves + wave) * 16 * kRedStride;
@@ -610,7 +624,17 @@ __global__ __launch_bounds__(512) void gemv_mfma_xr_kernel(const uint8_t* __rest
                     static_cast<float*>(yv)[o] = v;
             }
         }
-    }
+    };
+    using True = std::integral_constant<bool, true>;
+    using False = std::integral_constant<bool, false>;
+    auto all_steps = [&](auto fc) {
+        for (int t = 0; t + 1 < steps; ++t) row_step(fc, True{}, t);
+        row_step(fc, False{}, steps - 1);
+    };
+    if (TRY_F16 && f16)
+        all_steps(std::integral_constant<bool, TRY_F16>{});
+    else
+        all_steps(False{});
 }
 
 template <int T>
