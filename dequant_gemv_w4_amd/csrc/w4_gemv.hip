@@ -163,7 +163,7 @@ __device__ __forceinline__ float word_scale(uint32_t szw) {
 
 // SBF16: the scale bits are bfloat16 (else binary16); gshift: log2(group / 32), the slices
 // of one group (a group of 32, 64 or 128 inputs has its own scale/zero word)
-template <int MT, bool XF32, int SPT, int MAXT, bool RAGGED, bool SBF16>
+template <int MT, bool XF32, int SPT, int MAXT, bool RAGGED, bool SBF16, bool ONE = false>
 __global__ __launch_bounds__(MAXT) void gemv_kernel(const u32x4_t* __restrict__ wq,
                                                     const u32x4_t* __restrict__ sz4,
                                                     const void* __restrict__ xv,
@@ -207,8 +207,8 @@ __global__ __launch_bounds__(MAXT) void gemv_kernel(const u32x4_t* __restrict__ 
     const char* sbase = reinterpret_cast<const char*>(sz4);
     const int64_t row_bytes = (int64_t)S * 16;
 
-    // rows_per_wg is a multiple of CH*4: every chunk is whole; rows past N repeat row N-1
-    // (their sums are never stored)
+    // rows_per_wg is a multiple of CH*4 (every chunk is whole), or four with ONE; rows past N
+    // repeat row N-1 (their sums are never stored)
     u32x4_t wb[CH][R][SPT];
     u32x4_t sb[CH][SPT];
     // loads of the step (four rows) at local row rb into buffer c: the scale/zero words of
@@ -471,6 +471,8 @@ __global__ __launch_bounds__(MAXT) void gemv_kernel(const u32x4_t* __restrict__ 
 
     if (!XF32 && exact) {
         run_exact_bf16();
+    } else if constexpr (ONE) {
+        compute_step(B0{}, 0);   // workgroups of one step (four rows)
     } else {
         // two buffers of one step: the next step's loads are in flight while a step is
         // computed (rows_per_wg is a multiple of 8)
@@ -551,12 +553,30 @@ int rows_for(Kern kernel, int block, int n, int mt, int chunk_rows, std::atomic<
     return rows;
 }
 
+// Small matrices that fill less than one round of resident groups at the smallest chunk take
+// workgroups of one step (four rows), twice the waves per CU, when those still fit in one
+// round (measured on MI355X: 4096 x 4096 at M = 1, 4.4 against 4.9 us)
+bool one_step_fits(int n, int rows, int chunk_rows, int resident) {
+    const long slots = (long)resident * compute_units();
+    return rows == chunk_rows && (n + rows - 1) / rows < slots && (n + kRowsPerStep - 1) / kRowsPerStep <= slots;
+}
+
 template <int MT, bool XF32, int SPT, int MAXT, bool RAGGED, bool SBF16>
 hipError_t launch_var(GemvArgs a, dim3 block, hipStream_t s) {
     constexpr int CR = kChunk * kRowsPerStep;
     static std::atomic<int> cache[17];
     auto kern = gemv_kernel<MT, XF32, SPT, MAXT, RAGGED, SBF16>;
     a.rows = rows_for(kern, (int)block.x, a.n, MT, CR, cache);
+    if constexpr (MT == 1 && !XF32 && SPT == 1) {
+        if (one_step_fits(a.n, a.rows, CR, cache[block.x / 64].load(std::memory_order_relaxed))) {
+            const dim3 grid((unsigned)((a.n + kRowsPerStep - 1) / kRowsPerStep));
+            const size_t shmem = (size_t)(block.x / 64) * kRowsPerStep * MT * sizeof(float);
+            hipLaunchKernelGGL((gemv_kernel<MT, XF32, SPT, MAXT, RAGGED, SBF16, true>), grid, block, shmem, s,
+                               a.wq, a.sz4, a.x, a.y, a.y_bf16, a.n, a.k, a.m, kRowsPerStep, a.gshift,
+                               (int)grid.x, kRowsPerStep);
+            return hipGetLastError();
+        }
+    }
     unsigned wgs = (unsigned)((a.n + a.rows - 1) / a.rows);
     // A short last round: the last round of resident workgroups takes half the rows.
     // Workgroups start in index order as earlier ones finish, so the final ones otherwise
