@@ -90,7 +90,9 @@ __device__ __forceinline__ u32x4_t exact_codes(uint32_t w, uint32_t z1, uint32_t
     const f16x2_t h1 = __builtin_bit_cast(f16x2_t, add2h((w & c.m_hi) | c.magic, z16));  // 2, 3 (x16)
     const f16x2_t h2 = __builtin_bit_cast(f16x2_t, add2h((u & c.m_lo) | c.magic, z1));   // 4, 5
     const f16x2_t h3 = __builtin_bit_cast(f16x2_t, add2h((u & c.m_hi) | c.magic, z16));  // 6, 7 (x16)
-    s16x2_t e01 = {0, 0}, e23 = {0, 0};
+    // the first conversion of each pair writes the low half of a register whose high half
+    // the second one writes: start from h0 / h2 themselves, so no zeroed register is needed
+    s16x2_t e01 = __builtin_bit_cast(s16x2_t, h0), e23 = __builtin_bit_cast(s16x2_t, h2);
     e01 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(e01, h0, 1.0f, false);
     e01 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(e01, h1, 1.0f, true);
     e23 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(e23, h2, 1.0f, false);
