@@ -145,6 +145,19 @@ __device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
 }
 
 __device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_addr);
+// the same load with a uniform base address in SGPRs and a per-lane 32-bit byte offset
+__device__ __forceinline__ void lds_dma16_sv(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(lds_addr)
+                 : "memory");
+}
+__device__ __forceinline__ void lds_dma4_sv(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(lds_addr)
+                 : "memory");
+}
 constexpr int kXStageBytes = 16 * 256;   // x of one group: 16 rows x 128 inputs (bf16)
 
 // T: tiles of 16 rows per workgroup; CH: groups whose loads are issued together (a pair)
@@ -163,7 +176,7 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(const uint8_t* __restric
     float* red = reinterpret_cast<float*>(smem);
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: SGPR addresses
     const int n_waves = blockDim.x >> 6;
     const int Kg = K >> 7;
     const int r0 = blockIdx.x * RW;
@@ -184,15 +197,19 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(const uint8_t* __restric
     // group h = ((l >> 2) & 1) ^ d of the pair and 16-byte piece p = (l & 3) ^ (l >> 4), so
     // that the reads in MFMA lane order below hit 16 distinct bank quads per 16 lanes.
     // Rows past N repeat row N-1 (never stored).
-    const uint8_t* csrc[T][2];
-    int chalf[2];
+    // Each lane's byte offset from group 0 of the workgroup's first row is fixed; the group
+    // pair moves a uniform base.  (In the last pair of a wave with an odd number of groups the
+    // lanes of group g + 1 read the next group: the next wave's, the next row's, or for the
+    // last row the first bytes of the scale/zero words; scale 0 drops it.)
+    const uint8_t* wrow0 = wq + (int64_t)r0 * row_bytes;
+    uint32_t coff[T][2];
 #pragma unroll
     for (int d = 0; d < 2; ++d) {
-        chalf[d] = ((lane >> 2) & 1) ^ d;
+        const int chalf = ((lane >> 2) & 1) ^ d;
 #pragma unroll
         for (int t = 0; t < T; ++t) {
             const int n = min(r0 + 16 * t + 8 * d + (lane >> 3), N - 1);
-            csrc[t][d] = wq + (int64_t)n * row_bytes + 16 * ((lane & 3) ^ (lane >> 4));
+            coff[t][d] = (uint32_t)((int64_t)(n - r0) * row_bytes) + 16 * ((lane & 3) ^ (lane >> 4)) + 64 * chalf;
         }
     }
     // scale/zero word of this lane's row (column col of the MFMA tile) in each tile
@@ -207,11 +224,11 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(const uint8_t* __restric
     // quads of rows are loaded: MFMA rows past them read stale stage bytes and give only
     // outputs m >= M, which are dropped.
     const int xquads = (M + 3) >> 2;
-    const uint16_t* xsrc[4];
+    uint32_t xoff[4];   // bytes from x
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = 4 * i + (lane >> 4);
-        xsrc[i] = x + (int64_t)min(r, M - 1) * K + 8 * ((lane & 15) ^ (r & 15));
+        xoff[i] = 2u * (uint32_t)(min(r, M - 1) * K + 8 * ((lane & 15) ^ (r & 15)));
     }
 
     const CodeConsts cc;
@@ -226,20 +243,20 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(const uint8_t* __restric
     // hit that contributes nothing): codes, scale/zero words, x
     auto issue = [&](auto bc, int g) {
         constexpr int b = decltype(bc)::value;
+        const uint8_t* cbase = wrow0 + (int64_t)g * 64;
 #pragma unroll
         for (int t = 0; t < T; ++t)
 #pragma unroll
-            for (int d = 0; d < 2; ++d)
-                lds_dma16(csrc[t][d] + (int64_t)min(g + chalf[d], g1 - 1) * 64,
-                          cstage + (2 * t + d) * 1024);
+            for (int d = 0; d < 2; ++d) lds_dma16_sv(cbase, coff[t][d], cstage + (2 * t + d) * 1024);
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             const int gc = min(g + c, g1 - 1);
 #pragma unroll
             for (int t = 0; t < T; ++t) sb[b][c][t] = szrow[t][gc * 4];
+            const uint8_t* xbase = reinterpret_cast<const uint8_t*>(x) + (int64_t)gc * 256;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                if (i < xquads) lds_dma16(xsrc[i] + gc * 128, xstage + c * kXStageBytes + i * 1024);
+                if (i < xquads) lds_dma16_sv(xbase, xoff[i], xstage + c * kXStageBytes + i * 1024);
         }
         __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the compute
     };
@@ -424,7 +441,7 @@ __global__ __launch_bounds__(512) void gemv_mfma_xr_kernel(const uint8_t* __rest
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: SGPR addresses
     const int n_waves = blockDim.x >> 6;
     const int Kg = K >> 7;
     const int r0 = blockIdx.x * R;
@@ -444,11 +461,32 @@ __global__ __launch_bounds__(512) void gemv_mfma_xr_kernel(const uint8_t* __rest
     const f32x4_t zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
 
     // loads of row step t into the ring half t & 1; rows past N repeat row N-1 (never stored)
+    // per-lane byte offsets of a row step's loads from its first row and the wave's first group
+    // (codes) and from that row quad's first scale/zero word (used when the step lies inside
+    // the matrix and the wave has all its groups; the base address is then uniform)
+    uint32_t coff[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+        coff[h] = (uint32_t)((8 * h + (lane >> 3)) * row_bytes) + 64 * ((lane >> 2) & 1) + 16 * (lane & 3);
+    const uint32_t szoff[2] = {4u * (uint32_t)((col >> 2) * Kg * 4 + (col & 3) + 4 * kb),
+                               4u * (uint32_t)((col >> 2) * Kg * 4 + (col & 3) + 4 * (4 + kb))};
     auto issue_step = [&](int t) {
-        const int n = min(r0 + 16 * t + col, N - 1);
-        const uint32_t* szrow = sz + (int64_t)(n >> 2) * Kg * 4 + (n & 3) + (int64_t)g0 * 4;
         const uint32_t wb = ring + (t & 1) * 8 * kXrSlotBytes;
         const uint32_t sb = ring + 16 * kXrSlotBytes + (t & 1) * 2 * kXrSzBytes;
+        if (r0 + 16 * t + 16 <= N && ng == kXrGroups) {
+            const uint8_t* cbase = wq + (int64_t)(r0 + 16 * t) * row_bytes + (int64_t)g0 * 64;
+            const uint8_t* sbase = reinterpret_cast<const uint8_t*>(sz) +
+                                   4 * ((int64_t)((r0 + 16 * t) >> 2) * Kg * 4 + (int64_t)g0 * 4);
+            lds_dma4_sv(sbase, szoff[0], sb);
+#pragma unroll
+            for (int d = 0; d < 4; ++d) lds_dma16_sv(cbase + 128 * (d >> 1), coff[d & 1], wb + d * kXrSlotBytes);
+            lds_dma4_sv(sbase, szoff[1], sb + kXrSzBytes);
+#pragma unroll
+            for (int d = 4; d < 8; ++d) lds_dma16_sv(cbase + 128 * (d >> 1), coff[d & 1], wb + d * kXrSlotBytes);
+            return;
+        }
+        const int n = min(r0 + 16 * t + col, N - 1);
+        const uint32_t* szrow = sz + (int64_t)(n >> 2) * Kg * 4 + (n & 3) + (int64_t)g0 * 4;
         // load d: lane reads 16 bytes at 16 (lane & 7) of the 128-byte span of groups
         // 2(d>>1), 2(d>>1)+1 in row 8(d&1) + (lane >> 3): eight full lines per load
         auto code_load = [&](int d) {
