@@ -156,6 +156,13 @@ __device__ __forceinline__ void load_lds16(const void* g, uint32_t lds_addr) {
                  : "v"(g), "s"(lds_addr)
                  : "memory", "m0");
 }
+// the same with a uniform base address in SGPRs and a 32-bit byte offset per lane
+__device__ __forceinline__ void load_lds16_sv(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(lds_addr)
+                 : "memory", "m0");
+}
 
 __global__ __launch_bounds__(GT) void gemm_kernel(const uint8_t* __restrict__ wq,
                                                   const uint32_t* __restrict__ sz,
@@ -190,23 +197,26 @@ __global__ __launch_bounds__(GT) void gemm_kernel(const uint8_t* __restrict__ wq
     const int l32 = lane & 31;
     const int n_quads = (N + 3) >> 2;
 
-    // ---- per-lane global addresses of the stage loads (group 0; a group adds a fixed step)
+    // ---- per-lane byte offsets of the stage loads from the tile's first row (X') or column
+    // (W) at group 0; the group moves a uniform base held in SGPRs
     // X': wave w fills rows 16w .. 16w+15 with four 1 KiB loads of four rows each
-    const uint16_t* xsrc[4];
+    uint32_t xoff[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int row = 16 * wave + 4 * i + (lane >> 4);
         const int c = (lane & 15) ^ (row & 15);
-        xsrc[i] = Xh + (int64_t)min(m0 + row, M - 1) * K + 8 * c;
+        xoff[i] = 2u * (uint32_t)((min(m0 + row, M - 1) - m0) * K + 8 * c);
     }
     // W: wave w fills columns 32w .. 32w+31 with two loads of sixteen columns
-    const uint8_t* wsrc[2];
+    uint32_t woff[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int col = 32 * wave + 16 * i + (lane >> 2);
         const int piece = (lane & 3) ^ ((col >> 2) & 3);
-        wsrc[i] = wq + (int64_t)min(n0 + col, N - 1) * row_bytes + 16 * piece;
+        woff[i] = (uint32_t)((int64_t)(min(n0 + col, N - 1) - n0) * row_bytes) + 16 * piece;
     }
+    const uint8_t* xtile = reinterpret_cast<const uint8_t*>(Xh) + (int64_t)m0 * K * 2;
+    const uint8_t* wtile = wq + (int64_t)n0 * row_bytes;
     // SZ (wave 0): lane = column quad
     const uint32_t* szsrc = sz + (int64_t)min((n0 >> 2) + lane, n_quads - 1) * Kg * 4;
 
@@ -216,11 +226,12 @@ __global__ __launch_bounds__(GT) void gemm_kernel(const uint8_t* __restrict__ wq
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     auto issue_stage = [&](int st, int kg) {
         const uint32_t base = ring_lds + st * kStageBytes;
+        const uint8_t* xg = xtile + (int64_t)kg * BK * 2;
+        const uint8_t* wg = wtile + (int64_t)kg * (BK / 2);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) load_lds16(xsrc[i] + kg * BK, base + (4 * wave_u + i) * 1024);
+        for (int i = 0; i < 4; ++i) load_lds16_sv(xg, xoff[i], base + (4 * wave_u + i) * 1024);
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-            load_lds16(wsrc[i] + kg * (BK / 2), base + kXBytes + (2 * wave_u + i) * 1024);
+        for (int i = 0; i < 2; ++i) load_lds16_sv(wg, woff[i], base + kXBytes + (2 * wave_u + i) * 1024);
         if (wave_u == 0) load_lds16(szsrc + kg * 4, base + kXBytes + kWBytes);
     };
 
