@@ -293,7 +293,7 @@ w4_status w4_gemv_fmt(const void* prepared, int64_t N, int64_t K, const w4_forma
 }
 
 size_t w4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-    if (M < 1 || check_nk(N, K) != W4_OK) return 0;
+    if (M < 1 || check_nk(N, K) != W4_OK || K > W4_GEMM_MAX_K) return 0;
     return w4::gemm_workspace(M, K);
 }
 
@@ -303,7 +303,7 @@ w4_status w4_gemm(const void* prepared, int64_t N, int64_t K, const void* X, int
     if (yt != W4_F32 && yt != W4_BF16) return W4_ERR_DTYPE;
     w4_status st = check_nk(N, K);
     if (st != W4_OK) return st;
-    if (M < 1 || (M + 127) / 128 > 65535) return W4_ERR_SHAPE;
+    if (K > W4_GEMM_MAX_K || M < 1 || (M + 127) / 128 > 65535) return W4_ERR_SHAPE;
     // the tile count (128 x 256 output tiles, padded to a multiple of 8) is a grid size
     if (((M + 127) / 128) * ((N + 255) / 256) > (int64_t)INT32_MAX - 8) return W4_ERR_SHAPE;
     if (!workspace || workspace_bytes < w4_gemm_workspace_bytes(M, N, K)) return W4_ERR_WORKSPACE;
@@ -323,7 +323,7 @@ w4_status w4_gemm_noalloc(const void* prepared, int64_t N, int64_t K, const void
     if (yt != W4_F32 && yt != W4_BF16) return W4_ERR_DTYPE;
     w4_status st = check_nk(N, K);
     if (st != W4_OK) return st;
-    if (M < 1 || (M + 127) / 128 > 65535) return W4_ERR_SHAPE;
+    if (K > W4_GEMM_MAX_K || M < 1 || (M + 127) / 128 > 65535) return W4_ERR_SHAPE;
     if (((M + 127) / 128) * ((N + 255) / 256) > (int64_t)INT32_MAX - 8) return W4_ERR_SHAPE;
     if (w4_gemm_workspace_bytes(M, N, K) > W4_GEMM_NOALLOC_MAX_WORKSPACE) return W4_ERR_WORKSPACE;
     if (!aligned(prepared, 256) || !aligned(X, 16) || !aligned(Y, yt == W4_F32 ? 4 : 2))

@@ -53,6 +53,7 @@ extern "C" {
 #define W4_GEMV_MAX_M 16
 #define W4_GEMV_MAX_K 32768
 #define W4_FP8_MAX_K 65536
+#define W4_GEMM_MAX_K (1 << 20)
 
 typedef enum {
     W4_OK = 0,
@@ -230,8 +231,9 @@ w4_status w4_gemv_fmt(const void* prepared, int64_t N, int64_t K, const w4_forma
  *             copy of X, then per row its exponent and a window flag, each part
  *             256-B aligned), 16-B aligned; contents need no initialisation.  Calls
  *             sharing a workspace must be ordered.
- * Limits: N, K as w4_prepare; 1 <= M <= 65535*128; at most 2^31 - 9 output tiles of
- * 128 x 256 (else W4_ERR_SHAPE).
+ * Limits: N, K as w4_prepare and K <= W4_GEMM_MAX_K (the kernels address the operands of
+ * a 128 x 256 tile with 32-bit offsets); 1 <= M <= 65535*128; at most 2^31 - 9 output
+ * tiles of 128 x 256 (else W4_ERR_SHAPE; w4_gemm_workspace_bytes returns 0).
  */
 size_t w4_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 w4_status w4_gemm(const void* prepared, int64_t N, int64_t K,

@@ -68,6 +68,10 @@ def test_validation_errors_before_device_work():
     # more output tiles than a grid holds
     big = 1 << 62
     assert L.w4_gemm(_fake(), 2**31 - 1, 128, _fake(), 65535 * 128, _fake(), 0, _fake(), big, s) == 2
+    # K beyond W4_GEMM_MAX_K (2^20): the GEMM's 32-bit operand offsets
+    assert L.w4_gemm(_fake(), 4, (1 << 20) + 128, _fake(), 4, _fake(), 0, _fake(), big, s) == 2
+    assert L.w4_gemm_noalloc(_fake(), 4, (1 << 20) + 128, _fake(), 1, _fake(), 0, s) == 2
+    assert w4.w4_gemm_workspace_bytes(4, 4, (1 << 20) + 128) == 0
     assert L.w4_fp8_gemm(_fake(), _fake(), 2**31 - 1, _fake(), _fake(), 2**31 - 1, 128, _fake(), 0, s) == 2
     assert L.w4_int8_gemm(_fake(), _fake(), 2**31 - 1, _fake(), _fake(), 2**31 - 1, 128, _fake(), 0, s) == 2
     # the fixed-workspace GEMM: validated like w4_gemm, and a workspace beyond its array
