@@ -555,7 +555,8 @@ int rows_for(Kern kernel, int block, int n, int mt, int chunk_rows, std::atomic<
 
 // Small matrices that fill less than one round of resident groups at the smallest chunk take
 // workgroups of one step (four rows), twice the waves per CU, when those still fit in one
-// round (measured on MI355X: 4096 x 4096 at M = 1, 4.4 against 4.9 us)
+// round (measured on MI355X, 4096 x 4096 at M = 1: 4.4 against 4.9 us with bf16 x, 5.7
+// against 6.3 us with binary32 x)
 bool one_step_fits(int n, int rows, int chunk_rows, int resident) {
     const long slots = (long)resident * compute_units();
     return rows == chunk_rows && (n + rows - 1) / rows < slots && (n + kRowsPerStep - 1) / kRowsPerStep <= slots;
@@ -567,7 +568,7 @@ hipError_t launch_var(GemvArgs a, dim3 block, hipStream_t s) {
     static std::atomic<int> cache[17];
     auto kern = gemv_kernel<MT, XF32, SPT, MAXT, RAGGED, SBF16>;
     a.rows = rows_for(kern, (int)block.x, a.n, MT, CR, cache);
-    if constexpr (MT == 1 && !XF32 && SPT == 1) {
+    if constexpr (MT == 1 && SPT == 1) {
         if (one_step_fits(a.n, a.rows, CR, cache[block.x / 64].load(std::memory_order_relaxed))) {
             const dim3 grid((unsigned)((a.n + kRowsPerStep - 1) / kRowsPerStep));
             const size_t shmem = (size_t)(block.x / 64) * kRowsPerStep * MT * sizeof(float);

@@ -92,17 +92,18 @@ def test_llama70b_layer_every_output(matrix):
 
 @pytest.mark.parametrize("n,k", [(4096, 4096), (4094, 4096), (1030, 8192), (2050, 2048)])
 def test_one_step_workgroups(n, k):
-    """Small matrices at M = 1 (bf16 x) run workgroups of four rows: every output against the
-    oracle, with a ragged last workgroup (N not a multiple of 4), and with x wide enough in
-    its first 1024 inputs that those waves take the exact binary32 path."""
+    """Small matrices at M = 1 run workgroups of four rows: every output against the oracle,
+    with a ragged last workgroup (N not a multiple of 4), for binary32 x, and for bf16 x both
+    ordinary and wide enough in its first 1024 inputs that those waves take the exact path."""
     rng = np.random.default_rng(n + k)
     w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
     prep, _ = _quant_prepare(torch.from_numpy(w).to(DEV))
     x = rng.standard_normal((1, k)).astype(np.float32)
     xw = x.copy()
     xw[:, :1024] = synth.wide_range_activations(1, 1024, seed=n)
-    for label, xv in (("normal x", x), ("partly wide x", xw)):
-        xb = torch.from_numpy(xv).to(torch.bfloat16)
+    for label, xv, dt in (("normal x", x, torch.bfloat16), ("partly wide x", xw, torch.bfloat16),
+                          ("binary32 x", xw, torch.float32)):
+        xb = torch.from_numpy(xv).to(dt)
         yr, bound, _ = _ref_from_oracle(w, to_np32(xb))
         y = _run(prep, n, k, xb.to(DEV))
         r = assert_within(to_np32(y), yr, bound, f"{n}x{k} {label}")
