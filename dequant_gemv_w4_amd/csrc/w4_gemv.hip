@@ -45,7 +45,9 @@
 //     wait counts stay exact and a step waits only for its own loads).  The first step's
 //     loads follow x's directly, so they are in flight while x is converted;
 //   * groups of up to eight waves end the launch with a round of workgroups that take
-//     half the rows of the others, which shortens the tail of the weight stream;
+//     half the rows of the others, which shortens the tail of the weight stream; at M = 1 a
+//     matrix too small to fill one round of eight-row workgroups runs workgroups of a
+//     single step (four rows), which doubles the waves per CU;
 //   * the scale/zero words of the four rows of a step are one 16-byte load; two
 //     v_perm_b32 build the binary16 pairs -(1024 + zero) and -(1024 + 16 zero) from the
 //     zero bytes of the word;
