@@ -60,6 +60,24 @@ def test_prefill_shape_rows_and_full_sub_gemm():
     print(f"M=256 sub-GEMM: worst err/bound {r:.3e}")
 
 
+def test_large_k_operand_offsets():
+    """K = 65536 (512 groups): the stage loads address each tile's X' rows and weight columns
+    with 32-bit offsets from a uniform base; ragged M and N put clamped rows and columns in
+    the last tiles.  Every output against the oracle."""
+    rng = np.random.default_rng(77)
+    n, k, m = 300, 65536, 130
+    w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
+    X = torch.from_numpy(rng.standard_normal((m, k)).astype(np.float32)).to(torch.bfloat16)
+    prep = _prep(torch.from_numpy(w).to(DEV))
+    Y = w4.w4_gemm(prep, n, k, X.to(DEV))
+    torch.cuda.synchronize()
+    p, s, z = oracle.quantize_ref(w)
+    x32 = to_np32(X)
+    r = assert_within(to_np32(Y), oracle.gemv_ref(p, s, z, x32), oracle.tolerance_ref(p, s, z, x32),
+                      f"GEMM M={m} N={n} K={k}")
+    print(f"worst err/bound {r:.3e}")
+
+
 def test_gemm_deterministic():
     rng = np.random.default_rng(2)
     w = torch.from_numpy((0.02 * rng.standard_normal((512, 2048))).astype(np.float32)).to(DEV)
