@@ -158,12 +158,19 @@ def percentile(values: list, q: float) -> float:
     return v[lo] + (v[hi] - v[lo]) * (pos - lo)
 
 
-def per_shape(prepared, layers: int, dev: str, reps: int = 3, fused: bool = False, m: int = 1):
-    """Isolated GB/s per matrix shape at batch m: the same shape across all layers, back to back."""
+def per_shape(prepared, layers: int, dev: str, reps: int = 3, fused: bool = False, m: int = 1,
+              with_read: bool = False):
+    """Isolated GB/s per matrix shape at batch m: the same shape across all layers, back to back.
+
+    With ``with_read``, also the time of a plain read (w4_stream_read) of the same prepared
+    buffers in the same launch pattern, and the ratio of the two.
+    """
     import synth
+    import dequant_gemv_w4_amd as w4
     from dequant_gemv_w4_amd.decode import DecodeStep, GemvCall
     import torch
 
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
     out = {}
     order = synth.FUSED_ORDER if fused else synth.MATRIX_ORDER
     shapes = synth.LLAMA70B_FUSED_SHAPES if fused else synth.LLAMA70B_SHAPES
@@ -178,6 +185,27 @@ def per_shape(prepared, layers: int, dev: str, reps: int = 3, fused: bool = Fals
         ms = time_step(st, reps, 1)
         out[name] = {"N": n, "K": k, "us_per_call": round(ms * 1000 / layers, 2),
                      "GB/s": round(st.algorithmic_bytes() / (ms * 1e-3) / 1e9, 1)}
+        if with_read:
+            bufs = [prepared[(layer, name)] for layer in range(layers)]
+            for b in bufs:
+                w4.w4_stream_read(b, sink)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for b in bufs:
+                    w4.w4_stream_read(b, sink)
+            g.replay()
+            torch.cuda.synchronize()
+            start = torch.cuda.Event(enable_timing=True)
+            end = torch.cuda.Event(enable_timing=True)
+            start.record()
+            for _ in range(reps):
+                g.replay()
+            end.record()
+            end.synchronize()
+            read_us = start.elapsed_time(end) * 1000 / (reps * layers)
+            out[name]["read_probe_us_per_call"] = round(read_us, 2)
+            out[name]["gemv_vs_read"] = round(read_us / (ms * 1000 / layers), 4)
     return out
 
 
@@ -658,7 +686,7 @@ def main() -> int:
             del st
             log(f"M={m}: {msm:.3f} ms/step")
         result["batch_sweep_fused"] = batches
-        result["per_shape_fused_m1"] = per_shape(prepared, args.layers, dev, fused=True)
+        result["per_shape_fused_m1"] = per_shape(prepared, args.layers, dev, fused=True, with_read=True)
         result["read_ceiling"] = read_ceiling(prepared, args.layers, dev, ms)
         log(f"read ceiling: {result['read_ceiling']}")
         del step, prepared
