@@ -388,8 +388,8 @@ __device__ __forceinline__ void lds_dma4(const void* g, uint32_t lds_addr) {
 constexpr int vm_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
 
 // wait until the codes of group j of the current row step (and its scale/zero words) have
-// landed: later loads are the rest of this row step (8,7,6,5,3,2,1,0 for j = 0..7) plus the
-// ten loads of the next row step when it is in flight
+// landed: later loads are the rest of this row step (7, 5, 2 and 0 for the group pairs
+// j / 2 = 0..3) plus the ten loads of the next row step when it is in flight
 __device__ __forceinline__ void wait_group(int j, bool more) {
     // load d (0..7) holds rows 8(d&1).. of groups 2(d>>1), 2(d>>1)+1; group j needs load
     // 2(j>>1)+1; order: sz(0-3), d0..d3, sz(4-7), d4..d7
