@@ -360,6 +360,10 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(const uint8_t* __restric
 //     swaps give every lane of the column the words of all four groups.
 //   * Partial sums of the waves meet in LDS after every row step (double-buffered, one
 //     barrier per step).
+//   * A row step is compiled per activation format and per whether it issues the next
+//     step's loads, so its eight groups are straight-line code and the LDS reads of group
+//     j + 1 go out before group j is computed; steps that lie inside the matrix (a wave
+//     with all eight groups) load from a uniform base in SGPRs with fixed lane offsets.
 //   * With six or more row steps per workgroup (TRY_F16), a wave whose x converts exactly
 //     to binary16 with one power-of-two exponent per row of x (over the wave's groups)
 //     keeps binary16 x in its A operands and uses the exact binary16 codes with
