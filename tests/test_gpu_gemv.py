@@ -138,7 +138,8 @@ def test_short_last_round_rows():
 @pytest.mark.parametrize("n,k,m", [(1, 128, 1), (5, 256, 16), (1000, 384, 2), (77, 11008, 1),
                                    (64, 32768, 1), (64, 32768, 5), (4099, 2048, 8),
                                    (77, 11008, 4), (130, 16512, 2), (33, 16512, 3),
-                                   (2050, 384, 16), (96, 32768, 16), (40, 32768, 11)])
+                                   (2050, 384, 16), (96, 32768, 16), (40, 32768, 11),
+                                   (3, 128, 16), (7, 384, 8), (33, 1152, 4)])
 def test_shapes_and_ragged_edges(n, k, m):
     rng = np.random.default_rng(n + k + m)
     w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
