@@ -364,7 +364,7 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(const uint8_t* __restric
 //     step's loads, so its eight groups are straight-line code and the LDS reads of group
 //     j + 1 go out before group j is computed; steps that lie inside the matrix (a wave
 //     with all eight groups) load from a uniform base in SGPRs with fixed lane offsets.
-//   * With six or more row steps per workgroup (TRY_F16), a wave whose x converts exactly
+//   * A wave whose x converts exactly
 //     to binary16 with one power-of-two exponent per row of x (over the wave's groups)
 //     keeps binary16 x in its A operands and uses the exact binary16 codes with
 //     v_mfma_f32_16x16x32_f16: 9 instead of 17 vector instructions per eight codes, for
@@ -434,8 +434,6 @@ __device__ __forceinline__ void bcast_rows(uint32_t v, uint32_t (&b)[4]) {
     b[3] = (uint32_t)hi[1];
 }
 
-// TRY_F16: convert x to binary16 where it converts exactly (workgroups with enough row steps)
-template <bool TRY_F16>
 __global__ __launch_bounds__(512) void gemv_mfma_xr_kernel(const uint8_t* __restrict__ wq,
                                                          const uint32_t* __restrict__ sz,
                                                          const uint16_t* __restrict__ x,
@@ -537,15 +535,14 @@ __global__ __launch_bounds__(512) void gemv_mfma_xr_kernel(const uint8_t* __rest
     }
     issue_step(0);
 
-    // binary16 x (TRY_F16, on workgroups with enough row steps to pay for the conversion):
-    // x * 2^-E per row of x, E putting the largest value of the row over this
+    // binary16 x: x * 2^-E per row of x, E putting the largest value of the row over this
     // wave's groups just under 2^16; exact when every non-zero value lands on a normal
     // binary16 (within 2^25 of the largest, also after the further 2^-4 at the inputs of the
     // 16 (q - zero) codes).  The codes then need no bf16 conversion.  A wave whose rows do
     // not all pass keeps bf16 x.
     bool f16 = false;
     int ev[4] = {0, 0, 0, 0};   // E of the rows 4 kb + v this lane accumulates
-    if constexpr (TRY_F16) {
+    {
         u16x2_t vmax = {0, 0}, vmin = {0xFFFF, 0xFFFF};
         // (scheduling barriers per group keep the compiler from spreading the work over many
         // temporaries beside the 128 registers of x)
@@ -675,8 +672,8 @@ __global__ __launch_bounds__(512) void gemv_mfma_xr_kernel(const uint8_t* __rest
         for (int t = 0; t + 1 < steps; ++t) row_step(fc, True{}, t);
         row_step(fc, False{}, steps - 1);
     };
-    if (TRY_F16 && f16)
-        all_steps(std::integral_constant<bool, TRY_F16>{});
+    if (f16)
+        all_steps(std::integral_constant<bool, true>{});
     else
         all_steps(False{});
 }
@@ -739,24 +736,19 @@ static hipError_t launch_xr(const uint8_t* wq, const uint32_t* sz, const uint16_
     if (shmem > 65536) {
         static std::atomic<int> raised{0};
         if (!raised.load(std::memory_order_relaxed)) {
-            for (const void* f : {reinterpret_cast<const void*>(gemv_mfma_xr_kernel<false>),
-                                  reinterpret_cast<const void*>(gemv_mfma_xr_kernel<true>)}) {
-                hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                   (int)(8 * (kXrWaveRing + kXrRedBytes)));
-                if (e != hipSuccess) return e;
-            }
+            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_mfma_xr_kernel),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               (int)(8 * (kXrWaveRing + kXrRedBytes)));
+            if (e != hipSuccess) return e;
             raised.store(1, std::memory_order_relaxed);
         }
     }
     const dim3 grid((unsigned)((n + R - 1) / R));
     const dim3 block((unsigned)(64 * waves));
     // binary16 x costs about 1000 vector instructions per lane and workgroup and saves 256 per
-    // row step: taken from six row steps on (measured on MI355X: gate|up 57344 x 8192 at
-    // M = 4, 8, 16 in 58.5-61.1 us against 63.3-63.9 with bf16 x)
-    if (R / 16 >= 6)
-        hipLaunchKernelGGL(gemv_mfma_xr_kernel<true>, grid, block, shmem, s, wq, sz, x, y, yb, n, k, m, gpw, R);
-    else
-        hipLaunchKernelGGL(gemv_mfma_xr_kernel<false>, grid, block, shmem, s, wq, sz, x, y, yb, n, k, m, gpw, R);
+    // row step; measured on MI355X it pays from the ring's minimum of three row steps on
+    // (qkv 10240 x 8192 at M = 4, 8, 16: 15.9-16.5 us against 17.2-18.0 with bf16 x)
+    hipLaunchKernelGGL(gemv_mfma_xr_kernel, grid, block, shmem, s, wq, sz, x, y, yb, n, k, m, gpw, R);
     return hipGetLastError();
 }
 
