@@ -30,8 +30,8 @@ DEV = "cuda:0"
 # (N, K) reaching each product kernel: the one-row kernel at M = 1..3 on every shape; for
 # bf16 x at larger M the streaming matrix-core kernel (few rows, or K > 64 groups) and the
 # ring kernel (K <= 64 groups, at least 48 rows per workgroup over 256 compute units), which
-# converts x to binary16 from six 16-row steps per workgroup on (24576 rows) and keeps bf16
-# x below that (12288 rows) or where a wave's x does not convert exactly
+# converts x to binary16 per row and wave and keeps bf16 x where a wave's x does not convert
+# exactly
 SHAPES = {"small": (300, 1024), "ring": (12288, 1024), "ring_f16": (24576, 4096),
           "stream": (520, 9216)}
 M_VALUES = (1, 2, 3, 4, 8, 16)
