@@ -648,12 +648,12 @@ hipError_t launch_gemv(const uint8_t* prepared, int64_t n, int64_t k, const void
                        int64_t m, void* y, bool y_bf16, hipStream_t s) {
     // bf16 rows: the matrix-core kernels read the weights once for all rows.  The dot2
     // kernel below does M times the vector work per weight; it stays faster (measured on
-    // MI355X at the 70B shapes) at one row, at two rows while it needs a single pass over
-    // the weights (K <= 16384), and at three rows on shapes with K and N <= 16384 that the
-    // ring kernel takes.
+    // MI355X at the 70B shapes) at one row, and at two rows while it needs a single pass over
+    // the weights (K <= 16384) unless the resident-x kernel has more than 16384 rows to
+    // spread its x conversion over (gate_up 57344 x 8192 at M = 2: 46.8 us against 49.4;
+    // qkv 10240 x 8192: 16.2 against 14.7).
     const bool one_pass = k <= 16384;
-    const bool dot2_wins = m == 1 || (m == 2 && one_pass) ||
-                           (m == 3 && one_pass && n <= 16384 && gemv_ring_takes(n, k));
+    const bool dot2_wins = m == 1 || (m == 2 && one_pass && !(n > 16384 && gemv_resident_x_takes(n, k)));
     if (!x_f32 && !dot2_wins)
         return launch_gemv_mfma(prepared, n, k, static_cast<const uint16_t*>(x), m, y, y_bf16, s);
     return launch_gemv_dot2(prepared, n, k, kGroup, false, x, x_f32, m, y, y_bf16, s);

@@ -18,8 +18,8 @@
 // v_pk_add_f16 subtracts 1024 + zero (1024 + 16 zero) exactly, and two scaled conversions
 // (binary16 -> E4M3 -> bf16, exact for these small integers; the second one scales the
 // 16 (q - zero) values back by 2^-4) give bf16.  x enters unchanged as bf16, every product
-// is exact, and a code equal to its zero contributes exactly 0.  (The ring kernel further
-// down takes binary16 x and the binary16 codes themselves where that pays.)
+// is exact, and a code equal to its zero contributes exactly 0.  (The resident-x kernel
+// further down takes binary16 x and the binary16 codes themselves where that pays.)
 //
 // Mapping (gfx950, wave64):
 //   * the waves of a workgroup split K: wave w takes groups [w*gpw, (w+1)*gpw);
@@ -341,39 +341,44 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(const uint8_t* __restric
     }
 }
 
-// Variant for K <= 8192 (at most eight groups per wave, at most eight waves).
+// Variant for K <= 8192 (at most eight groups per wave, at most eight waves): x resident in
+// registers, codes straight into registers.
 //   * Each wave keeps the A operands of its groups (x, four MFMA steps per group) in
-//     registers, then walks all rows of the workgroup in steps of 16.  The A
-//     operands arrive through the wave's ring before the weights do, in two rounds of four
-//     groups, with loads of 4 rows x 256 contiguous bytes.
-//   * Weights and scale/zero words go straight from global memory into a ring in LDS that
-//     belongs to the wave (global_load_lds: lane l's bytes land at slot + 16 l, and lane l
-//     reads them back), two row steps ahead, so the bytes in flight do not take registers.
-//     Each code load covers 8 rows x 128 contiguous bytes (two groups), eight full cache
-//     lines; a load of 16 rows x 64 bytes (one group, the MFMA lane order) touches sixteen
-//     half lines and kept the address unit stalled by the L1 three quarters of its busy
-//     time (about 7 % slower on the 70B gate_up shape).  The reads of the MFMA operands
-//     pick their lanes' bytes out of that order.  The loads of a row step are issued in a
-//     fixed order (scale/zero of groups 0-3, codes of groups 0-3, scale/zero of groups 4-7,
-//     codes of groups 4-7) and each group waits for an exact count of later loads.
+//     registers, then walks all rows of the workgroup in steps of 16.  The A operands
+//     arrive through the wave's LDS area in two rounds of four groups, with loads of
+//     4 rows x 256 contiguous bytes.
+//   * Codes load straight into registers.  Load d = 2p + h of a row step covers rows
+//     8h .. 8h + 7 x the 128 contiguous bytes of groups 2p, 2p + 1 (eight full cache lines):
+//     lane l takes row 8h + (l & 7), group 2p + ((l >> 3) & 1), 16-byte piece l >> 4.  The
+//     MFMA wants lane l to hold row l & 15 of one group, so the two loads of a pair are
+//     exchanged between lanes l and l ^ 8 (one DPP row rotation by 8 and one select per
+//     register, four instructions per 32 codes).  A load in the MFMA lane order itself
+//     (16 rows x 64 bytes) touches sixteen half lines and streams 5-20 % slower; staging
+//     the codes through an LDS ring (direct-to-LDS loads) streamed about 16 % slower than
+//     these register loads on the 70B gate_up shape.
+//   * The loads are buffer loads from a uniform base with fixed 32-bit lane offsets, so a
+//     load costs no address arithmetic; the next row step's loads of a group pair go out
+//     as soon as that pair of the current step has been used, so one set of registers
+//     holds the codes (x takes 128 of the 256).  The first row step instead goes through
+//     LDS with direct-to-LDS loads while x is converted, when the registers are busy.
+//   * A row step starts at row min(r0 + 16 t, N - 16): the last step of the last
+//     workgroup moves back into the matrix and stores only its new rows, so no load needs
+//     a per-lane bound.
 //   * Scale/zero: lane (col, kb) loads the word of group g + kb of its row; three permlane
 //     swaps give every lane of the column the words of all four groups.
 //   * Partial sums of the waves meet in LDS after every row step (double-buffered, one
-//     barrier per step).
+//     barrier per step), scaled there by each wave's 2^E.
 //   * A row step is compiled per activation format and per whether it issues the next
-//     step's loads, so its eight groups are straight-line code and the LDS reads of group
-//     j + 1 go out before group j is computed; steps that lie inside the matrix (a wave
-//     with all eight groups) load from a uniform base in SGPRs with fixed lane offsets.
-//   * A wave whose x converts exactly
-//     to binary16 with one power-of-two exponent per row of x (over the wave's groups)
-//     keeps binary16 x in its A operands and uses the exact binary16 codes with
-//     v_mfma_f32_16x16x32_f16: 9 instead of 17 vector instructions per eight codes, for
-//     about 1000 once per workgroup; its row sums are scaled by 2^E before the reduction.
+//     step's loads, so its eight groups are straight-line code.
+//   * A wave whose x converts exactly to binary16 with one power-of-two exponent per row
+//     of x (over the wave's groups) keeps binary16 x in its A operands and uses the exact
+//     binary16 codes with v_mfma_f32_16x16x32_f16: 9 instead of 17 vector instructions per
+//     eight codes, for about 1000 once per workgroup.
 constexpr int kXrGroups = 8;                        // groups per wave
-constexpr int kXrSlotBytes = 1024;                  // one group of one 16-row tile
-constexpr int kXrSzBytes = 256;                     // one scale/zero word per lane
-constexpr int kXrWaveRing = 16 * kXrSlotBytes + 4 * kXrSzBytes;   // two row steps
-constexpr int kXrRedBytes = 2 * 16 * kRedStride * 4;              // per wave: two row steps
+constexpr int kXrWaveLds = 17 * 1024;               // per wave: x staging (16 KB), then the
+                                                    // first row step (8.5 KB) and E (64 B)
+constexpr int kXrEOffset = 16 * 1024;               // E of the 16 rows of x, in the wave's area
+constexpr int kXrRedBytes = 2 * 16 * kRedStride * 4;   // per wave: two row steps
 
 __device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_addr) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
@@ -391,31 +396,7 @@ __device__ __forceinline__ void lds_dma4(const void* g, uint32_t lds_addr) {
 // s_waitcnt immediate waiting for vmcnt <= n only (gfx9 encoding)
 constexpr int vm_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
 
-// wait until the codes of group j of the current row step (and its scale/zero words) have
-// landed: later loads are the rest of this row step (7, 5, 2 and 0 for the group pairs
-// j / 2 = 0..3) plus the ten loads of the next row step when it is in flight
-__device__ __forceinline__ void wait_group(int j, bool more) {
-    // load d (0..7) holds rows 8(d&1).. of groups 2(d>>1), 2(d>>1)+1; group j needs load
-    // 2(j>>1)+1; order: sz(0-3), d0..d3, sz(4-7), d4..d7
-    if (more) {
-        switch (j >> 1) {
-            case 0: __builtin_amdgcn_s_waitcnt(vm_imm(17)); break;
-            case 1: __builtin_amdgcn_s_waitcnt(vm_imm(15)); break;
-            case 2: __builtin_amdgcn_s_waitcnt(vm_imm(12)); break;
-            default: __builtin_amdgcn_s_waitcnt(vm_imm(10)); break;
-        }
-    } else {
-        switch (j >> 1) {
-            case 0: __builtin_amdgcn_s_waitcnt(vm_imm(7)); break;
-            case 1: __builtin_amdgcn_s_waitcnt(vm_imm(5)); break;
-            case 2: __builtin_amdgcn_s_waitcnt(vm_imm(2)); break;
-            default: __builtin_amdgcn_s_waitcnt(vm_imm(0)); break;
-        }
-    }
-    asm volatile("" ::: "memory");  // LDS reads of the slot stay after the wait
-}
-
-// barrier for LDS data only: no fence, so no wait for the ring's loads in flight
+// barrier for LDS data only: no fence, so no wait for the code loads in flight
 __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
@@ -434,12 +415,17 @@ __device__ __forceinline__ void bcast_rows(uint32_t v, uint32_t (&b)[4]) {
     b[3] = (uint32_t)hi[1];
 }
 
+// lane i of each 16-lane row takes the value of lane i ^ 8
+__device__ __forceinline__ uint32_t ror8(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false);
+}
+
 __global__ __launch_bounds__(512) void gemv_mfma_xr_kernel(const uint8_t* __restrict__ wq,
                                                          const uint32_t* __restrict__ sz,
                                                          const uint16_t* __restrict__ x,
                                                          void* __restrict__ yv, int y_bf16, int N,
                                                          int K, int M, int gpw, int R) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // rings, then partial sums
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];  // per-wave areas, then partial sums
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -452,62 +438,56 @@ __global__ __launch_bounds__(512) void gemv_mfma_xr_kernel(const uint8_t* __rest
     const int g0 = wave * gpw;
     const int ng = min(Kg - g0, gpw);   // >= 1: the host sizes the block so every wave has groups
     const int64_t row_bytes = K >> 1;
-    const int steps = R >> 4;
+    const int steps = min(R, N - r0 + 15) >> 4;   // the last workgroup may have fewer rows
+    const bool upper = (lane & 8) != 0;           // lanes 8..15 of each 16-lane row
 
     const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
-    const uint32_t ring = __builtin_amdgcn_readfirstlane(smem_lds + wave * kXrWaveRing);
-    const uint8_t* ring_p = smem + wave * kXrWaveRing;
-    float* red = reinterpret_cast<float*>(smem + n_waves * kXrWaveRing);   // [2][waves][16][stride]
+    const uint32_t area = __builtin_amdgcn_readfirstlane(smem_lds + wave * kXrWaveLds);
+    const uint8_t* area_p = smem + wave * kXrWaveLds;
+    float* red = reinterpret_cast<float*>(smem + n_waves * kXrWaveLds);   // [2][waves][16][stride]
 
     const CodeConsts cc;
     const f32x4_t zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
 
-    // loads of row step t into the ring half t & 1; rows past N repeat row N-1 (never stored)
-    // per-lane byte offsets of a row step's loads from its first row and the wave's first group
-    // (codes) and from that row quad's first scale/zero word (used when the step lies inside
-    // the matrix and the wave has all its groups; the base address is then uniform)
+    // lane byte offsets of code loads 2p and 2p + 1 from a row step's first row and the
+    // wave's first group (plus 128 p).  Groups past the wave's range read the next bytes of
+    // the prepared buffer (at most 448 past a row; the scale/zero words follow the codes),
+    // which scale 0 drops.
     uint32_t coff[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
-        coff[h] = (uint32_t)((8 * h + (lane >> 3)) * row_bytes) + 64 * ((lane >> 2) & 1) + 16 * (lane & 3);
-    const uint32_t szoff[2] = {4u * (uint32_t)((col >> 2) * Kg * 4 + (col & 3) + 4 * kb),
-                               4u * (uint32_t)((col >> 2) * Kg * 4 + (col & 3) + 4 * (4 + kb))};
-    auto issue_step = [&](int t) {
-        const uint32_t wb = ring + (t & 1) * 8 * kXrSlotBytes;
-        const uint32_t sb = ring + 16 * kXrSlotBytes + (t & 1) * 2 * kXrSzBytes;
-        if (r0 + 16 * t + 16 <= N && ng == kXrGroups) {
-            const uint8_t* cbase = wq + (int64_t)(r0 + 16 * t) * row_bytes + (int64_t)g0 * 64;
-            const uint8_t* sbase = reinterpret_cast<const uint8_t*>(sz) +
-                                   4 * ((int64_t)((r0 + 16 * t) >> 2) * Kg * 4 + (int64_t)g0 * 4);
-            lds_dma4_sv(sbase, szoff[0], sb);
-#pragma unroll
-            for (int d = 0; d < 4; ++d) lds_dma16_sv(cbase + 128 * (d >> 1), coff[d & 1], wb + d * kXrSlotBytes);
-            lds_dma4_sv(sbase, szoff[1], sb + kXrSzBytes);
-#pragma unroll
-            for (int d = 4; d < 8; ++d) lds_dma16_sv(cbase + 128 * (d >> 1), coff[d & 1], wb + d * kXrSlotBytes);
-            return;
-        }
-        const int n = min(r0 + 16 * t + col, N - 1);
-        const uint32_t* szrow = sz + (int64_t)(n >> 2) * Kg * 4 + (n & 3) + (int64_t)g0 * 4;
-        // load d: lane reads 16 bytes at 16 (lane & 7) of the 128-byte span of groups
-        // 2(d>>1), 2(d>>1)+1 in row 8(d&1) + (lane >> 3): eight full lines per load
-        auto code_load = [&](int d) {
-            const int nr = min(r0 + 16 * t + 8 * (d & 1) + (lane >> 3), N - 1);
-            const int gg = min(2 * (d >> 1) + ((lane >> 2) & 1), ng - 1);
-            lds_dma16(wq + (int64_t)nr * row_bytes + (int64_t)(g0 + gg) * 64 + 16 * (lane & 3),
-                      wb + d * kXrSlotBytes);
-        };
-        lds_dma4(szrow + min(kb, ng - 1) * 4, sb);
-#pragma unroll
-        for (int d = 0; d < 4; ++d) code_load(d);
-        lds_dma4(szrow + min(4 + kb, ng - 1) * 4, sb + kXrSzBytes);
-#pragma unroll
-        for (int d = 4; d < 8; ++d) code_load(d);
+        coff[h] = (uint32_t)((8 * h + (lane & 7)) * row_bytes) + 64 * ((lane >> 3) & 1) + 16 * kb;
+    const int sg0 = g0 + min(kb, ng - 1);
+    auto step_row = [&](int t) __attribute__((always_inline)) { return min(r0 + 16 * t, N - 16); };
+    auto code_base = [&](int t) __attribute__((always_inline)) {
+        return wq + (int64_t)step_row(t) * row_bytes + (int64_t)g0 * 64;
     };
-    // ---- x of this wave's groups (A operands) and their sums, once per workgroup.  x goes
-    // through the (still empty) ring in two rounds of four groups, with loads of 4 rows x 256
-    // contiguous bytes (chunk c of row r at slot c ^ (r & 15)); loading it straight into the
-    // MFMA lane order made each load touch 32 lines
+    // scale/zero words: lane (col, kb) takes row col's word of groups g0 + kb and g0 + 4 + kb
+    // (four groups = 64 bytes further).  Past the wave's groups the lane reads whatever word
+    // follows (scale 0 drops it); the resource ends with the words, so a read past them
+    // returns 0 and touches no memory.
+    const uint32_t sgo0 = 16u * (uint32_t)sg0;
+    auto load_sz = [&](int t, uint32_t (&s)[2]) __attribute__((always_inline)) {
+        const int rb = step_row(t);
+        const uint32_t* sq = sz + (int64_t)(rb >> 2) * Kg * 4;
+        const int nrec = (((N + 3) >> 2) - (rb >> 2)) * Kg * 16;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(sq), 0, nrec, 0x00020000);
+        const int rr = (rb & 3) + col;
+        const uint32_t o = 4u * (uint32_t)((rr >> 2) * Kg * 4 + (rr & 3)) + sgo0;
+        s[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)o, 0, 0);
+        s[1] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)o, 64, 0);
+    };
+    // buffer loads: uniform base in the resource, the lane's 32-bit offset, the pair's
+    // 128 bytes as the scalar offset; non-temporal (every byte is read once)
+    auto load_pair = [&](const uint8_t* cb, int p, u32x4_t (&c)[8]) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(cb), 0, 0x7FFFFFFF, 0x00020000);
+        c[2 * p] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)coff[0], 128 * p, 2));
+        c[2 * p + 1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)coff[1], 128 * p, 2));
+    };
+    // ---- x of this wave's groups (A operands), once per workgroup.  x goes through the
+    // wave's LDS area in two rounds of four groups, with loads of 4 rows x 256 contiguous
+    // bytes (chunk c of row r at slot c ^ (r & 15)); loading it straight into the MFMA lane
+    // order made each load touch 32 lines
     u32x4_t xa[kXrGroups][4];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -518,7 +498,7 @@ __global__ __launch_bounds__(512) void gemv_mfma_xr_kernel(const uint8_t* __rest
             for (int i = 0; i < 4; ++i) {
                 const int r = 4 * i + (lane >> 4);
                 const uint16_t* src = x + (int64_t)min(r, M - 1) * K + gc * 128 + 8 * ((lane & 15) ^ (r & 15));
-                lds_dma16(src, ring + q * 4096 + i * 1024);
+                lds_dma16(src, area + q * 4096 + i * 1024);
             }
         }
         __builtin_amdgcn_s_waitcnt(vm_imm(0));
@@ -528,12 +508,24 @@ __global__ __launch_bounds__(512) void gemv_mfma_xr_kernel(const uint8_t* __rest
 #pragma unroll
             for (int s = 0; s < 4; ++s)
                 xa[4 * half + q][s] = *reinterpret_cast<const u32x4_t*>(
-                    ring_p + q * 4096 + col * 256 + (((4 * kb + s) ^ col) * 16));
-        // the reads have returned before the next loads overwrite the ring
+                    area_p + q * 4096 + col * 256 + (((4 * kb + s) ^ col) * 16));
+        // the reads have returned before the next loads overwrite the area
         __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
         asm volatile("" ::: "memory");
     }
-    issue_step(0);
+    // the first row step goes through the (now free) LDS area by direct-to-LDS loads (lane
+    // l's bytes at 16 l), so that no registers are held for it during the x conversion
+    {
+        const int rb = step_row(0);
+        const uint32_t* sq = sz + (int64_t)(rb >> 2) * Kg * 4;
+        const int rr = (rb & 3) + col;
+        const uint32_t o = (uint32_t)((rr >> 2) * Kg * 4 + (rr & 3));
+        lds_dma4(sq + o + 4 * sg0, area + 8 * 1024);
+        lds_dma4(sq + o + 4 * g0 + 4 * min(4 + kb, ng - 1), area + 8 * 1024 + 256);
+        const uint8_t* cb = code_base(0);
+#pragma unroll
+        for (int d = 0; d < 8; ++d) lds_dma16(cb + 128 * (d >> 1) + coff[d & 1], area + d * 1024);
+    }
 
     // binary16 x: x * 2^-E per row of x, E putting the largest value of the row over this
     // wave's groups just under 2^16; exact when every non-zero value lands on a normal
@@ -541,7 +533,7 @@ __global__ __launch_bounds__(512) void gemv_mfma_xr_kernel(const uint8_t* __rest
     // 16 (q - zero) codes).  The codes then need no bf16 conversion.  A wave whose rows do
     // not all pass keeps bf16 x.
     bool f16 = false;
-    int ev[4] = {0, 0, 0, 0};   // E of the rows 4 kb + v this lane accumulates
+    int e_row = 0;   // E of x row col (0 for bf16 x)
     {
         u16x2_t vmax = {0, 0}, vmin = {0xFFFF, 0xFFFF};
         // (scheduling barriers per group keep the compiler from spreading the work over many
@@ -549,12 +541,12 @@ __global__ __launch_bounds__(512) void gemv_mfma_xr_kernel(const uint8_t* __rest
 #pragma unroll
         for (int j = 0; j < kXrGroups; ++j) {
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
+            for (int q = 0; q < 4; ++q)
 #pragma unroll
                 for (int d = 0; d < 4; ++d) {
-                    const u16x2_t mag = as_u16x2(xa[j][s][d] & 0x7FFF7FFFu);
+                    const u16x2_t mag = as_u16x2(xa[j][q][d] & 0x7FFF7FFFu);
                     vmax = __builtin_elementwise_max(vmax, mag);
-                    vmin = __builtin_elementwise_min(vmin, mag - (unsigned short)1);  // 0 -> 0xFFFF
+                    vmin = __builtin_elementwise_min(vmin, mag - (unsigned short)1);
                 }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -568,96 +560,111 @@ __global__ __launch_bounds__(512) void gemv_mfma_xr_kernel(const uint8_t* __rest
 #pragma unroll
             for (int j = 0; j < kXrGroups; ++j)
 #pragma unroll
-                for (int s = 0; s < 4; ++s)
+                for (int q = 0; q < 4; ++q)
 #pragma unroll
                     for (int d = 0; d < 4; ++d) {
-                        uint32_t v = xa[j][s][d];
+                        uint32_t v = xa[j][q][d];
                         asm volatile("" : "+v"(v));
-                        xa[j][s][d] = v;
+                        xa[j][q][d] = v;
                     }
             const uint32_t ce = (uint32_t)((fmax - 30) << 7) * 0x00010001u;
             const uint32_t co = (uint32_t)((fmax - 26) << 7) * 0x00010001u;
 #pragma unroll
             for (int j = 0; j < kXrGroups; ++j) {
 #pragma unroll
-                for (int s = 0; s < 4; ++s)
+                for (int q = 0; q < 4; ++q)
 #pragma unroll
-                    for (int d = 0; d < 4; ++d) xa[j][s][d] = to_f16_pair(xa[j][s][d], (d & 1) ? co : ce);
+                    for (int d = 0; d < 4; ++d) xa[j][q][d] = to_f16_pair(xa[j][q][d], (d & 1) ? co : ce);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            const int e = fmax - 127 - 15;   // of row col
-#pragma unroll
-            for (int v = 0; v < 4; ++v) ev[v] = __shfl(e, 4 * kb + v);
+            e_row = fmax - 127 - 15;
         }
     }
+    // E of each row of x, for the threads that combine the waves' partial sums (they scale
+    // each wave's sums by its 2^E; the first barrier orders these writes)
+    if (kb == 0) *reinterpret_cast<int*>(smem + wave * kXrWaveLds + kXrEOffset + 4 * col) = e_row;
+
+    // codes (c) and scale/zero words (s) of the current row step
+    u32x4_t c[8];
+    uint32_t s[2];
+    __builtin_amdgcn_s_waitcnt(vm_imm(0));
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int d = 0; d < 8; ++d) c[d] = *reinterpret_cast<const u32x4_t*>(area_p + d * 1024 + 16 * lane);
+    s[0] = *reinterpret_cast<const uint32_t*>(area_p + 8 * 1024 + 4 * lane);
+    s[1] = *reinterpret_cast<const uint32_t*>(area_p + 8 * 1024 + 256 + 4 * lane);
 
     // one row step; F: binary16 x and codes (else bf16), MORE: the next row step's loads are
-    // issued here.  Both are compile-time, so the group loop is straight-line code and the
-    // LDS reads of group j + 1 are issued before group j is computed.
-    auto row_step = [&](auto fc, auto mc, int t) {
+    // issued here, group pair by group pair as the registers of a pair are used.  Both are
+    // compile-time, so the eight groups are straight-line code.
+    auto row_step = [&](auto fc, auto mc, int t) __attribute__((always_inline)) {
         constexpr bool F = decltype(fc)::value;
         constexpr bool MORE = decltype(mc)::value;
-        if constexpr (MORE) issue_step(t + 1);
-        const uint8_t* wslots = ring_p + (t & 1) * 8 * kXrSlotBytes;
-        const uint8_t* sslots = ring_p + 16 * kXrSlotBytes + (t & 1) * 2 * kXrSzBytes;
-        auto codes_of = [&](int j) {
-            return *reinterpret_cast<const u32x4_t*>(
-                wslots + (2 * (j >> 1) + (col >> 3)) * kXrSlotBytes + 16 * (8 * (col & 7) + 4 * (j & 1) + kb));
-        };
+        uint32_t szw[4];
+        const uint32_t s_hi = s[1];
+        bcast_rows(s[0], szw);
+        if constexpr (MORE) load_sz(t + 1, s);
+        const uint8_t* cbn = code_base(t + 1);
         f32x4_t acc = zero4;
-        uint32_t szw[2][4];
-        u32x4_t wcur, wnext;
-        wait_group(0, MORE);
-        bcast_rows(*reinterpret_cast<const uint32_t*>(sslots + 4 * lane), szw[0]);
-        wcur = codes_of(0);
 #pragma unroll
-        for (int j = 0; j < kXrGroups; ++j) {
-            if (j + 1 < kXrGroups) {
-                wait_group(j + 1, MORE);
-                if ((j + 1) % 4 == 0)
-                    bcast_rows(*reinterpret_cast<const uint32_t*>(sslots + ((j + 1) / 4) * kXrSzBytes + 4 * lane),
-                               szw[(j + 1) / 4]);
-                wnext = codes_of(j + 1);
+        for (int pp = 0; pp < 4; ++pp) {
+            // exchange lanes l and l ^ 8: c[2pp] then holds group 2pp of rows 0..15 in MFMA
+            // lane order (row l & 15, piece l >> 4), c[2pp + 1] group 2pp + 1
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const uint32_t a = c[2 * pp][v], b = c[2 * pp + 1][v];
+                const uint32_t ra = ror8(a), rb = ror8(b);
+                c[2 * pp][v] = upper ? rb : a;
+                c[2 * pp + 1][v] = upper ? b : ra;
             }
-            const uint32_t word = szw[j / 4][j % 4];
-            const uint32_t z1 = cc.z1(word), z16 = cc.z16(word);
-            f32x4_t p = zero4;
-            if constexpr (F) {
 #pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    p = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(xa[j][s]),
-                                                               as_f16x8(exact_codes_f16(wcur[s], z1, z16, cc)),
-                                                               p, 0, 0, 0);
-            } else {
+            for (int hh = 0; hh < 2; ++hh) {
+                const int j = 2 * pp + hh;
+                if (j == 4) bcast_rows(s_hi, szw);
+                const uint32_t word = szw[j % 4];
+                const uint32_t z1 = cc.z1(word), z16 = cc.z16(word);
+                f32x4_t p = zero4;
+                if constexpr (F) {
 #pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[j][s]),
-                                                                as_bf16x8(exact_codes(wcur[s], z1, z16, cc)),
-                                                                p, 0, 0, 0);
+                    for (int q = 0; q < 4; ++q)
+                        p = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            as_f16x8(xa[j][q]), as_f16x8(exact_codes_f16(c[j][q], z1, z16, cc)), p, 0, 0, 0);
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            as_bf16x8(xa[j][q]), as_bf16x8(exact_codes(c[j][q], z1, z16, cc)), p, 0, 0, 0);
+                }
+                // a group past the wave's range is computed with scale 0 (no branch)
+                const float keep = j < ng ? 1.0f : 0.0f;
+                const float sc = keep * (float)__builtin_bit_cast(_Float16, (uint16_t)(word & 0xFFFFu));
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[v] = fmaf(sc, p[v], acc[v]);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            // a group past the wave's range is computed with scale 0 (no branch)
-            const float keep = j < ng ? 1.0f : 0.0f;
-            const float sc = keep * (float)__builtin_bit_cast(_Float16, (uint16_t)(word & 0xFFFFu));
-#pragma unroll
-            for (int v = 0; v < 4; ++v) acc[v] = fmaf(sc, p[v], acc[v]);
-            wcur = wnext;
+            if constexpr (MORE) load_pair(cbn, pp, c);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        // partial sums of this row step: lane holds column (row) col, rows m = 4 kb + v
-        float* rb = red + ((t & 1) * n_waves + wave) * 16 * kRedStride;
+        // partial sums of this row step: lane holds column (row) col, rows m = 4 kb + v of x
+        float* rbuf = red + ((t & 1) * n_waves + wave) * 16 * kRedStride;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const int m = 4 * kb + v;
-            if (m < M) rb[col * kRedStride + m] = ldexpf(acc[v], ev[v]);   // ev = 0 for bf16 x
+            if (m < M) rbuf[col * kRedStride + m] = acc[v];
         }
         lds_barrier();
+        const int rb = step_row(t);
+        const int rfirst = r0 + 16 * t;   // rows below were written by the previous step
         for (int i = tid; i < 16 * M; i += blockDim.x) {
             const int r = i & 15;
             const int m = i >> 4;
-            const int row = r0 + 16 * t + r;
-            if (row < N) {
+            const int row = rb + r;
+            if (row >= rfirst) {
                 const float* rs = red + (t & 1) * n_waves * 16 * kRedStride;
                 float v = 0.0f;
-                for (int w = 0; w < n_waves; ++w) v += rs[(w * 16 + r) * kRedStride + m];
+                for (int w = 0; w < n_waves; ++w)
+                    v += ldexpf(rs[(w * 16 + r) * kRedStride + m],
+                                *reinterpret_cast<const int*>(smem + w * kXrWaveLds + kXrEOffset + 4 * m));
                 const int64_t o = (int64_t)m * N + row;
                 if (y_bf16)
                     static_cast<uint16_t*>(yv)[o] = (uint16_t)bf16_bits_rne(v);
@@ -668,12 +675,12 @@ __global__ __launch_bounds__(512) void gemv_mfma_xr_kernel(const uint8_t* __rest
     };
     using True = std::integral_constant<bool, true>;
     using False = std::integral_constant<bool, false>;
-    auto all_steps = [&](auto fc) {
+    auto all_steps = [&](auto fc) __attribute__((always_inline)) {
         for (int t = 0; t + 1 < steps; ++t) row_step(fc, True{}, t);
         row_step(fc, False{}, steps - 1);
     };
     if (f16)
-        all_steps(std::integral_constant<bool, true>{});
+        all_steps(True{});
     else
         all_steps(False{});
 }
@@ -706,10 +713,10 @@ hipError_t launch_t(const uint8_t* wq, const uint32_t* sz, const uint16_t* x, vo
 // (12 KB of LDS stages per wave; on the 70B down shape eight waves of 28 groups ran faster
 // than sixteen of 14), two tiles (32 rows) per workgroup: the fastest of the settings
 // measured on MI355X at the 70B shapes.
-// Rows per workgroup of the ring kernel: one round of workgroups (one per CU), a multiple
-// of 16.  The ring pays off from three row steps on; below that the streaming kernel is
-// used (measured on MI355X at the 70B shapes: o 8192x8192 streams faster, qkv and gate_up
-// run faster on the ring).
+// Rows per workgroup of the resident-x kernel: one round of workgroups (one per CU), a
+// multiple of 16.  Holding x pays off from three row steps on; below that the streaming
+// kernel is used (measured on MI355X at the 70B shapes: o 8192x8192 streams faster, qkv and
+// gate_up run faster with x resident).
 static int xr_rows(int n) {
     static std::atomic<int> cus{0};
     int cu = cus.load(std::memory_order_relaxed);
@@ -726,19 +733,19 @@ static int xr_rows(int n) {
     return (r + 15) / 16 * 16;
 }
 
-// K <= 8192 and at least three row steps per workgroup: the ring kernel.
+// K <= 8192 and at least three row steps per workgroup: the resident-x kernel.
 static hipError_t launch_xr(const uint8_t* wq, const uint32_t* sz, const uint16_t* x, void* y, int yb,
                      int n, int k, int m, int R, hipStream_t s) {
     const int kg = k / kGroup;
     const int waves = (kg + kXrGroups - 1) / kXrGroups;
     const int gpw = (kg + waves - 1) / waves;
-    const size_t shmem = (size_t)waves * (kXrWaveRing + kXrRedBytes);
+    const size_t shmem = (size_t)waves * (kXrWaveLds + kXrRedBytes);
     if (shmem > 65536) {
         static std::atomic<int> raised{0};
         if (!raised.load(std::memory_order_relaxed)) {
             hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_mfma_xr_kernel),
                                                hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               (int)(8 * (kXrWaveRing + kXrRedBytes)));
+                                               (int)(8 * (kXrWaveLds + kXrRedBytes)));
             if (e != hipSuccess) return e;
             raised.store(1, std::memory_order_relaxed);
         }
@@ -746,13 +753,13 @@ static hipError_t launch_xr(const uint8_t* wq, const uint32_t* sz, const uint16_
     const dim3 grid((unsigned)((n + R - 1) / R));
     const dim3 block((unsigned)(64 * waves));
     // binary16 x costs about 1000 vector instructions per lane and workgroup and saves 256 per
-    // row step; measured on MI355X it pays from the ring's minimum of three row steps on
-    // (qkv 10240 x 8192 at M = 4, 8, 16: 15.9-16.5 us against 17.2-18.0 with bf16 x)
+    // row step; measured on MI355X it pays from the minimum of three row steps on (qkv
+    // 10240 x 8192 at M = 4, 8, 16: 15.9-16.5 us against 17.2-18.0 with bf16 x)
     hipLaunchKernelGGL(gemv_mfma_xr_kernel, grid, block, shmem, s, wq, sz, x, y, yb, n, k, m, gpw, R);
     return hipGetLastError();
 }
 
-bool gemv_ring_takes(int64_t n, int64_t k) {
+bool gemv_resident_x_takes(int64_t n, int64_t k) {
     if (k / kGroup > kXrGroups * 8) return false;
     return xr_rows((int)n) >= 48;
 }
@@ -760,7 +767,7 @@ bool gemv_ring_takes(int64_t n, int64_t k) {
 hipError_t launch_gemv_mfma(const uint8_t* prepared, int64_t n, int64_t k, const uint16_t* x,
                             int64_t m, void* y, bool y_bf16, hipStream_t s) {
     const int kg = (int)(k / kGroup);
-    if (gemv_ring_takes(n, k))
+    if (gemv_resident_x_takes(n, k))
         return launch_xr(prepared, reinterpret_cast<const uint32_t*>(prepared + sz_offset(n, k)),
                          x, y, y_bf16 ? 1 : 0, (int)n, (int)k, (int)m, xr_rows((int)n), s);
     constexpr int per_wave = 8;

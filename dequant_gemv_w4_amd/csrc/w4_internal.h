@@ -105,10 +105,10 @@ hipError_t launch_gemv_dot2(const uint8_t* prepared, int64_t n, int64_t k, int g
                             bool y_bf16, hipStream_t s);
 hipError_t launch_gemv_mfma(const uint8_t* prepared, int64_t n, int64_t k, const uint16_t* x,
                             int64_t m, void* y, bool y_bf16, hipStream_t s);
-// Whether launch_gemv_mfma runs the shape on the ring kernel (x held in registers, weights
-// streamed through a per-wave LDS ring): K of at most 64 groups and at least 48 rows per
-// workgroup when one workgroup runs per compute unit.
-bool gemv_ring_takes(int64_t n, int64_t k);
+// Whether launch_gemv_mfma runs the shape on the resident-x kernel (x held in registers for
+// all the workgroup's rows, codes loaded straight into registers): K of at most 64 groups and
+// at least 48 rows per workgroup when one workgroup runs per compute unit.
+bool gemv_resident_x_takes(int64_t n, int64_t k);
 size_t gemm_workspace(int64_t m, int64_t k);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t s);
 // 8-bit rows: E4M3 codes, or symmetric INT8 codes when int8 is set

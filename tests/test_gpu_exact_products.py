@@ -29,10 +29,10 @@ DEV = "cuda:0"
 
 # (N, K) reaching each product kernel: the one-row kernel at M = 1..3 on every shape; for
 # bf16 x at larger M the streaming matrix-core kernel (few rows, or K > 64 groups) and the
-# ring kernel (K <= 64 groups, at least 48 rows per workgroup over 256 compute units), which
+# resident-x kernel (K <= 64 groups, at least 48 rows per workgroup over 256 compute units), which
 # converts x to binary16 per row and wave and keeps bf16 x where a wave's x does not convert
 # exactly
-SHAPES = {"small": (300, 1024), "ring": (12288, 1024), "ring_f16": (24576, 4096),
+SHAPES = {"small": (300, 1024), "resident": (12288, 1024), "resident_f16": (24576, 4096),
           "stream": (520, 9216)}
 M_VALUES = (1, 2, 3, 4, 8, 16)
 
@@ -100,11 +100,11 @@ def test_wide_range_activations(shape):
     print(f"{shape}: worst err/bound {worst:.3e}")
 
 
-def test_ring_binary16_x_some_waves_fall_back():
-    """The ring kernel on 24576 x 4096 (four waves of eight groups, six row steps): x wide
+def test_resident_x_binary16_some_waves_fall_back():
+    """The resident-x kernel on 24576 x 4096 (four waves of eight groups, six row steps): x wide
     only in the first 1024 inputs, so the first wave of every workgroup keeps bf16 x and the
     other three convert it to binary16; every output against the oracle at M = 4, 8, 16."""
-    n, k = SHAPES["ring_f16"]
+    n, k = SHAPES["resident_f16"]
     rng = np.random.default_rng(61)
     w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
     prep, ref = _quant_prepare(w)
@@ -113,17 +113,17 @@ def test_ring_binary16_x_some_waves_fall_back():
     worst = 0.0
     for m in (4, 8, 16):
         xm = torch.from_numpy(x[:m]).to(DEV).to(torch.bfloat16).contiguous()
-        worst = max(worst, _check_gemv(prep, ref, n, k, xm, f"ring mixed M={m}"))
+        worst = max(worst, _check_gemv(prep, ref, n, k, xm, f"resident-x mixed M={m}"))
         # only rows 0..m-1 matter: a wide row among ordinary ones
         xm2 = torch.from_numpy(rng.standard_normal((m, k)).astype(np.float32)).to(torch.bfloat16)
         xm2[m // 2] = torch.from_numpy(x[0]).to(torch.bfloat16)
-        worst = max(worst, _check_gemv(prep, ref, n, k, xm2.to(DEV).contiguous(), f"ring one wide row M={m}"))
-    print(f"ring mixed: worst err/bound {worst:.3e}")
+        worst = max(worst, _check_gemv(prep, ref, n, k, xm2.to(DEV).contiguous(), f"resident-x one wide row M={m}"))
+    print(f"resident-x mixed: worst err/bound {worst:.3e}")
 
 
 @pytest.mark.parametrize("m", [4, 5, 7, 13, 16])
-def test_ring_binary16_ragged_rows(m):
-    """The ring kernel's binary16 path with a ragged last workgroup (24616 rows: 220
+def test_resident_x_binary16_ragged_rows(m):
+    """The resident-x kernel's binary16 path with a ragged last workgroup (24616 rows: 220
     workgroups of 112 rows, the last with 88, whose loads for the 24 missing rows repeat row
     N-1) and M not a multiple of four; every output against the oracle."""
     n, k = 24616, 4096
@@ -131,7 +131,7 @@ def test_ring_binary16_ragged_rows(m):
     w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
     prep, ref = _quant_prepare(w)
     x = torch.from_numpy(rng.standard_normal((m, k)).astype(np.float32)).to(torch.bfloat16)
-    r = _check_gemv(prep, ref, n, k, x.to(DEV).contiguous(), f"ring ragged M={m}")
+    r = _check_gemv(prep, ref, n, k, x.to(DEV).contiguous(), f"resident-x ragged M={m}")
     print(f"M={m}: worst err/bound {r:.3e}")
 
 

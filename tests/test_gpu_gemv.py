@@ -198,23 +198,23 @@ def test_deterministic_repeat():
     assert torch.equal(y1, y2)
 
 
-# ---- batched rows on the ring kernel (K <= 8192 and enough rows per workgroup): ragged
+# ---- batched rows on the resident-x kernel (K <= 8192 and enough rows per workgroup): ragged
 # group counts (K = 1152: a wave with four of its eight groups), ragged N, several M
 
 @pytest.mark.parametrize("n,k,m", [(20000, 1152, 3), (12300, 1152, 4), (12300, 1152, 16),
                                    (12289, 4096, 5)])
-def test_batched_ring_shapes_full(n, k, m):
+def test_batched_resident_x_shapes_full(n, k, m):
     rng = np.random.default_rng(n + k + m)
     w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
     x = torch.from_numpy(rng.standard_normal((m, k)).astype(np.float32)).to(torch.bfloat16)
     prep, _ = _quant_prepare(torch.from_numpy(w).to(DEV))
     y = _run(prep, n, k, x.to(DEV))
     yr, bound, _ = _ref_from_oracle(w, to_np32(x))
-    r = assert_within(to_np32(y), yr, bound, f"ring N={n} K={k} M={m}")
+    r = assert_within(to_np32(y), yr, bound, f"resident-x N={n} K={k} M={m}")
     print(f"N={n} K={k} M={m}: worst err/bound {r:.3e}")
 
 
-def test_batched_ring_sampled_rows_k8192():
+def test_batched_resident_x_sampled_rows_k8192():
     n, k, m = 20000, 8192, 16
     W = synth.normal_weights(n, k, 777, DEV)
     x16 = synth.normal_activations(m, k, 778, DEV)
@@ -226,10 +226,10 @@ def test_batched_ring_sampled_rows_k8192():
     for mm in (3, 4, 8, 16):
         y = to_np32(_run(prep, n, k, x16[:mm].contiguous()))
         assert_within(y[:, rows], oracle.gemv_ref(p, s, z, x32[:mm]),
-                      oracle.tolerance_ref(p, s, z, x32[:mm]), f"ring sampled M={mm}")
+                      oracle.tolerance_ref(p, s, z, x32[:mm]), f"resident-x sampled M={mm}")
 
 
-def test_batched_ring_one_hot_exact():
+def test_batched_resident_x_one_hot_exact():
     rng = np.random.default_rng(11)
     n, k, m = 12300, 1152, 16
     W = torch.from_numpy((0.02 * rng.standard_normal((n, k))).astype(np.float32)).to(DEV)
@@ -244,7 +244,7 @@ def test_batched_ring_one_hot_exact():
         assert np.array_equal(y[i].astype(np.float64), wh[:, c]), f"column {c}"
 
 
-def test_batched_ring_zero_rows_exact():
+def test_batched_resident_x_zero_rows_exact():
     rng = np.random.default_rng(12)
     n, k, m = 20000, 1152, 3
     w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
@@ -255,7 +255,7 @@ def test_batched_ring_zero_rows_exact():
     y = to_np32(_run(prep, n, k, x.to(DEV)))
     assert np.all(y[:, ::3] == 0.0)
     yr, bound, _ = _ref_from_oracle(w, to_np32(x))
-    assert_within(y, yr, bound, "ring rows with zero groups")
+    assert_within(y, yr, bound, "resident-x rows with zero groups")
 
 
 def test_decode_step_graph_replays_match_eager():
