@@ -489,6 +489,8 @@ __global__ __launch_bounds__(512) void gemv_mfma_xr_kernel(const uint8_t* __rest
     // bytes (chunk c of row r at slot c ^ (r & 15)); loading it straight into the MFMA lane
     // order made each load touch 32 lines
     u32x4_t xa[kXrGroups][4];
+    const int xquads = (M + 3) >> 2;   // quads of x rows loaded; rows past M are zero
+    const u32x4_t zero_x = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
 #pragma unroll
@@ -496,9 +498,11 @@ __global__ __launch_bounds__(512) void gemv_mfma_xr_kernel(const uint8_t* __rest
             const int gc = g0 + min(4 * half + q, ng - 1);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int r = 4 * i + (lane >> 4);
-                const uint16_t* src = x + (int64_t)min(r, M - 1) * K + gc * 128 + 8 * ((lane & 15) ^ (r & 15));
-                lds_dma16(src, area + q * 4096 + i * 1024);
+                if (i < xquads) {
+                    const int r = 4 * i + (lane >> 4);
+                    const uint16_t* src = x + (int64_t)min(r, M - 1) * K + gc * 128 + 8 * ((lane & 15) ^ (r & 15));
+                    lds_dma16(src, area + q * 4096 + i * 1024);
+                }
             }
         }
         __builtin_amdgcn_s_waitcnt(vm_imm(0));
@@ -507,8 +511,8 @@ __global__ __launch_bounds__(512) void gemv_mfma_xr_kernel(const uint8_t* __rest
         for (int q = 0; q < 4; ++q)
 #pragma unroll
             for (int s = 0; s < 4; ++s)
-                xa[4 * half + q][s] = *reinterpret_cast<const u32x4_t*>(
-                    area_p + q * 4096 + col * 256 + (((4 * kb + s) ^ col) * 16));
+                xa[4 * half + q][s] = col < M ? *reinterpret_cast<const u32x4_t*>(
+                    area_p + q * 4096 + col * 256 + (((4 * kb + s) ^ col) * 16)) : zero_x;
         // the reads have returned before the next loads overwrite the area
         __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
         asm volatile("" ::: "memory");
