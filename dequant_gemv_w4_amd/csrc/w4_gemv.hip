@@ -166,7 +166,7 @@ __device__ __forceinline__ float word_scale(uint32_t szw) {
 // SBF16: the scale bits are bfloat16 (else binary16); gshift: log2(group / 32), the slices
 // of one group (a group of 32, 64 or 128 inputs has its own scale/zero word)
 template <int MT, bool XF32, int SPT, int MAXT, bool RAGGED, bool SBF16, bool ONE = false>
-__global__ __launch_bounds__(MAXT) void gemv_kernel(const u32x4_t* __restrict__ wq,
+__global__ __launch_bounds__(MAXT, (MT == 1 && !XF32 && SPT == 1) ? 6 : 1) void gemv_kernel(const u32x4_t* __restrict__ wq,
                                                     const u32x4_t* __restrict__ sz4,
                                                     const void* __restrict__ xv,
                                                     void* __restrict__ yv, int y_bf16, int N,
@@ -215,18 +215,28 @@ __global__ __launch_bounds__(MAXT) void gemv_kernel(const u32x4_t* __restrict__ 
     u32x4_t sb[CH][SPT];
     // loads of the step (four rows) at local row rb into buffer c: the scale/zero words of
     // the four rows (one 16-byte load), then the rows' slices
+    // buffer loads: a uniform base per step (the step's first row, or its row quad's
+    // scale/zero words), the lane's fixed 32-bit offset, and the row within the step as the
+    // scalar offset, so a load needs no per-lane address arithmetic
     auto issue_step = [&](auto cc, int rb) {
         constexpr int c = decltype(cc)::value;
-        const int r = r0 + rb;
-        const char* srow = sbase + (int64_t)(min(r, N - 1) >> 2) * Kg * 16;
+        const int r = min(r0 + rb, N - 1);
+        const char* srow = sbase + (int64_t)(r >> 2) * Kg * 16;
+        const __amdgpu_buffer_rsrc_t srs =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(srow), 0, 0x7FFFFFFF, 0x00020000);
 #pragma unroll
-        for (int j = 0; j < SPT; ++j) sb[c][j] = *reinterpret_cast<const u32x4_t*>(srow + soff[j]);
+        for (int j = 0; j < SPT; ++j)
+            sb[c][j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(srs, (int)soff[j], 0, 0));
+        const char* rowp = wbase + (int64_t)r * row_bytes;
+        const __amdgpu_buffer_rsrc_t wrs =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(rowp), 0, 0x7FFFFFFF, 0x00020000);
 #pragma unroll
         for (int rr = 0; rr < R; ++rr) {
-            const char* rowp = wbase + (int64_t)min(r + rr, N - 1) * row_bytes;
+            // rows past N repeat row N-1 (their sums are never stored)
+            const int so = (min(r0 + rb + rr, N - 1) - r) * (int)row_bytes;
 #pragma unroll
             for (int j = 0; j < SPT; ++j)
-                wb[c][rr][j] = load_stream(reinterpret_cast<const u32x4_t*>(rowp + woff[j]));
+                wb[c][rr][j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wrs, (int)woff[j], so, 2));
         }
         // loads stay in step order, so a step only waits for its own loads
         __builtin_amdgcn_sched_barrier(0);
@@ -312,7 +322,7 @@ __global__ __launch_bounds__(MAXT) void gemv_kernel(const u32x4_t* __restrict__ 
             int fw = fmx[0][m];
 #pragma unroll
             for (int j = 1; j < SPT; ++j) fw = max(fw, fmx[j][m]);
-            fw = wave_max(fw);
+            fw = __builtin_amdgcn_readfirstlane(wave_max(fw));   // uniform: an SGPR
             xw[m] = fw - 127 - 15;
             const uint32_t ce = (uint32_t)((fw - 30) << 7) * 0x00010001u;
             const uint32_t co = (uint32_t)((fw - 26) << 7) * 0x00010001u;
@@ -558,7 +568,8 @@ int rows_for(Kern kernel, int block, int n, int mt, int chunk_rows, std::atomic<
 // Small matrices that fill less than one round of resident groups at the smallest chunk take
 // workgroups of one step (four rows), twice the waves per CU, when those still fit in one
 // round (measured on MI355X, 4096 x 4096 at M = 1: 4.4 against 4.9 us with bf16 x, 5.7
-// against 6.3 us with binary32 x)
+// against 6.3 us with binary32 x).  Only groups of up to four waves: the six-wave groups of
+// 4096 x 11008 ran 9.4 against 8.9 us with them.
 bool one_step_fits(int n, int rows, int chunk_rows, int resident) {
     const long slots = (long)resident * compute_units();
     return rows == chunk_rows && (n + rows - 1) / rows < slots && (n + kRowsPerStep - 1) / kRowsPerStep <= slots;
@@ -571,7 +582,8 @@ hipError_t launch_var(GemvArgs a, dim3 block, hipStream_t s) {
     auto kern = gemv_kernel<MT, XF32, SPT, MAXT, RAGGED, SBF16>;
     a.rows = rows_for(kern, (int)block.x, a.n, MT, CR, cache);
     if constexpr (MT == 1 && SPT == 1) {
-        if (one_step_fits(a.n, a.rows, CR, cache[block.x / 64].load(std::memory_order_relaxed))) {
+        if (block.x <= 256 &&
+            one_step_fits(a.n, a.rows, CR, cache[block.x / 64].load(std::memory_order_relaxed))) {
             const dim3 grid((unsigned)((a.n + kRowsPerStep - 1) / kRowsPerStep));
             const size_t shmem = (size_t)(block.x / 64) * kRowsPerStep * MT * sizeof(float);
             hipLaunchKernelGGL((gemv_kernel<MT, XF32, SPT, MAXT, RAGGED, SBF16, true>), grid, block, shmem, s,
