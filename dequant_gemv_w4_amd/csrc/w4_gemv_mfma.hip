@@ -359,8 +359,9 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(const uint8_t* __restric
 //   * The loads are buffer loads from a uniform base with fixed 32-bit lane offsets, so a
 //     load costs no address arithmetic; the next row step's loads of a group pair go out
 //     as soon as that pair of the current step has been used, so one set of registers
-//     holds the codes (x takes 128 of the 256).  The first row step instead goes through
-//     LDS with direct-to-LDS loads while x is converted, when the registers are busy.
+//     holds the codes (x takes 128 of the 256).  With more than eight rows of x the first
+//     row step instead goes through LDS with direct-to-LDS loads while x is converted, when
+//     the registers are busy.
 //   * A row step starts at row min(r0 + 16 t, N - 16): the last step of the last
 //     workgroup moves back into the matrix and stores only its new rows, so no load needs
 //     a per-lane bound.
@@ -373,7 +374,9 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(const uint8_t* __restric
 //   * A wave whose x converts exactly to binary16 with one power-of-two exponent per row
 //     of x (over the wave's groups) keeps binary16 x in its A operands and uses the exact
 //     binary16 codes with v_mfma_f32_16x16x32_f16: 9 instead of 17 vector instructions per
-//     eight codes, for about 1000 once per workgroup.
+//     eight codes, for about 1000 once per workgroup at 16 rows of x.  With up to eight rows
+//     each lane converts the bytes it staged (all 64 lanes hold rows of x) before the reads
+//     in MFMA order, a quarter (M <= 4) or half (M <= 8) of that work.
 constexpr int kXrGroups = 8;                        // groups per wave
 constexpr int kXrWaveLds = 17 * 1024;               // per wave: x staging (16 KB), then the
                                                     // first row step (8.5 KB) and E (64 B)
@@ -484,119 +487,234 @@ __global__ __launch_bounds__(512) void gemv_mfma_xr_kernel(const uint8_t* __rest
         c[2 * p] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)coff[0], 128 * p, 2));
         c[2 * p + 1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)coff[1], 128 * p, 2));
     };
-    // ---- x of this wave's groups (A operands), once per workgroup.  x goes through the
-    // wave's LDS area in two rounds of four groups, with loads of 4 rows x 256 contiguous
-    // bytes (chunk c of row r at slot c ^ (r & 15)); loading it straight into the MFMA lane
-    // order made each load touch 32 lines
-    u32x4_t xa[kXrGroups][4];
-    const int xquads = (M + 3) >> 2;   // quads of x rows loaded; rows past M are zero
-    const u32x4_t zero_x = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int gc = g0 + min(4 * half + q, ng - 1);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (i < xquads) {
-                    const int r = 4 * i + (lane >> 4);
-                    const uint16_t* src = x + (int64_t)min(r, M - 1) * K + gc * 128 + 8 * ((lane & 15) ^ (r & 15));
-                    lds_dma16(src, area + q * 4096 + i * 1024);
-                }
-            }
-        }
-        __builtin_amdgcn_s_waitcnt(vm_imm(0));
-        asm volatile("" ::: "memory");
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                xa[4 * half + q][s] = col < M ? *reinterpret_cast<const u32x4_t*>(
-                    area_p + q * 4096 + col * 256 + (((4 * kb + s) ^ col) * 16)) : zero_x;
-        // the reads have returned before the next loads overwrite the area
-        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-        asm volatile("" ::: "memory");
-    }
-    // the first row step goes through the (now free) LDS area by direct-to-LDS loads (lane
-    // l's bytes at 16 l), so that no registers are held for it during the x conversion
-    {
-        const int rb = step_row(0);
-        const uint32_t* sq = sz + (int64_t)(rb >> 2) * Kg * 4;
-        const int rr = (rb & 3) + col;
-        const uint32_t o = (uint32_t)((rr >> 2) * Kg * 4 + (rr & 3));
-        lds_dma4(sq + o + 4 * sg0, area + 8 * 1024);
-        lds_dma4(sq + o + 4 * g0 + 4 * min(4 + kb, ng - 1), area + 8 * 1024 + 256);
-        const uint8_t* cb = code_base(0);
-#pragma unroll
-        for (int d = 0; d < 8; ++d) lds_dma16(cb + 128 * (d >> 1) + coff[d & 1], area + d * 1024);
-    }
-
+    // ---- x of this wave's groups (A operands), once per workgroup, and the first row step.
+    // x goes through the wave's LDS area in two rounds of four groups, with loads of 4 rows x
+    // 256 contiguous bytes (chunk c of row r at slot c ^ (r & 15)); loading it straight into
+    // the MFMA lane order made each load touch 32 lines.  Only ceil(M/4) quads of rows are
+    // loaded; the lanes of rows past them hold zeros.
+    //
     // binary16 x: x * 2^-E per row of x, E putting the largest value of the row over this
     // wave's groups just under 2^16; exact when every non-zero value lands on a normal
     // binary16 (within 2^25 of the largest, also after the further 2^-4 at the inputs of the
     // 16 (q - zero) codes).  The codes then need no bf16 conversion.  A wave whose rows do
-    // not all pass keeps bf16 x.
+    // not all pass keeps bf16 x.  E of each row goes to LDS for the threads that combine the
+    // waves' partial sums (they scale each wave's sums by its 2^E; the first barrier orders
+    // these writes).
+    const int xquads = (M + 3) >> 2;
+    const u32x4_t zero_x = {0u, 0u, 0u, 0u};
+    u32x4_t xa[kXrGroups][4];
+    u32x4_t c[8];      // codes of the current row step
+    uint32_t s[2];     // its scale/zero words
     bool f16 = false;
-    int e_row = 0;   // E of x row col (0 for bf16 x)
-    {
-        u16x2_t vmax = {0, 0}, vmin = {0xFFFF, 0xFFFF};
-        // (scheduling barriers per group keep the compiler from spreading the work over many
-        // temporaries beside the 128 registers of x)
+    if (xquads <= 2) {
+        // up to eight rows of x: each lane converts the 16 bytes it loaded (row 4i + (lane >> 4)
+        // of quad i), where all 64 lanes hold rows of x, and writes them back for the reads
+        // in MFMA lane order (at M = 4 a quarter of the work of converting the MFMA operands;
+        // qkv 16.7 -> 14.3 us, gate_up 47.3 -> 45.3).  The first row step's loads go straight
+        // into registers, in flight while x is converted.
+        u32x4_t raw[kXrGroups][2];
 #pragma unroll
-        for (int j = 0; j < kXrGroups; ++j) {
+        for (int half = 0; half < 2; ++half) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int gc = g0 + min(4 * half + q, ng - 1);
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    if (i < xquads) {
+                        const int r = 4 * i + (lane >> 4);
+                        const uint16_t* src = x + (int64_t)min(r, M - 1) * K + gc * 128 + 8 * ((lane & 15) ^ (r & 15));
+                        lds_dma16(src, area + q * 4096 + i * 1024);
+                    }
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(vm_imm(0));
+            asm volatile("" ::: "memory");
 #pragma unroll
             for (int q = 0; q < 4; ++q)
 #pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    const u16x2_t mag = as_u16x2(xa[j][q][d] & 0x7FFF7FFFu);
-                    vmax = __builtin_elementwise_max(vmax, mag);
-                    vmin = __builtin_elementwise_min(vmin, mag - (unsigned short)1);
-                }
-            __builtin_amdgcn_sched_barrier(0);
+                for (int i = 0; i < 2; ++i)
+                    if (i < xquads)
+                        raw[4 * half + q][i] = *reinterpret_cast<const u32x4_t*>(area_p + q * 4096 + i * 1024 + 16 * lane);
+            // the reads have returned before the next loads overwrite the area
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+            asm volatile("" ::: "memory");
         }
-        const int fmax = (int)(max_across_rows(max(vmax.x, vmax.y)) >> 7);
-        const int mnz = 0xFFFF - (int)max_across_rows(0xFFFFu - min(vmin.x, vmin.y)) + 1;
-        const bool bad = mnz != 0x10000 && (fmax < 30 || fmax == 255 || mnz < ((fmax - 25) << 7));
-        f16 = __builtin_amdgcn_ballot_w64(bad) == 0;
-        if (f16) {
-            // x passes through an empty asm statement so that the conversion recomputes the
-            // magnitudes instead of keeping the 128 from the range check alive
+        {
+            load_sz(0, s);
+            const uint8_t* cb = code_base(0);
 #pragma unroll
-            for (int j = 0; j < kXrGroups; ++j)
+            for (int p = 0; p < 4; ++p) load_pair(cb, p, c);
+        }
+
+        int fq[2] = {0, 0};   // largest bf16 exponent field of row 4i + (lane >> 4)
+        {
+            bool bad = false;
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
+            for (int i = 0; i < 2; ++i) {
+                if (i < xquads) {
+                    u16x2_t vmax = {0, 0}, vmin = {0xFFFF, 0xFFFF};
 #pragma unroll
-                    for (int d = 0; d < 4; ++d) {
-                        uint32_t v = xa[j][q][d];
-                        asm volatile("" : "+v"(v));
-                        xa[j][q][d] = v;
+                    for (int j = 0; j < kXrGroups; ++j)
+#pragma unroll
+                        for (int d = 0; d < 4; ++d) {
+                            const u16x2_t mag = as_u16x2(raw[j][i][d] & 0x7FFF7FFFu);
+                            vmax = __builtin_elementwise_max(vmax, mag);
+                            vmin = __builtin_elementwise_min(vmin, mag - (unsigned short)1);  // 0 -> 0xFFFF
+                        }
+                    // over the 16 lanes of the row (one 16-lane row of the wave)
+                    uint32_t mx = max(vmax.x, vmax.y), mn = min(vmin.x, vmin.y);
+                    mx = max(mx, ror8(mx));
+                    mn = min(mn, ror8(mn));
+                    mx = max(mx, (uint32_t)__builtin_amdgcn_mov_dpp((int)mx, 0x124, 0xF, 0xF, false));
+                    mn = min(mn, (uint32_t)__builtin_amdgcn_mov_dpp((int)mn, 0x124, 0xF, 0xF, false));
+                    mx = max(mx, (uint32_t)__builtin_amdgcn_mov_dpp((int)mx, 0x122, 0xF, 0xF, false));
+                    mn = min(mn, (uint32_t)__builtin_amdgcn_mov_dpp((int)mn, 0x122, 0xF, 0xF, false));
+                    mx = max(mx, (uint32_t)__builtin_amdgcn_mov_dpp((int)mx, 0x121, 0xF, 0xF, false));
+                    mn = min(mn, (uint32_t)__builtin_amdgcn_mov_dpp((int)mn, 0x121, 0xF, 0xF, false));
+                    const int fmax = (int)(mx >> 7);
+                    const int mnz = (int)mn + 1;
+                    bad |= mnz != 0x10000 && (fmax < 30 || fmax == 255 || mnz < ((fmax - 25) << 7));
+                    fq[i] = fmax;
+                }
+            }
+            f16 = __builtin_amdgcn_ballot_w64(bad) == 0;
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            if (i < xquads && (lane & 15) == 0)
+                *reinterpret_cast<int*>(smem + wave * kXrWaveLds + kXrEOffset + 4 * (4 * i + (lane >> 4))) =
+                    f16 ? fq[i] - 127 - 15 : 0;
+        // back to LDS (converted or not), then the A operands in MFMA lane order
+#pragma unroll
+        for (int half = 1; half >= 0; --half) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    if (i < xquads) {
+                        if (f16) {
+                            const uint32_t ce = (uint32_t)((fq[i] - 30) << 7) * 0x00010001u;
+                            const uint32_t co = (uint32_t)((fq[i] - 26) << 7) * 0x00010001u;
+#pragma unroll
+                            for (int d = 0; d < 4; ++d)
+                                raw[4 * half + q][i][d] = to_f16_pair(raw[4 * half + q][i][d], (d & 1) ? co : ce);
+                        }
+                        *reinterpret_cast<u32x4_t*>(smem + wave * kXrWaveLds + q * 4096 + i * 1024 + 16 * lane) =
+                            raw[4 * half + q][i];
                     }
-            const uint32_t ce = (uint32_t)((fmax - 30) << 7) * 0x00010001u;
-            const uint32_t co = (uint32_t)((fmax - 26) << 7) * 0x00010001u;
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the writes have landed
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int sq = 0; sq < 4; ++sq)
+                    xa[4 * half + q][sq] = col < 4 * xquads ? *reinterpret_cast<const u32x4_t*>(
+                        area_p + q * 4096 + col * 256 + (((4 * kb + sq) ^ col) * 16)) : zero_x;
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): read before the next writes
+            asm volatile("" ::: "memory");
+        }
+    } else {
+        // more rows of x: the MFMA operands are converted in place; the first row step goes
+        // through the LDS area by direct-to-LDS loads (lane l's bytes at 16 l) while x is
+        // converted, when the registers are busy
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int gc = g0 + min(4 * half + q, ng - 1);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (i < xquads) {
+                        const int r = 4 * i + (lane >> 4);
+                        const uint16_t* src = x + (int64_t)min(r, M - 1) * K + gc * 128 + 8 * ((lane & 15) ^ (r & 15));
+                        lds_dma16(src, area + q * 4096 + i * 1024);
+                    }
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(vm_imm(0));
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    xa[4 * half + q][s] = col < M ? *reinterpret_cast<const u32x4_t*>(
+                        area_p + q * 4096 + col * 256 + (((4 * kb + s) ^ col) * 16)) : zero_x;
+            // the reads have returned before the next loads overwrite the area
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+            asm volatile("" ::: "memory");
+        }
+        // the first row step goes through the (now free) LDS area by direct-to-LDS loads (lane
+        // l's bytes at 16 l), so that no registers are held for it during the x conversion
+        {
+            const int rb = step_row(0);
+            const uint32_t* sq = sz + (int64_t)(rb >> 2) * Kg * 4;
+            const int rr = (rb & 3) + col;
+            const uint32_t o = (uint32_t)((rr >> 2) * Kg * 4 + (rr & 3));
+            lds_dma4(sq + o + 4 * sg0, area + 8 * 1024);
+            lds_dma4(sq + o + 4 * g0 + 4 * min(4 + kb, ng - 1), area + 8 * 1024 + 256);
+            const uint8_t* cb = code_base(0);
+#pragma unroll
+            for (int d = 0; d < 8; ++d) lds_dma16(cb + 128 * (d >> 1) + coff[d & 1], area + d * 1024);
+        }
+
+        int e_row = 0;   // E of x row col (0 for bf16 x)
+        {
+            u16x2_t vmax = {0, 0}, vmin = {0xFFFF, 0xFFFF};
+            // (scheduling barriers per group keep the compiler from spreading the work over many
+            // temporaries beside the 128 registers of x)
 #pragma unroll
             for (int j = 0; j < kXrGroups; ++j) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
 #pragma unroll
-                    for (int d = 0; d < 4; ++d) xa[j][q][d] = to_f16_pair(xa[j][q][d], (d & 1) ? co : ce);
+                    for (int d = 0; d < 4; ++d) {
+                        const u16x2_t mag = as_u16x2(xa[j][q][d] & 0x7FFF7FFFu);
+                        vmax = __builtin_elementwise_max(vmax, mag);
+                        vmin = __builtin_elementwise_min(vmin, mag - (unsigned short)1);
+                    }
                 __builtin_amdgcn_sched_barrier(0);
             }
-            e_row = fmax - 127 - 15;
-        }
-    }
-    // E of each row of x, for the threads that combine the waves' partial sums (they scale
-    // each wave's sums by its 2^E; the first barrier orders these writes)
-    if (kb == 0) *reinterpret_cast<int*>(smem + wave * kXrWaveLds + kXrEOffset + 4 * col) = e_row;
-
-    // codes (c) and scale/zero words (s) of the current row step
-    u32x4_t c[8];
-    uint32_t s[2];
-    __builtin_amdgcn_s_waitcnt(vm_imm(0));
-    asm volatile("" ::: "memory");
+            const int fmax = (int)(max_across_rows(max(vmax.x, vmax.y)) >> 7);
+            const int mnz = 0xFFFF - (int)max_across_rows(0xFFFFu - min(vmin.x, vmin.y)) + 1;
+            const bool bad = mnz != 0x10000 && (fmax < 30 || fmax == 255 || mnz < ((fmax - 25) << 7));
+            f16 = __builtin_amdgcn_ballot_w64(bad) == 0;
+            if (f16) {
+                // x passes through an empty asm statement so that the conversion recomputes the
+                // magnitudes instead of keeping the 128 from the range check alive
 #pragma unroll
-    for (int d = 0; d < 8; ++d) c[d] = *reinterpret_cast<const u32x4_t*>(area_p + d * 1024 + 16 * lane);
-    s[0] = *reinterpret_cast<const uint32_t*>(area_p + 8 * 1024 + 4 * lane);
-    s[1] = *reinterpret_cast<const uint32_t*>(area_p + 8 * 1024 + 256 + 4 * lane);
+                for (int j = 0; j < kXrGroups; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+#pragma unroll
+                        for (int d = 0; d < 4; ++d) {
+                            uint32_t v = xa[j][q][d];
+                            asm volatile("" : "+v"(v));
+                            xa[j][q][d] = v;
+                        }
+                const uint32_t ce = (uint32_t)((fmax - 30) << 7) * 0x00010001u;
+                const uint32_t co = (uint32_t)((fmax - 26) << 7) * 0x00010001u;
+#pragma unroll
+                for (int j = 0; j < kXrGroups; ++j) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+#pragma unroll
+                        for (int d = 0; d < 4; ++d) xa[j][q][d] = to_f16_pair(xa[j][q][d], (d & 1) ? co : ce);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                e_row = fmax - 127 - 15;
+            }
+        }
+        if (kb == 0) *reinterpret_cast<int*>(smem + wave * kXrWaveLds + kXrEOffset + 4 * col) = e_row;
+
+        __builtin_amdgcn_s_waitcnt(vm_imm(0));
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int d = 0; d < 8; ++d) c[d] = *reinterpret_cast<const u32x4_t*>(area_p + d * 1024 + 16 * lane);
+        s[0] = *reinterpret_cast<const uint32_t*>(area_p + 8 * 1024 + 4 * lane);
+        s[1] = *reinterpret_cast<const uint32_t*>(area_p + 8 * 1024 + 256 + 4 * lane);
+    }
 
     // one row step; F: binary16 x and codes (else bf16), MORE: the next row step's loads are
     // issued here, group pair by group pair as the registers of a pair are used.  Both are
