@@ -121,6 +121,26 @@ def test_resident_x_binary16_some_waves_fall_back():
     print(f"resident-x mixed: worst err/bound {worst:.3e}")
 
 
+@pytest.mark.parametrize("m", [3, 5, 8])
+def test_resident_x_few_rows_ragged_groups_and_a_wide_wave(m):
+    """The resident-x kernel with up to eight rows of x (x converted where it was staged) on
+    12300 x 1152: two waves of five and four groups (slots past a wave's groups read the next
+    bytes), a last workgroup of 12 rows (its one row step starts 4 rows back, in the previous
+    workgroup's rows, and stores only its own), and x wide in the second wave's inputs only,
+    so one wave keeps bf16 x; every output against the oracle."""
+    n, k = 12300, 1152
+    rng = np.random.default_rng(90 + m)
+    w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
+    prep, ref = _quant_prepare(w)
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    x[:, 640:] = synth.wide_range_activations(m, k - 640, seed=91 + m)
+    xb = torch.from_numpy(x).to(DEV).to(torch.bfloat16).contiguous()
+    r = _check_gemv(prep, ref, n, k, xb, f"resident-x few rows M={m}")
+    xn = torch.from_numpy(rng.standard_normal((m, k)).astype(np.float32)).to(DEV).to(torch.bfloat16)
+    r = max(r, _check_gemv(prep, ref, n, k, xn.contiguous(), f"resident-x few rows plain M={m}"))
+    print(f"M={m}: worst err/bound {r:.3e}")
+
+
 @pytest.mark.parametrize("m", [4, 5, 7, 13, 16])
 def test_resident_x_binary16_ragged_rows(m):
     """The resident-x kernel's binary16 path with a ragged last workgroup (24616 rows: 220
