@@ -238,6 +238,54 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(const uint8_t* __restric
 #pragma unroll
     for (int t = 0; t < T; ++t) acc[t] = zero4;
 
+    // binary16 x for up to four rows of x: x * 2^-E per row of x, E putting the row's
+    // largest value over this wave's groups just under 2^16 (a pass over those groups of x,
+    // lane l reading row l >> 4, chunk l & 15), exact when every non-zero value lands on a
+    // normal binary16 (within 2^25 of the largest, also after the further 2^-4 at the inputs
+    // of the 16 (q - zero) codes).  Each group pair's staged x is then converted where it
+    // landed, all 64 lanes holding rows of x, and the codes need no bf16 conversion (9
+    // instead of 17 vector instructions per eight codes).  A wave whose rows do not all pass
+    // keeps bf16 x.  Measured on MI355X (70B down 8192 x 28672 at M = 4: 32.3 -> 29.9 us);
+    // with eight rows the pass and the conversion cost more than the codes save (33.6 -> 37.6).
+    bool f16 = false;
+    int fq = 0;   // largest bf16 exponent field of row lane >> 4
+    if (xquads == 1 && g0 < g1) {
+        const uint16_t* xr = x + (int64_t)min(lane >> 4, M - 1) * K + 8 * (lane & 15);
+        u16x2_t vmax = {0, 0}, vmin = {0xFFFF, 0xFFFF};
+        // batches of 16 groups: every load of a batch is in flight before any is used
+        for (int gb = g0; gb < g1; gb += 16) {
+            u32x4_t v[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                v[u] = *reinterpret_cast<const u32x4_t*>(xr + (int64_t)min(gb + u, g1 - 1) * 128);
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const u16x2_t mag = as_u16x2(v[u][d] & 0x7FFF7FFFu);
+                    vmax = __builtin_elementwise_max(vmax, mag);
+                    vmin = __builtin_elementwise_min(vmin, mag - (unsigned short)1);  // 0 -> 0xFFFF
+                }
+        }
+        // over the 16 lanes of the row (one 16-lane row of the wave)
+        uint32_t mx = max(vmax.x, vmax.y), mn = min(vmin.x, vmin.y);
+        mx = max(mx, (uint32_t)__builtin_amdgcn_mov_dpp((int)mx, 0x128, 0xF, 0xF, false));
+        mn = min(mn, (uint32_t)__builtin_amdgcn_mov_dpp((int)mn, 0x128, 0xF, 0xF, false));
+        mx = max(mx, (uint32_t)__builtin_amdgcn_mov_dpp((int)mx, 0x124, 0xF, 0xF, false));
+        mn = min(mn, (uint32_t)__builtin_amdgcn_mov_dpp((int)mn, 0x124, 0xF, 0xF, false));
+        mx = max(mx, (uint32_t)__builtin_amdgcn_mov_dpp((int)mx, 0x122, 0xF, 0xF, false));
+        mn = min(mn, (uint32_t)__builtin_amdgcn_mov_dpp((int)mn, 0x122, 0xF, 0xF, false));
+        mx = max(mx, (uint32_t)__builtin_amdgcn_mov_dpp((int)mx, 0x121, 0xF, 0xF, false));
+        mn = min(mn, (uint32_t)__builtin_amdgcn_mov_dpp((int)mn, 0x121, 0xF, 0xF, false));
+        fq = (int)(mx >> 7);
+        const int mnz = (int)mn + 1;
+        const bool bad = mnz != 0x10000 && (fq < 30 || fq == 255 || mnz < ((fq - 25) << 7));
+        f16 = __builtin_amdgcn_ballot_w64(bad) == 0;
+    }
+    const uint32_t xce = (uint32_t)((fq - 30) << 7) * 0x00010001u;   // conversion constants
+    const uint32_t xco = (uint32_t)((fq - 26) << 7) * 0x00010001u;
+    uint8_t* xstage_w = smem + wave * kWaveBytes;
+
     uint32_t sb[2][CH][T];
     // loads of the pair g, g+1 (a group past the wave's range repeats its last group: a cache
     // hit that contributes nothing): codes, scale/zero words, x
@@ -260,11 +308,25 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(const uint8_t* __restric
         }
         __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the compute
     };
-    auto step = [&](auto bc, int g) {
+    auto step = [&](auto fc, auto bc, int g) {
+        constexpr bool F = decltype(fc)::value;
         constexpr int b = decltype(bc)::value;
         // every load of this pair has landed (the next pair's are not issued yet)
         __builtin_amdgcn_s_waitcnt(0x0F70);
         asm volatile("" ::: "memory");
+        if constexpr (F) {
+            // binary16 x: each lane converts the 16 bytes it staged (row lane >> 4), in place
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+                u32x4_t* slot = reinterpret_cast<u32x4_t*>(xstage_w + c * kXStageBytes + 16 * lane);
+                u32x4_t v = *slot;
+#pragma unroll
+                for (int d = 0; d < 4; ++d) v[d] = to_f16_pair(v[d], (d & 1) ? xco : xce);
+                *slot = v;
+            }
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+            asm volatile("" ::: "memory");
+        }
         u32x4_t xb[CH][4];
         u32x4_t wb[CH][T];
 #pragma unroll
@@ -293,10 +355,17 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(const uint8_t* __restric
                 const uint32_t szw = sb[b][c][t];
                 const uint32_t z1 = cc.z1(szw), z16 = cc.z16(szw);
                 f32x4_t p = zero4;
+                if constexpr (F) {
 #pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        as_bf16x8(xb[c][s]), as_bf16x8(exact_codes(wb[c][t][s], z1, z16, cc)), p, 0, 0, 0);
+                    for (int s = 0; s < 4; ++s)
+                        p = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            as_f16x8(xb[c][s]), as_f16x8(exact_codes_f16(wb[c][t][s], z1, z16, cc)), p, 0, 0, 0);
+                } else {
+#pragma unroll
+                    for (int s = 0; s < 4; ++s)
+                        p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            as_bf16x8(xb[c][s]), as_bf16x8(exact_codes(wb[c][t][s], z1, z16, cc)), p, 0, 0, 0);
+                }
                 const float sc =
                     keep * (float)__builtin_bit_cast(_Float16, (uint16_t)(szw & 0xFFFFu));
 #pragma unroll
@@ -307,15 +376,29 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(const uint8_t* __restric
     };
 
     // (a wave without groups skips the loop; the host sizes the grid so that none is)
-    if (g0 < g1) {
+    auto run = [&](auto fc) {
         issue(std::integral_constant<int, 0>{}, g0);
         for (int g = g0; g < g1; g += 2 * CH) {
-            step(std::integral_constant<int, 0>{}, g);
+            step(fc, std::integral_constant<int, 0>{}, g);
             if (g + CH >= g1) break;
-            step(std::integral_constant<int, 1>{}, g + CH);
+            step(fc, std::integral_constant<int, 1>{}, g + CH);
         }
+    };
+    if (g0 < g1) {
+        if (f16)
+            run(std::integral_constant<bool, true>{});
+        else
+            run(std::integral_constant<bool, false>{});
     }
 
+    // 2^E of the rows m = 4 kb + v this lane accumulates (binary16 x has at most four rows:
+    // row m's exponent sits in lanes 16 m .. 16 m + 15)
+    int ev[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int a0 = __shfl(fq, 16 * v);   // rows past the fourth are never stored here
+        ev[v] = f16 ? a0 - 127 - 15 : 0;
+    }
     __syncthreads();   // every wave is done with its stages: the LDS now takes the sums
     // partial sums of this wave: lane holds column n = col, rows m = 4*kb + v
 #pragma unroll
@@ -323,7 +406,7 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(const uint8_t* __restric
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const int m = 4 * kb + v;
-            if (m < M) red[(wave * RW + 16 * t + col) * kRedStride + m] = acc[t][v];
+            if (m < M) red[(wave * RW + 16 * t + col) * kRedStride + m] = ldexpf(acc[t][v], ev[v]);
         }
     __syncthreads();
 

@@ -141,6 +141,23 @@ def test_resident_x_few_rows_ragged_groups_and_a_wide_wave(m):
     print(f"M={m}: worst err/bound {r:.3e}")
 
 
+@pytest.mark.parametrize("m", [3, 4])
+def test_streaming_binary16_x_one_wave_falls_back(m):
+    """The streaming kernel with up to four rows of x (binary16 x, converted where it was
+    staged) on 520 x 9216: eight waves of nine groups (an odd count: the last pair's second
+    group lies past the wave's range), x wide only in the first wave's 1152 inputs, so that
+    wave keeps bf16 x; every output against the oracle."""
+    n, k = SHAPES["stream"]
+    rng = np.random.default_rng(80 + m)
+    w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
+    prep, ref = _quant_prepare(w)
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    x[:, :1152] = synth.wide_range_activations(m, 1152, seed=81 + m)
+    xb = torch.from_numpy(x).to(DEV).to(torch.bfloat16).contiguous()
+    r = _check_gemv(prep, ref, n, k, xb, f"streaming one wide wave M={m}")
+    print(f"M={m}: worst err/bound {r:.3e}")
+
+
 @pytest.mark.parametrize("m", [4, 5, 7, 13, 16])
 def test_resident_x_binary16_ragged_rows(m):
     """The resident-x kernel's binary16 path with a ragged last workgroup (24616 rows: 220
