@@ -454,8 +454,8 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(const uint8_t* __restric
 //     barrier per step), scaled there by each wave's 2^E.
 //   * A row step is compiled per activation format and per whether it issues the next
 //     step's loads, so its eight groups are straight-line code.
-//   * A wave whose x converts exactly to binary16 with one power-of-two exponent per row
-//     of x (over the wave's groups) keeps binary16 x in its A operands and uses the exact
+//   * A wave whose x converts exactly to binary16 with one power-of-two exponent (over
+//     its groups and all rows of x) keeps binary16 x in its A operands and uses the exact
 //     binary16 codes with v_mfma_f32_16x16x32_f16: 9 instead of 17 vector instructions per
 //     eight codes, for about 1000 once per workgroup at 16 rows of x.  With up to eight rows
 //     each lane converts the bytes it staged (all 64 lanes hold rows of x) before the reads
@@ -463,7 +463,6 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(const uint8_t* __restric
 constexpr int kXrGroups = 8;                        // groups per wave
 constexpr int kXrWaveLds = 17 * 1024;               // per wave: x staging (16 KB), then the
                                                     // first row step (8.5 KB) and E (64 B)
-constexpr int kXrEOffset = 16 * 1024;               // E of the 16 rows of x, in the wave's area
 constexpr int kXrRedBytes = 2 * 16 * kRedStride * 4;   // per wave: two row steps
 
 __device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_addr) {
@@ -576,19 +575,21 @@ __global__ __launch_bounds__(512) void gemv_mfma_xr_kernel(const uint8_t* __rest
     // the MFMA lane order made each load touch 32 lines.  Only ceil(M/4) quads of rows are
     // loaded; the lanes of rows past them hold zeros.
     //
-    // binary16 x: x * 2^-E per row of x, E putting the largest value of the row over this
-    // wave's groups just under 2^16; exact when every non-zero value lands on a normal
-    // binary16 (within 2^25 of the largest, also after the further 2^-4 at the inputs of the
-    // 16 (q - zero) codes).  The codes then need no bf16 conversion.  A wave whose rows do
-    // not all pass keeps bf16 x.  E of each row goes to LDS for the threads that combine the
-    // waves' partial sums (they scale each wave's sums by its 2^E; the first barrier orders
-    // these writes).
+    // binary16 x: x * 2^-E, one E per wave putting the largest value of its x (all rows, its
+    // groups) just under 2^16; exact when every non-zero value lands on a normal binary16
+    // (within 2^25 of the largest, also after the further 2^-4 at the inputs of the 16 (q -
+    // zero) codes).  The codes then need no bf16 conversion.  A wave whose x does not pass
+    // keeps bf16 x.  Each wave scales its partial sums by 2^E (a scalar) before they are
+    // combined, so the combine is a plain sum (with an exponent per row of x, reading the
+    // exponents there cost qkv 0.5-0.7 us at M = 4 and 8).  Scaling by a power of two
+    // commutes with the roundings, so the results are those of one exponent per row.
     const int xquads = (M + 3) >> 2;
     const u32x4_t zero_x = {0u, 0u, 0u, 0u};
     u32x4_t xa[kXrGroups][4];
     u32x4_t c[8];      // codes of the current row step
     uint32_t s[2];     // its scale/zero words
     bool f16 = false;
+    int fw = 0;        // the wave's largest bf16 exponent field over its x (uniform)
     if (xquads <= 2) {
         // up to eight rows of x: each lane converts the 16 bytes it loaded (row 4i + (lane >> 4)
         // of quad i), where all 64 lanes hold rows of x, and writes them back for the reads
@@ -629,9 +630,8 @@ __global__ __launch_bounds__(512) void gemv_mfma_xr_kernel(const uint8_t* __rest
             for (int p = 0; p < 4; ++p) load_pair(cb, p, c);
         }
 
-        int fq[2] = {0, 0};   // largest bf16 exponent field of row 4i + (lane >> 4)
         {
-            bool bad = false;
+            uint32_t mxq[2] = {0, 0}, mnq[2] = {0xFFFFu, 0xFFFFu};   // per row, over its 16 lanes
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 if (i < xquads) {
@@ -644,7 +644,6 @@ __global__ __launch_bounds__(512) void gemv_mfma_xr_kernel(const uint8_t* __rest
                             vmax = __builtin_elementwise_max(vmax, mag);
                             vmin = __builtin_elementwise_min(vmin, mag - (unsigned short)1);  // 0 -> 0xFFFF
                         }
-                    // over the 16 lanes of the row (one 16-lane row of the wave)
                     uint32_t mx = max(vmax.x, vmax.y), mn = min(vmin.x, vmin.y);
                     mx = max(mx, ror8(mx));
                     mn = min(mn, ror8(mn));
@@ -654,19 +653,20 @@ __global__ __launch_bounds__(512) void gemv_mfma_xr_kernel(const uint8_t* __rest
                     mn = min(mn, (uint32_t)__builtin_amdgcn_mov_dpp((int)mn, 0x122, 0xF, 0xF, false));
                     mx = max(mx, (uint32_t)__builtin_amdgcn_mov_dpp((int)mx, 0x121, 0xF, 0xF, false));
                     mn = min(mn, (uint32_t)__builtin_amdgcn_mov_dpp((int)mn, 0x121, 0xF, 0xF, false));
-                    const int fmax = (int)(mx >> 7);
-                    const int mnz = (int)mn + 1;
-                    bad |= mnz != 0x10000 && (fmax < 30 || fmax == 255 || mnz < ((fmax - 25) << 7));
-                    fq[i] = fmax;
+                    mxq[i] = mx;
+                    mnq[i] = mn;
                 }
+            }
+            // one exponent for the wave: its largest value over all rows of x
+            fw = __builtin_amdgcn_readfirstlane((int)(max_across_rows(max(mxq[0], mxq[1])) >> 7));
+            bool bad = false;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int mnz = (int)mnq[i] + 1;
+                bad |= mnz != 0x10000 && (fw < 30 || fw == 255 || mnz < ((fw - 25) << 7));
             }
             f16 = __builtin_amdgcn_ballot_w64(bad) == 0;
         }
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-            if (i < xquads && (lane & 15) == 0)
-                *reinterpret_cast<int*>(smem + wave * kXrWaveLds + kXrEOffset + 4 * (4 * i + (lane >> 4))) =
-                    f16 ? fq[i] - 127 - 15 : 0;
         // back to LDS (converted or not), then the A operands in MFMA lane order
 #pragma unroll
         for (int half = 1; half >= 0; --half) {
@@ -676,8 +676,8 @@ __global__ __launch_bounds__(512) void gemv_mfma_xr_kernel(const uint8_t* __rest
                 for (int i = 0; i < 2; ++i) {
                     if (i < xquads) {
                         if (f16) {
-                            const uint32_t ce = (uint32_t)((fq[i] - 30) << 7) * 0x00010001u;
-                            const uint32_t co = (uint32_t)((fq[i] - 26) << 7) * 0x00010001u;
+                            const uint32_t ce = (uint32_t)((fw - 30) << 7) * 0x00010001u;
+                            const uint32_t co = (uint32_t)((fw - 26) << 7) * 0x00010001u;
 #pragma unroll
                             for (int d = 0; d < 4; ++d)
                                 raw[4 * half + q][i][d] = to_f16_pair(raw[4 * half + q][i][d], (d & 1) ? co : ce);
@@ -742,7 +742,6 @@ __global__ __launch_bounds__(512) void gemv_mfma_xr_kernel(const uint8_t* __rest
             for (int d = 0; d < 8; ++d) lds_dma16(cb + 128 * (d >> 1) + coff[d & 1], area + d * 1024);
         }
 
-        int e_row = 0;   // E of x row col (0 for bf16 x)
         {
             u16x2_t vmax = {0, 0}, vmin = {0xFFFF, 0xFFFF};
             // (scheduling barriers per group keep the compiler from spreading the work over many
@@ -759,10 +758,21 @@ __global__ __launch_bounds__(512) void gemv_mfma_xr_kernel(const uint8_t* __rest
                     }
                 __builtin_amdgcn_sched_barrier(0);
             }
-            const int fmax = (int)(max_across_rows(max(vmax.x, vmax.y)) >> 7);
-            const int mnz = 0xFFFF - (int)max_across_rows(0xFFFFu - min(vmin.x, vmin.y)) + 1;
-            const bool bad = mnz != 0x10000 && (fmax < 30 || fmax == 255 || mnz < ((fmax - 25) << 7));
-            f16 = __builtin_amdgcn_ballot_w64(bad) == 0;
+            // one exponent for the wave: its largest value over all rows of x (the lanes of a
+            // 16-lane row hold the 16 rows of x, the four 16-lane rows the same rows)
+            uint32_t mx = max_across_rows(max(vmax.x, vmax.y));
+            uint32_t mn = 0xFFFFu - max_across_rows(0xFFFFu - min(vmin.x, vmin.y));
+            mx = max(mx, ror8(mx));
+            mn = min(mn, ror8(mn));
+            mx = max(mx, (uint32_t)__builtin_amdgcn_mov_dpp((int)mx, 0x124, 0xF, 0xF, false));
+            mn = min(mn, (uint32_t)__builtin_amdgcn_mov_dpp((int)mn, 0x124, 0xF, 0xF, false));
+            mx = max(mx, (uint32_t)__builtin_amdgcn_mov_dpp((int)mx, 0x122, 0xF, 0xF, false));
+            mn = min(mn, (uint32_t)__builtin_amdgcn_mov_dpp((int)mn, 0x122, 0xF, 0xF, false));
+            mx = max(mx, (uint32_t)__builtin_amdgcn_mov_dpp((int)mx, 0x121, 0xF, 0xF, false));
+            mn = min(mn, (uint32_t)__builtin_amdgcn_mov_dpp((int)mn, 0x121, 0xF, 0xF, false));
+            fw = __builtin_amdgcn_readfirstlane((int)(mx >> 7));
+            const int mnz = __builtin_amdgcn_readfirstlane((int)mn) + 1;
+            f16 = !(mnz != 0x10000 && (fw < 30 || fw == 255 || mnz < ((fw - 25) << 7)));
             if (f16) {
                 // x passes through an empty asm statement so that the conversion recomputes the
                 // magnitudes instead of keeping the 128 from the range check alive
@@ -776,8 +786,8 @@ __global__ __launch_bounds__(512) void gemv_mfma_xr_kernel(const uint8_t* __rest
                             asm volatile("" : "+v"(v));
                             xa[j][q][d] = v;
                         }
-                const uint32_t ce = (uint32_t)((fmax - 30) << 7) * 0x00010001u;
-                const uint32_t co = (uint32_t)((fmax - 26) << 7) * 0x00010001u;
+                const uint32_t ce = (uint32_t)((fw - 30) << 7) * 0x00010001u;
+                const uint32_t co = (uint32_t)((fw - 26) << 7) * 0x00010001u;
 #pragma unroll
                 for (int j = 0; j < kXrGroups; ++j) {
 #pragma unroll
@@ -786,10 +796,8 @@ __global__ __launch_bounds__(512) void gemv_mfma_xr_kernel(const uint8_t* __rest
                         for (int d = 0; d < 4; ++d) xa[j][q][d] = to_f16_pair(xa[j][q][d], (d & 1) ? co : ce);
                     __builtin_amdgcn_sched_barrier(0);
                 }
-                e_row = fmax - 127 - 15;
             }
         }
-        if (kb == 0) *reinterpret_cast<int*>(smem + wave * kXrWaveLds + kXrEOffset + 4 * col) = e_row;
 
         __builtin_amdgcn_s_waitcnt(vm_imm(0));
         asm volatile("" ::: "memory");
@@ -798,6 +806,8 @@ __global__ __launch_bounds__(512) void gemv_mfma_xr_kernel(const uint8_t* __rest
         s[0] = *reinterpret_cast<const uint32_t*>(area_p + 8 * 1024 + 4 * lane);
         s[1] = *reinterpret_cast<const uint32_t*>(area_p + 8 * 1024 + 256 + 4 * lane);
     }
+
+    const int ew = f16 ? fw - 127 - 15 : 0;   // the wave's partial sums are scaled by 2^ew
 
     // one row step; F: binary16 x and codes (else bf16), MORE: the next row step's loads are
     // issued here, group pair by group pair as the registers of a pair are used.  Both are
@@ -855,7 +865,7 @@ __global__ __launch_bounds__(512) void gemv_mfma_xr_kernel(const uint8_t* __rest
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const int m = 4 * kb + v;
-            if (m < M) rbuf[col * kRedStride + m] = acc[v];
+            if (m < M) rbuf[col * kRedStride + m] = ldexpf(acc[v], ew);
         }
         lds_barrier();
         const int rb = step_row(t);
@@ -867,9 +877,7 @@ __global__ __launch_bounds__(512) void gemv_mfma_xr_kernel(const uint8_t* __rest
             if (row >= rfirst) {
                 const float* rs = red + (t & 1) * n_waves * 16 * kRedStride;
                 float v = 0.0f;
-                for (int w = 0; w < n_waves; ++w)
-                    v += ldexpf(rs[(w * 16 + r) * kRedStride + m],
-                                *reinterpret_cast<const int*>(smem + w * kXrWaveLds + kXrEOffset + 4 * m));
+                for (int w = 0; w < n_waves; ++w) v += rs[(w * 16 + r) * kRedStride + m];
                 const int64_t o = (int64_t)m * N + row;
                 if (y_bf16)
                     static_cast<uint16_t*>(yv)[o] = (uint16_t)bf16_bits_rne(v);
