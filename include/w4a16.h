@@ -134,9 +134,11 @@ w4_status w4_unprepare(const void* prepared, int64_t N, int64_t K,
  * value q - zero of a code (a code equal to its zero adds exactly 0); bf16 x enters
  * the one-row kernel as binary16 x * 2^-E, E per wave of 2048 inputs (exact within 2^25
  * of the wave's largest value; a wave with a value outside that window, and binary32 x,
- * use one binary32 FMA per input instead), and the matrix-core kernels (2 <= M <= 16)
- * as bf16 with bf16 q - zero codes, or, on workgroups with six or more 16-row steps, as
- * binary16 x * 2^-E per row of x with binary16 codes where x converts exactly.
+ * use one binary32 FMA per input instead), and the matrix-core kernels (2 <= M <= 16;
+ * M = 2 stays on the one-row kernel unless the matrix has more than 16384 rows and
+ * K <= 8192) as binary16 x * 2^-E with binary16 codes where x converts exactly (E per
+ * wave: on matrices with K <= 8192 and at least 48 rows per compute unit, and on the
+ * others with M <= 4), else as bf16 with bf16 q - zero codes.
  *   prepared  from w4_prepare (256-B aligned).
  *   x         [M, K] row-major, bfloat16 (xt = W4_BF16) or binary32 (W4_F32); 16-B aligned.
  *   y         [M, N] row-major, binary32 (yt = W4_F32) or bfloat16 (W4_BF16); must
