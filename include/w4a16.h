@@ -136,9 +136,9 @@ w4_status w4_unprepare(const void* prepared, int64_t N, int64_t K,
  * of the wave's largest value; a wave with a value outside that window, and binary32 x,
  * use one binary32 FMA per input instead), and the matrix-core kernels (2 <= M <= 16;
  * M = 2 stays on the one-row kernel unless the matrix has more than 16384 rows and
- * K <= 8192) as binary16 x * 2^-E with binary16 codes where x converts exactly (E per
- * wave: on matrices with K <= 8192 and at least 48 rows per compute unit, and on the
- * others with M <= 4), else as bf16 with bf16 q - zero codes.
+ * K <= 8192) as binary16 x * 2^-E with binary16 codes where x converts exactly (on
+ * matrices with K <= 8192 and at least 48 rows per compute unit, E per wave; on the
+ * others with M <= 4, E per wave and row of x), else as bf16 with bf16 q - zero codes.
  *   prepared  from w4_prepare (256-B aligned).
  *   x         [M, K] row-major, bfloat16 (xt = W4_BF16) or binary32 (W4_F32); 16-B aligned.
  *   y         [M, N] row-major, binary32 (yt = W4_F32) or bfloat16 (W4_BF16); must
