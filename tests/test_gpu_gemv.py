@@ -150,6 +150,43 @@ def test_shapes_and_ragged_edges(n, k, m):
     assert_within(to_np32(y), yr, bound, f"N={n} K={k} M={m}")
 
 
+def _sweep_cases(count=24, seed=2026):
+    """Seeded (N, K, M, wide) cases: half with N >= 12033 and K <= 1536 (the resident-x kernel
+    for 3 <= M <= 16), half with N <= 3000 and K up to 16384 (the one-row and streaming
+    kernels), M from 1 to 16, and in about a third x wide in one random span of inputs."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(count):
+        if i % 2 == 0:
+            n = int(rng.integers(12033, 20000))
+            k = 128 * int(rng.integers(1, 13))
+        else:
+            n = int(rng.integers(1, 3001))
+            k = 128 * int(rng.integers(1, 129))
+            n = max(1, min(n, 24_000_000 // k))
+        m = int(rng.integers(1, 17))
+        cases.append((n, k, m, bool(rng.random() < 0.35)))
+    return cases
+
+
+@pytest.mark.parametrize("n,k,m,wide", _sweep_cases())
+def test_random_shape_sweep(n, k, m, wide):
+    """Every output against the oracle on seeded shapes across the kernels' routing: ragged
+    rows, groups per wave and row steps, every M, and waves whose x falls back to bf16."""
+    rng = np.random.default_rng(n * 7 + k * 3 + m)
+    w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    if wide:
+        a = 128 * int(rng.integers(0, k // 128))
+        b = min(k, a + 128 * int(rng.integers(1, 5)))
+        x[:, a:b] = synth.wide_range_activations(m, b - a, seed=n + k)
+    xb = torch.from_numpy(x).to(torch.bfloat16)
+    prep, _ = _quant_prepare(torch.from_numpy(w).to(DEV))
+    y = _run(prep, n, k, xb.to(DEV))
+    yr, bound, _ = _ref_from_oracle(w, to_np32(xb))
+    assert_within(to_np32(y), yr, bound, f"sweep N={n} K={k} M={m} wide={wide}")
+
+
 @pytest.mark.parametrize("m", [1, 7, 16])
 def test_f32_activations_several_rows(m):
     rng = np.random.default_rng(m)
