@@ -139,7 +139,8 @@ def test_short_last_round_rows():
                                    (64, 32768, 1), (64, 32768, 5), (4099, 2048, 8),
                                    (77, 11008, 4), (130, 16512, 2), (33, 16512, 3),
                                    (2050, 384, 16), (96, 32768, 16), (40, 32768, 11),
-                                   (3, 128, 16), (7, 384, 8), (33, 1152, 4)])
+                                   (3, 128, 16), (7, 384, 8), (33, 1152, 4),
+                                   (50, 128, 4), (33, 256, 3), (200, 128, 8)])
 def test_shapes_and_ragged_edges(n, k, m):
     rng = np.random.default_rng(n + k + m)
     w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
@@ -239,7 +240,8 @@ def test_deterministic_repeat():
 # group counts (K = 1152: a wave with four of its eight groups), ragged N, several M
 
 @pytest.mark.parametrize("n,k,m", [(20000, 1152, 3), (12300, 1152, 4), (12300, 1152, 16),
-                                   (12289, 4096, 5)])
+                                   (12289, 4096, 5), (16001, 128, 3), (16001, 128, 16),
+                                   (13000, 256, 8), (12100, 384, 12)])
 def test_batched_resident_x_shapes_full(n, k, m):
     rng = np.random.default_rng(n + k + m)
     w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
@@ -264,6 +266,25 @@ def test_batched_resident_x_sampled_rows_k8192():
         y = to_np32(_run(prep, n, k, x16[:mm].contiguous()))
         assert_within(y[:, rows], oracle.gemv_ref(p, s, z, x32[:mm]),
                       oracle.tolerance_ref(p, s, z, x32[:mm]), f"resident-x sampled M={mm}")
+
+
+@pytest.mark.parametrize("k", [8192, 8320])
+@pytest.mark.parametrize("m", [4, 16])
+def test_batched_routing_boundary_sampled_rows(k, m):
+    """K = 64 groups (the most the resident-x kernel holds) and 65 groups (the streaming
+    kernel) at the same N: sampled rows, including both ends of the last workgroup."""
+    n = 12500
+    W = synth.normal_weights(n, k, 900 + k, DEV)
+    x16 = synth.normal_activations(m, k, 901 + k, DEV)
+    prep, _ = _quant_prepare(W)
+    rng = np.random.default_rng(k + m)
+    rows = np.unique(np.concatenate([[0, 1, 15, 16, 47, 48, n - 17, n - 16, n - 1],
+                                     rng.choice(n, 200, replace=False)]))
+    p, s, z = oracle.quantize_ref(to_np32(W[torch.from_numpy(rows).to(DEV)]))
+    x32 = to_np32(x16)
+    y = to_np32(_run(prep, n, k, x16))
+    assert_within(y[:, rows], oracle.gemv_ref(p, s, z, x32), oracle.tolerance_ref(p, s, z, x32),
+                  f"N={n} K={k} M={m} sampled")
 
 
 def test_batched_resident_x_one_hot_exact():
