@@ -158,6 +158,34 @@ def test_streaming_binary16_x_one_wave_falls_back(m):
     print(f"M={m}: worst err/bound {r:.3e}")
 
 
+@pytest.mark.parametrize("n,k,m,wave", [(40000, 8192, 1, 1), (8192, 28672, 1, 5),
+                                         (12000, 8192, 2, 2), (4096, 4096, 1, 1)])
+def test_one_row_kernel_one_wave_falls_back(n, k, m, wave):
+    """The dot2 kernel (M = 1, 2) with x wide only in the inputs of one wave (2048 per wave),
+    so that wave of every workgroup takes the exact path while the others stay on binary16 x:
+    workgroups of 16 and 8 rows (40000 x 8192: three and one barriers between steps), 32 rows
+    of fourteen waves (8192 x 28672: seven), 8 rows at M = 2, and one-step workgroups (4096 x
+    4096).  The exact path passes as many barriers as the pipelined one, so the workgroup's
+    partial sums are all written before they are combined.  Sampled rows (both ends of every
+    kind of workgroup) against the oracle."""
+    W = synth.normal_weights(n, k, 500 + n, DEV)
+    p, s, z = w4.w4_quantize(W)
+    prep = w4.w4_prepare(p, s, z)
+    rng = np.random.default_rng(n + m)
+    x = rng.standard_normal((m, k)).astype(np.float32)
+    a = 2048 * wave
+    x[:, a:a + 2048] = synth.wide_range_activations(m, 2048, seed=501 + n)
+    xb = torch.from_numpy(x).to(torch.bfloat16)
+    rows = np.unique(np.concatenate([np.arange(0, 40), np.arange(n - 40, n),
+                                     rng.choice(n, 240, replace=False)]))
+    rp, rs, rz = oracle.quantize_ref(to_np32(W[torch.from_numpy(rows).to(DEV)]))
+    y = to_np32(w4.w4_gemv(prep, n, k, xb.to(DEV).contiguous()))
+    xn = to_np32(xb)
+    r = assert_within(y[:, rows], oracle.gemv_ref(rp, rs, rz, xn), oracle.tolerance_ref(rp, rs, rz, xn),
+                      f"dot2 one wide wave {n}x{k} M={m}")
+    print(f"{n}x{k} M={m}: worst err/bound {r:.3e}")
+
+
 @pytest.mark.parametrize("m", [4, 5, 7, 13, 16])
 def test_resident_x_binary16_ragged_rows(m):
     """The resident-x kernel's binary16 path with a ragged last workgroup (24616 rows: 220
