@@ -43,7 +43,9 @@
 //     rows through two register buffers: the loads of the next step are issued before a
 //     step is computed (scheduling barriers keep them in order, so the compiler's in-order
 //     wait counts stay exact and a step waits only for its own loads).  The first step's
-//     loads follow x's directly, so they are in flight while x is converted;
+//     loads follow x's directly, so they are in flight while x is converted.  With bf16 x
+//     the waves meet at a barrier before each step's loads, so the workgroup reads the
+//     step's rows whole;
 //   * groups of up to eight waves end the launch with a round of workgroups that take
 //     half the rows of the others, which shortens the tail of the weight stream; at M = 1 a
 //     matrix too small to fill one round of eight-row workgroups runs workgroups of a
