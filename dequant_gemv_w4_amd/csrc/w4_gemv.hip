@@ -44,8 +44,8 @@
 //     step is computed (scheduling barriers keep them in order, so the compiler's in-order
 //     wait counts stay exact and a step waits only for its own loads).  The first step's
 //     loads follow x's directly, so they are in flight while x is converted.  With bf16 x
-//     the waves meet at a barrier before each step's loads, so the workgroup reads the
-//     step's rows whole;
+//     (and binary32 x two rows at a time) the waves meet at a barrier before each step's
+//     loads, so the workgroup reads the step's rows whole;
 //   * groups of up to eight waves end the launch with a round of workgroups that take
 //     half the rows of the others, which shortens the tail of the weight stream; at M = 1 a
 //     matrix too small to fill one round of eight-row workgroups runs workgroups of a
@@ -425,11 +425,12 @@ __global__ __launch_bounds__(MAXT, (MT == 1 && !XF32 && SPT == 1) ? 6 : 1) void 
     // memory wait: the previous step's loads stay in flight), so that together they read the
     // step's four whole rows at once instead of drifting over many rows.  Measured on MI355X:
     // 70B decode step 6.52-6.53 -> 6.42-6.44 ms at M = 1, 0.1-0.2 us per shape faster at
-    // M = 2; with binary32 x, whose vector work per input is several times larger, it cost up
-    // to 3 us per shape at M = 1, so those kernels go without.  The pipelined loop below
+    // M = 2.  With binary32 x (several times the vector work per input) it ran the launches
+    // of two rows 0.9-2.6 us faster per shape but cost up to 3 us at one row and 6 us with two
+    // slices per lane, so only the former take it.  The pipelined loop below
     // passes rows_per_wg / 4 - 1 barriers (none in one-step workgroups); a wave on the exact
     // path passes as many, so that every barrier of the workgroup pairs up.
-    constexpr bool kLockstep = !XF32 && SPT == 1 && MT <= 2 && !ONE;
+    constexpr bool kLockstep = SPT == 1 && !ONE && (XF32 ? MT == 2 : MT <= 2);
 
     // bf16 x outside the binary16 window (rare): the wave runs the exact path, one row at a
     // time with loads of its own -- a separate loop, so that it adds nothing to the
